@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs for the gated delta rule, shared by the tests, the
+benchmark and the smoke check.
+
+This module holds none of the operator's arithmetic: it only draws random
+numbers, shapes them and rounds them to the working dtype.  Both the HIP path
+and the CPU oracle consume what it returns; neither is imported here.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, PCG64, fp64 draws in the
+order: sequence lengths, q, k, v, g_raw, beta_raw, h0, do):
+  q, k   ~ N(0, 1), then L2-normalised over the last dim per (token, head)
+  v      ~ N(0, 1)
+  g      = -softplus(N(0, 1)) * g_scale          (log-decay, < 0)
+  beta   = sigmoid(N(0, 1))
+  h0     ~ N(0, h0_std^2) when h0_std > 0, else no initial state
+  do     ~ N(0, 1) when with_grad
+Each value is computed in fp64 and rounded to the storage dtype: fp32 by
+round-to-nearest-even, bf16 by RNE to fp32 and then RNE to bf16.  g, beta and
+states are fp32.  The arrays returned are fp64 holding exactly those rounded
+values, so the oracle sees the bits the GPU sees.
+
+Varlen lengths: L = floor(exp(U(ln lo, ln hi))) drawn until the total reaches
+``total``; the last length is cut to fit (it is never zero).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    B: int
+    T: int                 # per batch row (dense) or total packed tokens (varlen)
+    H: int
+    dk: int
+    dv: int
+    dtype: str             # "fp32" or "bf16"
+    g_scale: float = 0.1
+    h0_std: float = 0.0
+    varlen: bool = False
+    len_lo: int = 128
+    len_hi: int = 16384
+    with_grad: bool = False
+    chunk: int = 64
+
+
+# The five workloads, plus the training-step shape the throughput metric uses.
+CONFIGS = {
+    "c0": Config("c0_fwd_fp32_T256_H2_d64", 1, 256, 2, 64, 64, "fp32"),
+    "c1": Config("c1_fwd_bf16_T4096_H16_d128", 1, 4096, 16, 128, 128, "bf16"),
+    "c2": Config("c2_fwd_bf16_varlen32768_H16_d128", 1, 32768, 16, 128, 128, "bf16",
+                 varlen=True),
+    "c3": Config("c3_fwd_bf16_T65536_H16_d128_h0", 1, 65536, 16, 128, 128, "bf16",
+                 g_scale=0.02, h0_std=0.02),
+    "c4": Config("c4_fwdbwd_bf16_B2_T8192_H16_d128", 2, 8192, 16, 128, 128, "bf16",
+                 with_grad=True),
+    "metric": Config("fwdbwd_bf16_B1_T4096_H16_d128", 1, 4096, 16, 128, 128, "bf16",
+                     with_grad=True),
+}
+
+
+def round_fp32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "fp32":
+        return round_fp32(x)
+    raise ValueError(dtype)
+
+
+def varlen_lengths(rng: np.random.Generator, total: int, lo: int, hi: int) -> list:
+    lens = []
+    acc = 0
+    while acc < total:
+        L = int(math.floor(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        L = max(1, min(L, total - acc))
+        lens.append(L)
+        acc += L
+    return lens
+
+
+def _l2norm(x):
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, 1e-12)
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def make_inputs(cfg: Config, seed: int = 0, *, T: int | None = None, B: int | None = None,
+                H: int | None = None, lengths: list | None = None) -> dict:
+    """Draw one input set.  ``T``/``B``/``H`` override the config's sizes (for
+    small test cases); ``lengths`` forces the varlen sequence lengths."""
+    rng = np.random.default_rng(seed)
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    H = cfg.H if H is None else H
+    cu = None
+    if cfg.varlen or lengths is not None:
+        if lengths is None:
+            lengths = varlen_lengths(rng, T, cfg.len_lo, cfg.len_hi)
+        B = 1
+        T = int(sum(lengths))
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    N = B if cu is None else len(cu) - 1
+    dt = cfg.dtype
+    q = _l2norm(rng.standard_normal((B, T, H, cfg.dk)))
+    k = _l2norm(rng.standard_normal((B, T, H, cfg.dk)))
+    v = rng.standard_normal((B, T, H, cfg.dv))
+    g = -_softplus(rng.standard_normal((B, T, H))) * cfg.g_scale
+    beta = _sigmoid(rng.standard_normal((B, T, H)))
+    h0 = rng.standard_normal((N, H, cfg.dk, cfg.dv)) * cfg.h0_std if cfg.h0_std > 0 else None
+    do = rng.standard_normal((B, T, H, cfg.dv)) if cfg.with_grad else None
+    out = dict(q=round_to(q, dt), k=round_to(k, dt), v=round_to(v, dt), g=round_fp32(g),
+               beta=round_fp32(beta), h0=None if h0 is None else round_fp32(h0),
+               do=None if do is None else round_to(do, dt), cu_seqlens=cu, dtype=dt,
+               B=B, T=T, H=H, dk=cfg.dk, dv=cfg.dv, N=N)
+    return out
