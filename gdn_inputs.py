@@ -68,9 +68,14 @@ def round_fp32(x: np.ndarray) -> np.ndarray:
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
     f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    u = f.view(np.uint32)
+    # RNE to the top 16 bits (in place); no overflow for finite inputs
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u &= np.uint32(0xFFFF0000)
+    return f.astype(np.float64)
 
 
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:

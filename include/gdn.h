@@ -1,0 +1,144 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet (GDN) chunked gated
+ * delta-rule operator, forward and backward, on one AMD MI355X (gfx950).
+ *
+ * The operator is the linear-attention core of Qwen3.5 that the XTuner /
+ * Ascend 910C training article rebuilds natively (section 3.1.2, "GDN linear
+ * attention rebuilt natively in Ascend C"; Fig. 7 lists its kernel family:
+ * the forward state update that also runs inside the backward, the reverse
+ * pass through the state-transition chain, the local dv update and the
+ * dq/dk/dw/dg projection; Fig. 8 adds the triangular-solve helper).  The
+ * article prints no formula; the recurrence implemented is the gated delta
+ * rule, per sequence and head:
+ *
+ *     S_t = exp(g_t) * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * S_t is d_v x d_k.  It crosses this interface transposed: a state tensor is
+ * [N][H][d_k][d_v] fp32 with element (n, h, i, j) = S[j][i] of sequence n,
+ * head h.
+ *
+ * Layouts (contiguous, last index fastest; B*T tokens in total):
+ *   q, k, dq, dk : [B][T][H][d_k]      dtype of the problem (fp32 or bf16)
+ *   v, o, do, dv : [B][T][H][d_v]      dtype of the problem
+ *   g, beta, dg, dbeta : [B][T][H]     fp32 (g is the natural-log decay)
+ *   h0, ht, dht, dh0   : [N][H][d_k][d_v] fp32
+ * Dense problems have N = B sequences of T tokens each.  Packed
+ * variable-length problems have B = 1, T = total tokens and N sequences
+ * given by cu_seqlens (int32, N+1 entries, cu[0] = 0, non-decreasing,
+ * cu[N] = T; zero-length sequences are allowed and pass their state through).
+ *
+ * Ownership and execution:
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises device memory; it keeps no global state and is reentrant.
+ *  - All device work is enqueued on the caller's stream (hipStream_t passed
+ *    as void*, NULL = the null stream); the calls return without waiting.
+ *  - Inputs are read-only.  Outputs are fully overwritten (never
+ *    accumulated) and must not alias any input, each other or the workspace.
+ *  - The workspace is caller-provided device memory of at least the size
+ *    the *_workspace_bytes query returns, 256-byte aligned.  It is
+ *    stream-ordered scratch: reusable once the stream has passed the call.
+ *  - Every device pointer must be 16-byte aligned.
+ *
+ * Errors: every argument is checked on the host before any HIP call; a
+ * failing check returns GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED or
+ * GDN_ERR_WORKSPACE_TOO_SMALL and enqueues nothing.  A launch failure returns
+ * GDN_ERR_HIP.  Device faults surface at the caller's next synchronisation.
+ * gdn_last_error_message() returns a thread-local description of the last
+ * non-OK return.  Nothing aborts, prints or throws across this interface.
+ *
+ * Supported set: d_k = d_v in {64, 128}, chunk = 64, dtype fp32 or bf16,
+ * any T >= 0 (a problem with no tokens enqueues only state copies).
+ * Anything else returns GDN_ERR_UNSUPPORTED.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARGUMENT = 1,
+  GDN_ERR_UNSUPPORTED = 2,
+  GDN_ERR_WORKSPACE_TOO_SMALL = 3,
+  GDN_ERR_HIP = 4
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+  int64_t batch;   /* B; must be 1 when cu_seqlens are given                    */
+  int64_t seqlen;  /* T: tokens per batch row, or total packed tokens (varlen)  */
+  int64_t heads;   /* H                                                          */
+  int64_t dk;      /* key/query head dim                                         */
+  int64_t dv;      /* value head dim (must equal dk)                             */
+  int64_t chunk;   /* chunk length of the chunked form; must be 64               */
+  int64_t num_seqs;                /* N when varlen; ignored when dense            */
+  const int32_t* cu_seqlens_host;  /* [N+1] host copy: validation and launch sizes */
+  const int32_t* cu_seqlens_dev;   /* [N+1] device copy read by the kernels        */
+                                   /* both NULL: dense; both non-NULL: varlen      */
+  float scale;     /* o = scale * S q                                             */
+  gdn_dtype dtype; /* dtype of q, k, v, o, do, dq, dk, dv                         */
+} gdn_problem;
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+/* Workspace sizes in bytes for a valid problem; 0 if the problem is invalid
+ * or unsupported (the matching call then reports why). */
+size_t gdn_fwd_workspace_bytes(const gdn_problem* p);
+size_t gdn_bwd_workspace_bytes(const gdn_problem* p);
+
+/* Forward: o and (if ht != NULL) the final states.
+ *   q, k, v : device, layouts above, problem dtype
+ *   g, beta : device fp32 [B][T][H]
+ *   h0      : device fp32 [N][H][dk][dv] initial states, or NULL for zeros
+ *   o       : device output, problem dtype
+ *   ht      : device fp32 [N][H][dk][dv] final states, or NULL to skip
+ *   workspace / workspace_bytes : device scratch, >= gdn_fwd_workspace_bytes
+ * On return the workspace also holds the per-chunk forward context
+ * (decays, WY factors, chunk-entry states, corrected values); gdn_bwd may
+ * reuse it (see fwd_workspace below) as long as it is left untouched. */
+gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* h0, void* o, float* ht,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of L = sum_t <do_t, o_t> + <dht, ht>:
+ *   do      : device upstream gradient of o, problem dtype
+ *   dht     : device fp32 gradient of the final states, or NULL for zero
+ *   dq, dk, dv : device outputs, problem dtype
+ *   dg, dbeta  : device fp32 outputs [B][T][H]
+ *   dh0     : device fp32 [N][H][dk][dv] gradient of h0, or NULL to skip
+ *             (defined also when h0 is NULL: the gradient at a zero state)
+ *   fwd_workspace : NULL, or the workspace of a completed gdn_fwd call with
+ *             the same problem and the same q, k, v, g, beta, h0, left
+ *             untouched since; then the forward context is read from it
+ *             instead of being recomputed.  Anything else there gives
+ *             undefined results.
+ *   workspace / workspace_bytes : device scratch, >= gdn_bwd_workspace_bytes
+ */
+gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* h0, const void* d_o,
+                   const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                   float* dh0, const void* fwd_workspace, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Static name of a status code. */
+const char* gdn_status_string(gdn_status s);
+
+/* Thread-local description of the last non-OK status returned on this
+ * thread ("" if none). */
+const char* gdn_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,232 @@
+"""Gated DeltaNet (GDN) chunked gated delta-rule operator on AMD MI355X.
+
+Thin Python binding of ``libgdn.so`` (C ABI declared in ``include/gdn.h``):
+argument marshalling only.  Every step of the operator runs in the library's
+HIP kernels; PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or fails, these functions raise.
+
+    o, ht = fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
+    dq, dk, dv, dg, dbeta, dh0 = bwd(q, k, v, g, beta, do, ...)
+
+Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g, beta [B,T,H] fp32; states
+[N,H,dk,dv] fp32 holding S^T.  Packed variable-length input: B = 1 and
+cu_seqlens (int32, N+1) -- either one tensor (copied to host and device as
+needed) or a (host_tensor, device_tensor) pair with equal contents.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE_TOO_SMALL, GDN_ERR_HIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+
+EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_fwd",
+            "gdn_bwd", "gdn_status_string", "gdn_last_error_message")
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("num_seqs", ctypes.c_int64), ("cu_seqlens_host", ctypes.c_void_p),
+                ("cu_seqlens_dev", ctypes.c_void_p), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (status_string(status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() or "
+                               "python -m linear_attention_gated_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        p, sz = ctypes.c_void_p, ctypes.c_size_t
+        prob = ctypes.POINTER(GdnProblem)
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_fwd_workspace_bytes.argtypes = [prob]
+        L.gdn_fwd_workspace_bytes.restype = sz
+        L.gdn_bwd_workspace_bytes.argtypes = [prob]
+        L.gdn_bwd_workspace_bytes.restype = sz
+        L.gdn_fwd.argtypes = [prob] + [p] * 8 + [p, sz, p]
+        L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_bwd.argtypes = [prob] + [p] * 15 + [p, sz, p]
+        L.gdn_bwd.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error_message.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def last_error_message() -> str:
+    return lib().gdn_last_error_message().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, last_error_message())
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    if dt == torch.float32:
+        return GDN_F32
+    raise GdnError(GDN_ERR_UNSUPPORTED, "dtype %s (need float32 or bfloat16)" % dt)
+
+
+def _cu_pair(cu_seqlens, device):
+    if cu_seqlens is None:
+        return None, None
+    if isinstance(cu_seqlens, (tuple, list)) and len(cu_seqlens) == 2 and all(
+            isinstance(x, torch.Tensor) for x in cu_seqlens):
+        host, dev = cu_seqlens
+    else:
+        t = torch.as_tensor(cu_seqlens, dtype=torch.int32)
+        host = t.cpu()
+        dev = t.to(device)
+    host = host.to(torch.int32).contiguous()
+    dev = dev.to(torch.int32).contiguous()
+    return host, dev
+
+
+def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0) -> GdnProblem:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    p = GdnProblem()
+    p.batch, p.seqlen, p.heads, p.dk, p.dv, p.chunk = B, T, H, dk, dv, 64
+    p.num_seqs = 0 if cu_host is None else cu_host.numel() - 1
+    p.cu_seqlens_host = None if cu_host is None else cu_host.data_ptr()
+    p.cu_seqlens_dev = None if cu_dev is None else cu_dev.data_ptr()
+    p.scale = float(scale)
+    p.dtype = _dtype_code(q.dtype)
+    return p
+
+
+def _num_seqs(q, cu_host):
+    return q.shape[0] if cu_host is None else cu_host.numel() - 1
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+class Context:
+    """Forward context kept for a later backward: the forward workspace and
+    the problem it was computed for."""
+
+    def __init__(self, workspace, problem_key):
+        self.workspace = workspace
+        self.problem_key = problem_key
+
+
+def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
+        output_final_state=True, return_context=False, workspace=None):
+    """Forward pass.  Returns (o, ht) or (o, ht, Context)."""
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, dt, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(beta, "beta", torch.float32, dev)
+    _require(initial_state, "initial_state", torch.float32, dev)
+    cu_h, cu_d = _cu_pair(cu_seqlens, dev)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale)
+    L = lib()
+    nbytes = L.gdn_fwd_workspace_bytes(ctypes.byref(p))
+    if nbytes == 0:
+        _check(L.gdn_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0,
+                         None))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    B, T, H, dk = q.shape
+    N = _num_seqs(q, cu_h)
+    o = torch.empty((B, T, H, v.shape[-1]), dtype=dt, device=dev)
+    ht = torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32, device=dev) \
+        if output_final_state else None
+    _check(L.gdn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                     _ptr(initial_state), _ptr(o), _ptr(ht), _ptr(workspace), nbytes, _stream(dev)))
+    if return_context:
+        key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
+               float(scale))
+        return o, ht, Context(workspace, key)
+    return o, ht
+
+
+def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, scale=1.0,
+        context: Context | None = None, need_dh0=True, workspace=None):
+    """Backward pass of L = <do, o> + <dht, ht>.  Returns (dq, dk, dv, dg, dbeta, dh0);
+    dh0 is None when need_dh0 is False.  With ``context`` from ``fwd(...,
+    return_context=True)`` on the same inputs, the forward is not recomputed."""
+    dev = q.device
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+        _require(t, name, dt, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(beta, "beta", torch.float32, dev)
+    _require(initial_state, "initial_state", torch.float32, dev)
+    _require(dht, "dht", torch.float32, dev)
+    cu_h, cu_d = _cu_pair(cu_seqlens, dev)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale)
+    if context is not None:
+        key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
+               float(scale))
+        if key != context.problem_key:
+            raise ValueError("context was computed for a different problem")
+    L = lib()
+    nbytes = L.gdn_bwd_workspace_bytes(ctypes.byref(p))
+    if nbytes == 0:
+        _check(L.gdn_bwd(ctypes.byref(p), *([None] * 16), 0, None))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    N = _num_seqs(q, cu_h)
+    B, T, H, dk = q.shape
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta)
+    dh0 = torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32, device=dev) if need_dh0 else None
+    fws = None if context is None else context.workspace
+    _check(L.gdn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                     _ptr(initial_state), _ptr(do), _ptr(dht), _ptr(dq), _ptr(dk_), _ptr(dv),
+                     _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(fws), _ptr(workspace), nbytes,
+                     _stream(dev)))
+    return dq, dk_, dv, dg, dbeta, dh0

@@ -1,0 +1,315 @@
+// api.cpp -- the C ABI of libgdn.so: argument validation, workspace layout
+// and the launch sequence.  Every check runs on the host before any HIP call.
+//
+// Launch sequence (all on the caller's stream, no host synchronisation):
+//   forward : plan -> K1 prep (gamma, T = (I+A)^-1, WY factors)
+//                  -> K2 state pass (sequential over chunks)
+//                  -> K3 output
+//   backward: [plan -> K1 -> K2 recompute, unless a forward workspace is given]
+//             -> K4 prep -> K5 reverse state-gradient pass -> K6 gradients
+// The split mirrors the native kernel family of the XTuner / Ascend 910C
+// article (section 3.1.2, Fig. 7): a forward state update that also runs
+// inside the backward, the reverse pass through the state-transition chain,
+// the local dv step and the dq/dk/dw/dg step.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  int64_t B = 0, T = 0, H = 0, D = 0, N = 0, NC = 0, tokens = 0;
+  bool varlen = false, bf16 = false;
+  size_t esz = 0;
+  // byte offsets into a workspace
+  size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0;
+  size_t fwd_bytes = 0;
+  size_t QgT = 0, dOf = 0, WnT = 0, Ktn = 0, HPf = 0, dVf = 0, dVl = 0;
+  size_t bwd_bytes = 0;
+};
+
+// Validate the problem description and derive sizes.  No HIP call.
+gdn_status plan_problem(const gdn_problem* p, Layout* L) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (p->heads < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "heads = %lld < 1", (long long)p->heads);
+  if (p->dk < 1 || p->dv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "dk/dv must be >= 1");
+  if (p->dk != p->dv) return fail(GDN_ERR_UNSUPPORTED, "dk (%lld) != dv (%lld)", (long long)p->dk, (long long)p->dv);
+  if (p->dk != 64 && p->dk != 128) return fail(GDN_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)p->dk);
+  if (p->chunk != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk %lld != 64", (long long)p->chunk);
+  if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
+  const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
+  if (has_h != has_d)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
+  L->varlen = has_h;
+  L->H = p->heads;
+  L->D = p->dk;
+  L->T = p->seqlen;
+  L->bf16 = p->dtype == GDN_BF16;
+  L->esz = L->bf16 ? 2 : 4;
+  const int64_t maxtok = (int64_t)1 << 31;
+  if (L->varlen) {
+    if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
+    if (p->num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs = %lld < 1", (long long)p->num_seqs);
+    if (((uintptr_t)p->cu_seqlens_dev) % 4) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_dev misaligned");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d != 0", cu[0]);
+    int64_t nc = 0;
+    for (int64_t n = 0; n < p->num_seqs; ++n) {
+      if (cu[n + 1] < cu[n])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %lld (%d -> %d)", (long long)n, cu[n], cu[n + 1]);
+      nc += (cu[n + 1] - cu[n] + 63) / 64;
+    }
+    if (cu[p->num_seqs] != p->seqlen)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d != seqlen %lld", cu[p->num_seqs], (long long)p->seqlen);
+    L->B = 1;
+    L->N = p->num_seqs;
+    L->NC = nc;
+  } else {
+    if (p->batch < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "batch = %lld < 1", (long long)p->batch);
+    L->B = p->batch;
+    L->N = p->batch;
+    L->NC = p->batch * ((p->seqlen + 63) / 64);
+  }
+  L->tokens = L->B * L->T;
+  if (L->tokens * L->H >= maxtok || L->NC * L->H >= maxtok / 64 || L->N * L->H >= maxtok / 64)
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large (tokens*heads must stay below 2^31)");
+
+  // workspace layout
+  const size_t ch = (size_t)(L->NC * L->H);
+  const size_t D = (size_t)L->D, e = L->esz;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  L->chunk_tab = take(sizeof(int32_t) * 4 * (size_t)L->NC);
+  L->seq_tab = take(sizeof(int32_t) * 4 * (size_t)L->N);
+  L->gamma = take(sizeof(float) * 64 * ch);
+  L->Wn = take(e * ch * 64 * D);
+  L->Ktf = take(e * ch * 64 * D);
+  L->Ua = take(e * ch * 64 * D);
+  L->Hf = take(e * ch * D * D);
+  L->Vf = take(e * ch * 64 * D);
+  L->fwd_bytes = off;
+  L->QgT = take(e * ch * 64 * D);
+  L->dOf = take(e * ch * 64 * D);
+  L->WnT = take(e * ch * 64 * D);
+  L->Ktn = take(e * ch * 64 * D);
+  L->HPf = take(e * ch * D * D);
+  L->dVf = take(e * ch * 64 * D);
+  L->dVl = take(sizeof(float) * ch * 64 * D);
+  L->bwd_bytes = off;
+  return GDN_OK;
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+gdn_status check_ptrs(const Range* req, int nreq, const Range* opt, int nopt, const Range* outs, int nout,
+                      const Range* ins, int nin) {
+  for (int i = 0; i < nreq; ++i) {
+    if (req[i].n > 0 && !req[i].p) return fail(GDN_ERR_INVALID_ARGUMENT, "%s is NULL", req[i].name);
+  }
+  for (int i = 0; i < nreq + nopt; ++i) {
+    const Range& r = i < nreq ? req[i] : opt[i - nreq];
+    if (r.p && ((uintptr_t)r.p) % 16)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
+  }
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(outs[i], ins[j]))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "output %s overlaps %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(outs[i], outs[j]))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return GDN_OK;
+}
+
+gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
+  gdn::Params P;
+  std::memset(&P, 0, sizeof(P));
+  P.H = (int)L.H;
+  P.N = (int)L.N;
+  P.NC = (int)L.NC;
+  P.scale = p->scale;
+  P.dense_T = L.varlen ? 0 : (int)L.T;
+  P.total_tokens = (int)L.tokens;
+  P.cu = L.varlen ? p->cu_seqlens_dev : nullptr;
+  P.chunk_tab = reinterpret_cast<int4*>(ws + L.chunk_tab);
+  P.seq_tab = reinterpret_cast<int4*>(ws + L.seq_tab);
+  P.gamma = reinterpret_cast<float*>(ws + L.gamma);
+  P.Wn = ws + L.Wn;
+  P.Ktf = ws + L.Ktf;
+  P.Ua = ws + L.Ua;
+  P.Hf = ws + L.Hf;
+  P.Vf = ws + L.Vf;
+  return P;
+}
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARGUMENT: return "GDN_ERR_INVALID_ARGUMENT";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t gdn_fwd_workspace_bytes(const gdn_problem* p) {
+  try {
+    Layout L;
+    return plan_problem(p, &L) == GDN_OK ? L.fwd_bytes : 0;
+  } catch (...) {
+    return 0;
+  }
+}
+
+size_t gdn_bwd_workspace_bytes(const gdn_problem* p) {
+  try {
+    Layout L;
+    return plan_problem(p, &L) == GDN_OK ? L.bwd_bytes : 0;
+  } catch (...) {
+    return 0;
+  }
+}
+
+gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* h0, void* o, float* ht, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  try {
+    Layout L;
+    gdn_status st = plan_problem(p, &L);
+    if (st != GDN_OK) return st;
+    const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
+    const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
+    const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
+    const Range req[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {o, qk, "o"}, {workspace, L.fwd_bytes, "workspace"}};
+    const Range opt[] = {{h0, sb, "h0"}, {ht, sb, "ht"}};
+    const Range outs[] = {{o, qk, "o"}, {ht, sb, "ht"}, {workspace, L.fwd_bytes, "workspace"}};
+    const Range ins[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {h0, sb, "h0"}};
+    st = check_ptrs(req, 7, opt, 2, outs, 3, ins, 6);
+    if (st != GDN_OK) return st;
+    if (workspace && ((uintptr_t)workspace) % ALIGN)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < L.fwd_bytes)
+      return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, L.fwd_bytes);
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    gdn::Params P = base_params(p, L, reinterpret_cast<char*>(workspace));
+    P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0; P.o = o; P.ht = ht;
+    const int D = (int)L.D;
+    hipError_t e;
+    if ((e = gdn::launch_plan(P, s)) != hipSuccess) return hip_fail(e, "plan launch");
+    if ((e = gdn::launch_fwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_prep launch");
+    if ((e = gdn::launch_fwd_state(P, D, L.bf16, true, s)) != hipSuccess) return hip_fail(e, "fwd_state launch");
+    if ((e = gdn::launch_fwd_out(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_out launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_fwd");
+  }
+}
+
+gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                   const float* beta, const float* h0, const void* d_o, const float* dht, void* dq,
+                   void* dk, void* dv, float* dg, float* dbeta, float* dh0, const void* fwd_workspace,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    Layout L;
+    gdn_status st = plan_problem(p, &L);
+    if (st != GDN_OK) return st;
+    const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
+    const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
+    const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
+    const Range req[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {d_o, qk, "do"}, {dq, qk, "dq"}, {dk, qk, "dk"}, {dv, qk, "dv"}, {dg, gb, "dg"},
+                         {dbeta, gb, "dbeta"}, {workspace, L.bwd_bytes, "workspace"}};
+    const Range opt[] = {{h0, sb, "h0"}, {dht, sb, "dht"}, {dh0, sb, "dh0"},
+                         {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
+    const Range outs[] = {{dq, qk, "dq"}, {dk, qk, "dk"}, {dv, qk, "dv"}, {dg, gb, "dg"}, {dbeta, gb, "dbeta"},
+                          {dh0, sb, "dh0"}, {workspace, L.bwd_bytes, "workspace"}};
+    const Range ins[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {h0, sb, "h0"}, {d_o, qk, "do"}, {dht, sb, "dht"},
+                         {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
+    st = check_ptrs(req, 12, opt, 4, outs, 7, ins, 9);
+    if (st != GDN_OK) return st;
+    if (workspace && ((uintptr_t)workspace) % ALIGN)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (fwd_workspace && ((uintptr_t)fwd_workspace) % ALIGN)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "fwd_workspace is not 256-byte aligned");
+    if (workspace_bytes < L.bwd_bytes)
+      return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, L.bwd_bytes);
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = reinterpret_cast<char*>(workspace);
+    // forward context: from the caller's forward workspace, or recomputed here
+    char* ctx = fwd_workspace ? const_cast<char*>(reinterpret_cast<const char*>(fwd_workspace)) : ws;
+    gdn::Params P = base_params(p, L, ctx);
+    P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0;
+    P.dO = d_o; P.dht = dht; P.dq = dq; P.dk = dk; P.dv = dv; P.dg = dg; P.dbeta = dbeta; P.dh0 = dh0;
+    P.QgT = ws + L.QgT; P.dOf = ws + L.dOf; P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
+    P.HPf = ws + L.HPf; P.dVf = ws + L.dVf; P.dVl = reinterpret_cast<float*>(ws + L.dVl);
+    const int D = (int)L.D;
+    hipError_t e;
+    if (!fwd_workspace) {
+      if ((e = gdn::launch_plan(P, s)) != hipSuccess) return hip_fail(e, "plan launch");
+      if ((e = gdn::launch_fwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_prep launch");
+      if ((e = gdn::launch_fwd_state(P, D, L.bf16, false, s)) != hipSuccess) return hip_fail(e, "fwd_state launch");
+    }
+    if ((e = gdn::launch_bwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_prep launch");
+    if ((e = gdn::launch_bwd_state(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_state launch");
+    if ((e = gdn::launch_bwd_grad(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_grad launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_bwd");
+  }
+}
+
+}  // extern "C"

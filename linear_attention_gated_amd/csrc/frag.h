@@ -1,0 +1,170 @@
+// frag.h -- wave64 MFMA fragment algebra for gfx950 (CDNA4).
+//
+// Every dense product in this library is built from one primitive: a 16x16
+// output tile accumulated over a 32-deep slice of the contraction,
+//     D[m][n] += sum_k A[m][k] * B[k][n].
+// bf16 operands use one v_mfma_f32_16x16x32_bf16; fp32 operands use eight
+// v_mfma_f32_16x16x4_f32 (so the fp32 path never rounds below fp32).
+//
+// Operand fragments.  Lane l (li = l % 16, lg = l / 16) holds 8 values of a
+// matrix X: index row (li) of a 16-row block and 8 positions of a 32-wide
+// contraction block.  The position held in element e is
+//     kslot(lg, e) = 4 lg + e        (e < 4)
+//                  = 16 + 4 lg + e-4 (e >= 4).
+// The same slot map is used for both operands of every MFMA, so the product
+// is exact regardless of the hardware's own k order.  "F(X; a, b)" below
+// means fragments of X whose index dimension is a and contraction dimension
+// is b.  Loaded from a row-major X[a][b] (b contiguous) a fragment is two
+// 4-element vector loads.
+//
+// Accumulators.  Lane l holds D[4 lg + q][li], q = 0..3.  Two vertically
+// adjacent accumulator tiles (rows 32 kb + 0..15 and 32 kb + 16..31) hold,
+// in lane l, rows 32 kb + kslot(lg, e) of column li: converted to the operand
+// type they are exactly F(D; column, row), the fragment of D^T.  Products
+// therefore chain in registers: the output of one MFMA product is the
+// operand of the next, transposed for free.  An MFMA against an identity
+// fragment turns a row-major fragment into the other orientation (exact).
+//
+// Fragment-native storage: a tensor consumed as fragments is stored as
+// records of 64 lanes x 8 elements, lane-major, so a wave loads a fragment
+// with one fully coalesced 16-byte-per-lane access.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename E> struct VecT;
+template <> struct VecT<bf16> { using x8 = bf16x8; using x4 = bf16x4; };
+template <> struct VecT<float> { using x8 = f32x8; using x4 = f32x4; };
+template <typename E> using frag_t = typename VecT<E>::x8;
+template <typename E> using quad_t = typename VecT<E>::x4;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ constexpr int kslot(int lg, int e) {
+  return e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4);
+}
+
+// ---- MFMA ---------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- conversions --------------------------------------------------------
+template <typename E> __device__ __forceinline__ frag_t<E> to_frag(f32x4 lo, f32x4 hi);
+template <> __device__ __forceinline__ bf16x8 to_frag<bf16>(f32x4 lo, f32x4 hi) {
+  f32x8 t = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_convertvector(t, bf16x8);
+}
+template <> __device__ __forceinline__ f32x8 to_frag<float>(f32x4 lo, f32x4 hi) {
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename E> __device__ __forceinline__ quad_t<E> to_quad(f32x4 x);
+template <> __device__ __forceinline__ bf16x4 to_quad<bf16>(f32x4 x) {
+  return __builtin_convertvector(x, bf16x4);
+}
+template <> __device__ __forceinline__ f32x4 to_quad<float>(f32x4 x) { return x; }
+
+template <typename E> __device__ __forceinline__ f32x4 quad_to_f32(quad_t<E> x);
+template <> __device__ __forceinline__ f32x4 quad_to_f32<bf16>(bf16x4 x) {
+  return __builtin_convertvector(x, f32x4);
+}
+template <> __device__ __forceinline__ f32x4 quad_to_f32<float>(f32x4 x) { return x; }
+
+template <typename E> __device__ __forceinline__ f32x8 frag_to_f32(frag_t<E> x);
+template <> __device__ __forceinline__ f32x8 frag_to_f32<bf16>(bf16x8 x) {
+  return __builtin_convertvector(x, f32x8);
+}
+template <> __device__ __forceinline__ f32x8 frag_to_f32<float>(f32x8 x) { return x; }
+
+template <typename E> __device__ __forceinline__ frag_t<E> f32_to_frag(f32x8 x);
+template <> __device__ __forceinline__ bf16x8 f32_to_frag<bf16>(f32x8 x) {
+  return __builtin_convertvector(x, bf16x8);
+}
+template <> __device__ __forceinline__ f32x8 f32_to_frag<float>(f32x8 x) { return x; }
+
+template <typename E> __device__ __forceinline__ frag_t<E> zero_frag() {
+  return f32_to_frag<E>(f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
+}
+
+template <typename E> __device__ __forceinline__ frag_t<E> join(quad_t<E> a, quad_t<E> b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---- fragment loads / stores --------------------------------------------
+// Natural fragment from row-major memory: `row` points at X[a0 + li][b0].
+template <typename E> __device__ __forceinline__ frag_t<E> load_frag_row(const E* row, int lg) {
+  quad_t<E> a = *reinterpret_cast<const quad_t<E>*>(row + 4 * lg);
+  quad_t<E> b = *reinterpret_cast<const quad_t<E>*>(row + 16 + 4 * lg);
+  return join<E>(a, b);
+}
+
+// Fragment-native record: 64 lanes x 8 elements.
+template <typename E> __device__ __forceinline__ frag_t<E> load_rec(const E* rec, int lane) {
+  return *reinterpret_cast<const frag_t<E>*>(rec + 8 * lane);
+}
+template <typename E> __device__ __forceinline__ void store_rec(E* rec, int lane, frag_t<E> f) {
+  *reinterpret_cast<frag_t<E>*>(rec + 8 * lane) = f;
+}
+// Accumulator-native record: 64 lanes x 4 elements.
+template <typename E> __device__ __forceinline__ f32x4 load_acc(const E* rec, int lane) {
+  return quad_to_f32<E>(*reinterpret_cast<const quad_t<E>*>(rec + 4 * lane));
+}
+template <typename E> __device__ __forceinline__ void store_acc(E* rec, int lane, f32x4 x) {
+  *reinterpret_cast<quad_t<E>*>(rec + 4 * lane) = to_quad<E>(x);
+}
+
+// Identity fragment F(I; a, b) for an index block a whose 16 rows fall in
+// half `hsel` (0: slots 0..15, 1: slots 16..31) of its contraction block.
+template <typename E> __device__ __forceinline__ frag_t<E> ident_frag(int hsel, int li, int lg) {
+  f32x8 t = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (lg == (li >> 2)) t[4 * hsel + (li & 3)] = 1.f;
+  return f32_to_frag<E>(t);
+}
+
+__device__ __forceinline__ f32x4 scale4(f32x4 x, float s) {
+  return f32x4{x[0] * s, x[1] * s, x[2] * s, x[3] * s};
+}
+
+// Wave-wide inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float t = __shfl_up(x, off, 64);
+    if (lane >= off) x += t;
+  }
+  return x;
+}
+
+// Sum over the four lane groups (lanes li, li+16, li+32, li+48).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+// Sum over the 16 lanes of a group.
+__device__ __forceinline__ float sum_in_group(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+}  // namespace gdn

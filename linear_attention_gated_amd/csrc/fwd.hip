@@ -1,0 +1,493 @@
+// fwd.hip -- chunk planner and the forward kernels of the gated delta rule.
+//
+// Chunked form (per sequence and head; chunks of 64 tokens restart at each
+// sequence start; rows r, s of a chunk; h = S^T is d_k x d_v):
+//   gamma_r = sum_{s<=r} g_s,  Gam = exp(gamma),  D_rs = exp(gamma_r - gamma_s) (s <= r)
+//   A  = strict_lower(diag(beta) (K K^T) * D),   T = (I + A)^-1
+//   W  = T diag(beta Gam) K,    U = T diag(beta) V
+//   V' = U - W h
+//   O  = scale [diag(Gam) Q h + ((Q K^T) * D) V']
+//   h' = exp(gamma_L) h + Kt^T V',   Kt = diag(exp(gamma_L - gamma)) K
+// This is the decomposition of the native kernel family in the XTuner /
+// Ascend 910C article (section 3.1.2, Fig. 7 and Fig. 8): an intra-chunk
+// triangular solve (solve_tril), a forward state update across chunks and an
+// output step; the equations are derived from the token recurrence.
+#include "frag.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// --------------------------------------------------------------------------
+// Planner: chunk table and sequence table from cu_seqlens (or dense B x T).
+// One workgroup: a scan over sequences for the first-chunk offsets, then a
+// binary search per chunk.
+__global__ __launch_bounds__(1024) void k_plan(Params p) {
+  __shared__ int s_scan[1024];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < p.N; base += 1024) {
+    const int n = base + tid;
+    int t0 = 0, len = 0, nc = 0;
+    if (n < p.N) {
+      if (p.cu) {
+        t0 = p.cu[n];
+        len = p.cu[n + 1] - t0;
+      } else {
+        t0 = n * p.dense_T;
+        len = p.dense_T;
+      }
+      nc = len > 0 ? (len + CHUNK - 1) / CHUNK : 0;
+    }
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int incl = s_scan[tid];
+    if (n < p.N) {
+      // clamp to the chunk count and token count the host planned for, so a
+      // device cu_seqlens that differs from the host copy cannot send any
+      // kernel outside its buffers
+      const int cs = min(s_carry + incl - nc, p.NC);
+      const int ts = min(max(t0, 0), p.total_tokens);
+      p.seq_tab[n] = make_int4(cs, min(nc, p.NC - cs), ts, min(max(len, 0), p.total_tokens - ts));
+    }
+    __syncthreads();
+    if (tid == 1023) s_carry += incl;
+    __syncthreads();
+  }
+  __threadfence();
+  __syncthreads();
+  for (int c = tid; c < p.NC; c += 1024) {
+    int lo = 0, hi = p.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.seq_tab[mid].x <= c) lo = mid; else hi = mid - 1;
+    }
+    const int4 s = p.seq_tab[lo];
+    const int j = c - s.x;
+    const int t0 = min(s.z + CHUNK * j, p.total_tokens);
+    const int len = max(0, min(min(CHUNK, s.w - CHUNK * j), p.total_tokens - t0));
+    p.chunk_tab[c] = make_int4(t0, len, lo, j);
+  }
+}
+
+// --------------------------------------------------------------------------
+// K1: per (chunk, head): gamma, A, T = (I + A)^-1, and the fragment-native
+// operands of the state pass: -W, Kt^T, U.  D/32 waves; wave w owns feature
+// columns [32w, 32w + 32).
+template <typename E, int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
+  constexpr int NW = D / 32;
+  constexpr int KB = D / 32;
+  constexpr int LDA = 68;
+  __shared__ float sA[64 * LDA];
+  __shared__ float sT[64 * LDA];
+  __shared__ float sX[3 * 256];
+  __shared__ float s_gam[64], s_beta[64];
+
+  const int ch = blockIdx.x;
+  const int H = p.H;
+  const int c = ch / H, h = ch - c * H;
+  const int4 ct = p.chunk_tab[c];
+  const int tok0 = ct.x, L = ct.y;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x;
+  const E* K = reinterpret_cast<const E*>(p.k);
+  const E* V = reinterpret_cast<const E*>(p.v);
+
+  // chunk-local cumulative log decay; padded rows get g = 0, beta = 0
+  float gv = 0.f, bv = 0.f;
+  if (lane < L) {
+    gv = p.g[(size_t)(tok0 + lane) * H + h];
+    bv = p.beta[(size_t)(tok0 + lane) * H + h];
+  }
+  const float gam = wave_incl_scan(gv, lane);
+  if (w == 0) {
+    s_gam[lane] = gam;
+    s_beta[lane] = bv;
+    p.gamma[(size_t)ch * 64 + lane] = gam;
+  }
+  // upper blocks of T are zero
+  for (int e = tid; e < 64 * 64; e += 64 * NW) {
+    const int r = e >> 6, s = e & 63;
+    if ((s >> 4) > (r >> 4)) sT[r * LDA + s] = 0.f;
+  }
+
+  // natural key fragments F(K; s, i) for all row blocks
+  frag_t<E> kf[4][KB];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int row = 16 * sb + li;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
+                           : zero_frag<E>();
+  }
+  __syncthreads();
+
+  // A = strict_lower(diag(beta) K K^T * D): ten lower tiles, round-robin over waves
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rr = TR[t], sc = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mma(kf[sc][kb], kf[rr][kb], acc);
+      // lane holds G[r = 16rr + li][s = 16sc + 4lg + q]
+      const int r = 16 * rr + li;
+      const float gr = s_gam[r], br = s_beta[r];
+      float4 out;
+      float* po = reinterpret_cast<float*>(&out);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s = 16 * sc + 4 * lg + q;
+        po[q] = s < r ? br * acc[q] * __expf(gr - s_gam[s]) : 0.f;
+      }
+      *reinterpret_cast<float4*>(&sA[r * LDA + 16 * sc + 4 * lg]) = out;
+    }
+  }
+  __syncthreads();
+
+  // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution (wave 0,
+  // lane = (block lg, column li)), then the off-diagonal blocks by levels:
+  // T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb.
+  if (w == 0) {
+    const int b0 = 16 * lg, j = li;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= sA[(b0 + r) * LDA + b0 + s] * t[s];
+      t[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDA + b0 + j] = t[r];
+  }
+  __syncthreads();
+  for (int d = 1; d < 4; ++d) {
+    const int nblk = 4 - d;
+    for (int e = tid; e < nblk * 256; e += 64 * NW) {
+      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
+      float x = 0.f;
+      for (int kk = 16 * b; kk < 16 * a; ++kk) x += sA[(16 * a + r) * LDA + kk] * sT[kk * LDA + 16 * b + col];
+      sX[e] = x;
+    }
+    __syncthreads();
+    for (int e = tid; e < nblk * 256; e += 64 * NW) {
+      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
+      const float* xb = sX + (e / 256) * 256;
+      float x = 0.f;
+      for (int kk = 0; kk <= r; ++kk) x += sT[(16 * a + r) * LDA + 16 * a + kk] * xb[kk * 16 + col];
+      sT[(16 * a + r) * LDA + 16 * b + col] = -x;
+    }
+    __syncthreads();
+  }
+
+  // T fragments F(T; r, s) (lower triangular: (rb <= 1, skb = 1) is zero)
+  frag_t<E> tf[4][2];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb) {
+      const float* row = sT + (16 * rb + li) * LDA + 32 * skb;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * lg);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg);
+      tf[rb][skb] = to_frag<E>(a, b);
+    }
+
+  const float gL = s_gam[63];
+  const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
+  const size_t rec_ch = (size_t)ch;
+
+  // K transposes for this wave's feature columns: acc rows s, columns i
+  f32x4 kt[4][2];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int row = 16 * sb + li;
+    const frag_t<E> kw = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
+                                 : zero_frag<E>();
+    kt[sb][0] = mma(kw, id0, zero4());
+    kt[sb][1] = mma(kw, id1, zero4());
+  }
+  // per-row scales for rows s = 16sb + 4lg + q
+  float sc_w[4][4], sc_k[4][4], sc_u[4][4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = 16 * sb + 4 * lg + q;
+      const float gs = s_gam[s], bs = s_beta[s];
+      sc_w[sb][q] = bs * __expf(gs);
+      sc_k[sb][q] = __expf(gL - gs);
+      sc_u[sb][q] = bs;
+    }
+  auto rowscale = [](f32x4 x, const float* s4) {
+    return f32x4{x[0] * s4[0], x[1] * s4[1], x[2] * s4[2], x[3] * s4[3]};
+  };
+
+  E* Ktf = reinterpret_cast<E*>(p.Ktf);
+  E* Wn = reinterpret_cast<E*>(p.Wn);
+  E* Ua = reinterpret_cast<E*>(p.Ua);
+  constexpr int NJ = D / 16;
+
+  frag_t<E> xw[2][2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb) {
+      xw[hs][skb] = to_frag<E>(rowscale(kt[2 * skb][hs], sc_w[2 * skb]),
+                               rowscale(kt[2 * skb + 1][hs], sc_w[2 * skb + 1]));
+      const frag_t<E> kk = to_frag<E>(rowscale(kt[2 * skb][hs], sc_k[2 * skb]),
+                                      rowscale(kt[2 * skb + 1][hs], sc_k[2 * skb + 1]));
+      const int ib = 2 * w + hs;
+      store_rec<E>(Ktf + ((rec_ch * NJ + ib) * 2 + skb) * REC, lane, kk);
+    }
+  }
+  // W^T tiles: acc[i][r] = sum_s Xw[s][i] T[r][s]
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    f32x4 wt0 = zero4(), wt1 = zero4();
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb) {
+      if (rb <= 1 && skb == 1) continue;
+      wt0 = mma(xw[0][skb], tf[rb][skb], wt0);
+      wt1 = mma(xw[1][skb], tf[rb][skb], wt1);
+    }
+    store_rec<E>(Wn + ((rec_ch * 4 + rb) * KB + w) * REC, lane, to_frag<E>(-wt0, -wt1));
+  }
+
+  // V transposes and U = T diag(beta) V
+  frag_t<E> vfw[4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int row = 16 * sb + li;
+    vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
+                      : zero_frag<E>();
+  }
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const frag_t<E> idh = hs ? id1 : id0;
+    f32x4 vt[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) vt[sb] = mma(vfw[sb], idh, zero4());
+    frag_t<E> xu[2];
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb)
+      xu[skb] = to_frag<E>(rowscale(vt[2 * skb], sc_u[2 * skb]), rowscale(vt[2 * skb + 1], sc_u[2 * skb + 1]));
+    const int jb = 2 * w + hs;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 u = zero4();
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) {
+        if (rb <= 1 && skb == 1) continue;
+        u = mma(tf[rb][skb], xu[skb], u);
+      }
+      store_acc<E>(Ua + ((rec_ch * NJ + jb) * 4 + rb) * AREC, lane, u);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// K2: sequential state pass.  One wave per (sequence, head, 16-column block
+// jb of d_v); the columns of the state are independent, so a wave needs no
+// communication: its d_k x 16 state stays in accumulator registers.
+// Per chunk: store the entering state (fragment-native), V' = U - W h,
+// store V', h <- exp(gamma_L) h + Kt^T V'.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void k_fwd_state(Params p, int write_ht) {
+  constexpr int NJ = D / 16, KB = D / 32;
+  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
+  if (unit >= p.N * p.H) return;
+  const int n = unit / p.H, h = unit - n * p.H;
+  const int4 st = p.seq_tab[n];
+  const int c0 = st.x, nc = st.y;
+  const size_t sbase = (size_t)unit * D * D;
+
+  f32x4 hs[NJ];
+#pragma unroll
+  for (int ib = 0; ib < NJ; ++ib) {
+    if (p.h0) {
+      const float* src = p.h0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+      hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+    } else {
+      hs[ib] = zero4();
+    }
+  }
+  const E* Wn = reinterpret_cast<const E*>(p.Wn);
+  const E* Ktf = reinterpret_cast<const E*>(p.Ktf);
+  const E* Ua = reinterpret_cast<const E*>(p.Ua);
+  E* Hf = reinterpret_cast<E*>(p.Hf);
+  E* Vf = reinterpret_cast<E*>(p.Vf);
+
+  for (int ci = 0; ci < nc; ++ci) {
+    const size_t ch = (size_t)(c0 + ci) * p.H + h;
+    frag_t<E> hfr[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+    }
+    f32x4 vp[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) vp[rb] = load_acc<E>(Ua + ((ch * NJ + jb) * 4 + rb) * AREC, lane);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        vp[rb] = mma(load_rec<E>(Wn + ((ch * 4 + rb) * KB + kb) * REC, lane), hfr[kb], vp[rb]);
+    frag_t<E> vfr[2];
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb) {
+      vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
+      store_rec<E>(Vf + ((ch * NJ + jb) * 2 + skb) * REC, lane, vfr[skb]);
+    }
+    const float GL = __expf(p.gamma[ch * 64 + 63]);
+#pragma unroll
+    for (int ib = 0; ib < NJ; ++ib) {
+      f32x4 x = scale4(hs[ib], GL);
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb)
+        x = mma(load_rec<E>(Ktf + ((ch * NJ + ib) * 2 + skb) * REC, lane), vfr[skb], x);
+      hs[ib] = x;
+    }
+  }
+  if (write_ht && p.ht) {
+#pragma unroll
+    for (int ib = 0; ib < NJ; ++ib) {
+      float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+      dst[0] = hs[ib][0];
+      dst[D] = hs[ib][1];
+      dst[2 * D] = hs[ib][2];
+      dst[3 * D] = hs[ib][3];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// K3: output.  Per (chunk, head), 4 waves; wave w computes rows [16w, 16w+16).
+//   O^T[j][r] = Gam_r sum_i h[i][j] Q[r][i] + sum_s V'[s][j] P[r][s]
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_fwd_out(Params p) {
+  constexpr int NJ = D / 16, KB = D / 32;
+  const int ch = blockIdx.x;
+  const int H = p.H;
+  const int c = ch / H, h = ch - c * H;
+  const int4 ct = p.chunk_tab[c];
+  const int tok0 = ct.x, L = ct.y;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
+  const E* Q = reinterpret_cast<const E*>(p.q);
+  const E* K = reinterpret_cast<const E*>(p.k);
+  const E* Hf = reinterpret_cast<const E*>(p.Hf);
+  const E* Vf = reinterpret_cast<const E*>(p.Vf);
+  E* O = reinterpret_cast<E*>(p.o);
+  const float* gam = p.gamma + (size_t)ch * 64;
+
+  const int r = 16 * w + li;
+  const float gr = gam[r];
+  frag_t<E> qf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    qf[kb] = r < L ? load_frag_row<E>(Q + ((size_t)(tok0 + r) * H + h) * D + 32 * kb, lg) : zero_frag<E>();
+
+  // P^T tiles for s-blocks <= w: lane holds P[r][s = 16sb + 4lg + q]
+  f32x4 pt[4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    pt[sb] = zero4();
+    if (sb > w) continue;
+    const int srow = 16 * sb + li;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const frag_t<E> kfr = srow < L ? load_frag_row<E>(K + ((size_t)(tok0 + srow) * H + h) * D + 32 * kb, lg)
+                                     : zero_frag<E>();
+      acc = mma(kfr, qf[kb], acc);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s = 16 * sb + 4 * lg + q;
+      acc[q] = s <= r ? acc[q] * __expf(gr - gam[s]) : 0.f;
+    }
+    pt[sb] = acc;
+  }
+  const frag_t<E> pf0 = to_frag<E>(pt[0], pt[1]);
+  const frag_t<E> pf1 = to_frag<E>(pt[2], pt[3]);
+  const float Gr = __expf(gr);
+  const bool has1 = w >= 2;
+
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc = mma(load_rec<E>(Hf + (((size_t)ch * NJ + jb) * KB + kb) * REC, lane), qf[kb], acc);
+    acc = scale4(acc, Gr);
+    acc = mma(load_rec<E>(Vf + (((size_t)ch * NJ + jb) * 2 + 0) * REC, lane), pf0, acc);
+    if (has1) acc = mma(load_rec<E>(Vf + (((size_t)ch * NJ + jb) * 2 + 1) * REC, lane), pf1, acc);
+    acc = scale4(acc, p.scale);
+    if (r < L)
+      *reinterpret_cast<quad_t<E>*>(O + ((size_t)(tok0 + r) * H + h) * D + 16 * jb + 4 * lg) = to_quad<E>(acc);
+  }
+}
+
+// --------------------------------------------------------------------------
+hipError_t launch_plan(const Params& p, hipStream_t s) {
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_plan, dim3(1), dim3(1024), args, 0, s);
+}
+
+template <typename E, int D>
+static hipError_t fwd_prep_t(const Params& p, hipStream_t s) {
+  if (p.NC == 0) return hipSuccess;
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_fwd_prep<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+}
+template <typename E, int D>
+static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
+  if (p.N * p.H == 0) return hipSuccess;
+  Params a = p;
+  int wh = write_ht ? 1 : 0;
+  void* args[] = {&a, &wh};
+  return hipLaunchKernel((const void*)k_fwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64), args, 0, s);
+}
+template <typename E, int D>
+static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
+  if (p.NC == 0) return hipSuccess;
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_fwd_out<E, D>, dim3(p.NC * p.H), dim3(256), args, 0, s);
+}
+
+#define GDN_DISPATCH(fn, ...)                                        \
+  do {                                                               \
+    if (is_bf16) {                                                   \
+      if (D == 64) return fn<bf16, 64>(__VA_ARGS__);                 \
+      if (D == 128) return fn<bf16, 128>(__VA_ARGS__);               \
+    } else {                                                         \
+      if (D == 64) return fn<float, 64>(__VA_ARGS__);                \
+      if (D == 128) return fn<float, 128>(__VA_ARGS__);              \
+    }                                                                \
+    return hipErrorInvalidValue;                                     \
+  } while (0)
+
+hipError_t launch_fwd_prep(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(fwd_prep_t, p, s); }
+hipError_t launch_fwd_state(const Params& p, int D, bool is_bf16, bool write_ht, hipStream_t s) {
+  GDN_DISPATCH(fwd_state_t, p, write_ht, s);
+}
+hipError_t launch_fwd_out(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(fwd_out_t, p, s); }
+
+}  // namespace gdn

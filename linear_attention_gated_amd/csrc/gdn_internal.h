@@ -1,0 +1,71 @@
+// gdn_internal.h -- parameters and workspace layout shared by the host
+// planner (api.cpp) and the kernels (*.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int CHUNK = 64;   // chunk length of the chunked form
+constexpr int REC = 512;    // elements per fragment record (64 lanes x 8)
+constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
+
+// Record counts per (chunk, head), for head dim D:
+//   Wn  F(-W; r, i)      [4][D/32]        forward WY factor, negated
+//   Ktf F(Kt; i, s)      [D/16][2]        decayed keys, transposed
+//   Ua  acc U[r][j]      [D/16][4]        WY values (accumulator records)
+//   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
+//   Vf  F(V'; j, s)      [D/16][2]        corrected values
+//   QgT F(s*Gam*Q; i, r) [D/16][2]        backward: scaled queries, transposed
+//   dOf F(dO; j, r)      [D/16][2]        backward: upstream grad, transposed
+//   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
+//   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
+//   dVl acc dV'loc[s][j] [D/16][4] fp32   backward: intra-chunk part of dV'
+//   HPf F(H'; j, i)      [D/16][D/32]     backward: state gradient after the chunk
+//   dVf F(dV'; j, r)     [D/16][2]        backward: gradient of V'
+struct Params {
+  int H, N, NC;           // heads, sequences, chunks
+  float scale;
+  int dense_T;            // tokens per sequence when dense (cu == nullptr)
+  int total_tokens;       // B * T
+  const int32_t* cu;      // device cu_seqlens or nullptr
+
+  const void *q, *k, *v;
+  const float *g, *beta, *h0;
+  const void* dO;
+  const float* dht;
+
+  void* o;
+  float* ht;
+  void *dq, *dk, *dv;
+  float *dg, *dbeta, *dh0;
+
+  int4* chunk_tab;        // per chunk: first token, length, sequence, index in sequence
+  int4* seq_tab;          // per sequence: first chunk, chunk count, first token, length
+
+  float* gamma;           // [NC][H][64] chunk-local cumulative log decay
+  void *Wn, *Ktf, *Ua, *Hf, *Vf;
+  void *QgT, *dOf, *WnT, *Ktn, *HPf, *dVf;
+  float* dVl;
+};
+
+// Launchers (each returns the first launch error, hipSuccess otherwise).
+hipError_t launch_plan(const Params& p, hipStream_t s);
+hipError_t launch_fwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_fwd_state(const Params& p, int D, bool bf16, bool write_ht, hipStream_t s);
+hipError_t launch_fwd_out(const Params& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_bwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_bwd_state(const Params& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_bwd_grad(const Params& p, int D, bool bf16, hipStream_t s);
+
+// Grid of the sequential kernels: one wave per (sequence, head, 16-column
+// block), padded so that the column blocks of one (sequence, head) share an
+// XCD (workgroup ids are dealt round-robin over the 8 XCDs).
+inline int state_grid(int units, int D) {
+  const int nj = D / 16;
+  const int groups = (units + 7) / 8;
+  return groups * 8 * nj;
+}
+
+}  // namespace gdn

@@ -1,0 +1,169 @@
+"""The C ABI on the host: the library loads without a GPU, exports what
+include/gdn.h declares, and rejects every invalid argument before any HIP
+call.  CPU only: every call below is invalid by construction (each case breaks
+exactly one check), so no kernel is ever launched on the fake pointers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_gated_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    lib = gdn.lib()
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.lib().gdn_abi_version() == 1
+    assert gdn.status_string(0) == "GDN_OK"
+    assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_problem_struct_layout():
+    # int64 x7, two pointers, float, enum(int) -> 80 bytes on x86-64
+    assert ctypes.sizeof(gdn.GdnProblem) == 80
+
+
+FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation
+
+
+def base_problem(**kw):
+    p = gdn.GdnProblem()
+    p.batch, p.seqlen, p.heads, p.dk, p.dv, p.chunk = 1, 256, 2, 64, 64, 64
+    p.num_seqs = 0
+    p.cu_seqlens_host = None
+    p.cu_seqlens_dev = None
+    p.scale = 1.0
+    p.dtype = gdn.GDN_BF16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def fwd_ptrs(p, ws_bytes=None, **over):
+    T = p.batch * p.seqlen
+    qk = T * p.heads * max(p.dk, 1) * (2 if p.dtype == gdn.GDN_BF16 else 4)
+    gb = T * p.heads * 4
+    sb = max(p.num_seqs if p.cu_seqlens_host else p.batch, 1) * p.heads * 64 * 64 * 4
+    base = FAKE
+    ptrs = {}
+    for name, size in (("q", qk), ("k", qk), ("v", qk), ("g", gb), ("beta", gb), ("h0", sb),
+                       ("o", qk), ("ht", sb)):
+        ptrs[name] = base
+        base += (size + 4095) // 4096 * 4096 + 4096
+    ptrs["ws"] = base
+    ptrs.update(over)
+    need = gdn.lib().gdn_fwd_workspace_bytes(ctypes.byref(p))
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return ptrs, ws_bytes
+
+
+def call_fwd(p, ws_bytes=None, **over):
+    ptrs, wsb = fwd_ptrs(p, ws_bytes, **over)
+    P = ctypes.c_void_p
+    st = gdn.lib().gdn_fwd(ctypes.byref(p), P(ptrs["q"]), P(ptrs["k"]), P(ptrs["v"]), P(ptrs["g"]),
+                           P(ptrs["beta"]), P(ptrs["h0"]), P(ptrs["o"]), P(ptrs["ht"]),
+                           P(ptrs["ws"]), wsb, None)
+    return st, gdn.last_error_message()
+
+
+def test_workspace_query_valid_and_invalid():
+    L = gdn.lib()
+    p = base_problem()
+    f = L.gdn_fwd_workspace_bytes(ctypes.byref(p))
+    b = L.gdn_bwd_workspace_bytes(ctypes.byref(p))
+    assert f > 0 and b > f and f % 256 == 0
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(base_problem(dk=96, dv=96))) == 0
+    assert L.gdn_fwd_workspace_bytes(None) == 0
+
+
+CASES = [
+    ("dk_not_dv", dict(dv=128), {}, gdn.GDN_ERR_UNSUPPORTED, "dk"),
+    ("dim_96", dict(dk=96, dv=96), {}, gdn.GDN_ERR_UNSUPPORTED, "head dim"),
+    ("chunk_32", dict(chunk=32), {}, gdn.GDN_ERR_UNSUPPORTED, "chunk"),
+    ("dtype_7", dict(dtype=7), {}, gdn.GDN_ERR_UNSUPPORTED, "dtype"),
+    ("heads_0", dict(heads=0), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "heads"),
+    ("batch_0", dict(batch=0), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "batch"),
+    ("seqlen_neg", dict(seqlen=-1), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "seqlen"),
+    ("scale_nan", dict(scale=float("nan")), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "scale"),
+    ("null_q", {}, dict(q=0), gdn.GDN_ERR_INVALID_ARGUMENT, "q is NULL"),
+    ("null_beta", {}, dict(beta=0), gdn.GDN_ERR_INVALID_ARGUMENT, "beta is NULL"),
+    ("null_ws", {}, dict(ws=0), gdn.GDN_ERR_INVALID_ARGUMENT, "workspace is NULL"),
+    ("misaligned_k", {}, dict(k=FAKE + 8), gdn.GDN_ERR_INVALID_ARGUMENT, "aligned"),
+    ("misaligned_ws", {}, dict(ws=FAKE + (1 << 36) + 16), gdn.GDN_ERR_INVALID_ARGUMENT,
+     "256-byte"),
+    ("o_aliases_q", {}, dict(o=FAKE), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("ht_aliases_h0", {}, dict(ht="h0"), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("name,pkw,pover,status,msg", CASES, ids=[c[0] for c in CASES])
+def test_invalid_arguments(name, pkw, pover, status, msg):
+    p = base_problem(**pkw)
+    if pover.get("ht") == "h0":
+        ptrs, _ = fwd_ptrs(p)
+        pover = dict(ht=ptrs["h0"] + 64)
+    st, m = call_fwd(p, **pover)
+    assert st == status, (st, m)
+    assert msg in m, m
+
+
+def test_workspace_too_small():
+    p = base_problem()
+    need = gdn.lib().gdn_fwd_workspace_bytes(ctypes.byref(p))
+    st, m = call_fwd(p, ws_bytes=need - 256)
+    assert st == gdn.GDN_ERR_WORKSPACE_TOO_SMALL, m
+
+
+def _varlen(cu, **kw):
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    p = base_problem(seqlen=cu[-1], num_seqs=len(cu) - 1,
+                     cu_seqlens_host=ctypes.addressof(arr), cu_seqlens_dev=FAKE + (1 << 40), **kw)
+    return p, arr
+
+
+@pytest.mark.parametrize("cu,msg", [([1, 5, 9], "cu_seqlens[0]"), ([0, 9, 5], "decreases"),
+                                    ([0, 4, 9], None)])
+def test_varlen_validation(cu, msg):
+    p, arr = _varlen(cu)
+    if msg is None:
+        # consistent cu_seqlens, but seqlen disagrees with cu[N]
+        p.seqlen = 10
+        msg = "seqlen"
+    st, m = call_fwd(p)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and msg in m, m
+
+
+def test_varlen_needs_batch_one_and_both_copies():
+    p, arr = _varlen([0, 4, 9], batch=2)
+    st, m = call_fwd(p)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "batch" in m
+    p, arr = _varlen([0, 4, 9])
+    p.cu_seqlens_dev = None
+    st, m = call_fwd(p)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "both" in m
+
+
+def test_bwd_rejects_missing_outputs():
+    p = base_problem()
+    P = ctypes.c_void_p
+    args = [P(FAKE + i * (1 << 30)) for i in range(15)]
+    args[11] = None  # dg (order: q k v g beta h0 do dht dq dk dv dg dbeta dh0 fwd_ws)
+    st = gdn.lib().gdn_bwd(ctypes.byref(p), *args, P(FAKE + (1 << 36)),
+                           gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(p)), None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "dg is NULL" in gdn.last_error_message()
