@@ -1,9 +1,835 @@
-// bwd.hip -- backward kernels (in progress).
+// bwd.hip -- backward kernels of the gated delta rule (chunked form).
+//
+// Per chunk, with the forward quantities of fwd.hip (gamma, D, A, T, W, U,
+// V', entering state h) and H' = dL/dh' (gradient of the state leaving the
+// chunk), and Q scaled by `scale`:
+//   dV'  = P^T dO + Kt H'                  P = (Q K^T) * D, lower incl. diagonal
+//   dh   = exp(gamma_L) H' + (Gam Q)^T dO - W^T dV'     (becomes H' of the previous chunk)
+//   dP   = dO V'^T (lower)
+//   dQ   = Gam dO h^T + (dP * D) K
+//   dK   = (dP * D)^T Q + diag(exp(gamma_L - gamma)) V' H'^T + diag(beta Gam) T^T dW
+//          + (E + E^T) K,      E = dA * beta_r D (strict lower)
+//   dW   = -dV' h^T,  dU = dV',  dT = dW Xw^T + dU Xu^T  (Xw = diag(beta Gam) K, Xu = diag(beta) V)
+//   dA   = strict_lower(-T^T dT T^T)
+//   dV   = diag(beta) T^T dU
+//   dbeta_r = Gam_r k_r.(T^T dW)_r + v_r.(T^T dU)_r + sum_s dA_rs (K K^T * D)_rs
+//   dgamma collects the decay terms (output, P, Xw, A, Kt and the state decay);
+//   dg_s = sum_{r >= s} dgamma_r within the chunk.
+// These are the reverse-mode equations of the chunked forward; the kernel
+// split follows the native family in the XTuner / Ascend 910C article
+// (section 3.1.2, Fig. 7): a local dv step (K4), the reverse pass through the
+// state-transition chain (K5) and the dq/dk/dw/dg projection with the WY
+// backward folded in (K6).
 #include "frag.h"
 #include "gdn_internal.h"
 
 namespace gdn {
-hipError_t launch_bwd_prep(const Params&, int, bool, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_bwd_state(const Params&, int, bool, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_bwd_grad(const Params&, int, bool, hipStream_t) { return hipErrorNotSupported; }
+
+// --------------------------------------------------------------------------
+// K4: per (chunk, head), D/32 waves; wave w owns feature columns [32w, 32w+32).
+// Writes the fragment-native operands of the reverse pass:
+//   Ktn = F(Kt; s, i), QgT = F(scale*Gam*Q; i, r), dOf = F(dO; j, r),
+//   WnT = F(-W; i, r), and dVl = P^T dO (accumulator records, fp32).
+template <typename E, int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
+  constexpr int KB = D / 32, NJ = D / 16;
+  __shared__ float s_gam[64];
+  const int ch = blockIdx.x;
+  const int H = p.H;
+  const int c = ch / H, h = ch - c * H;
+  const int4 ct = p.chunk_tab[c];
+  const int tok0 = ct.x, L = ct.y;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
+  const E* Q = reinterpret_cast<const E*>(p.q);
+  const E* K = reinterpret_cast<const E*>(p.k);
+  const E* dO = reinterpret_cast<const E*>(p.dO);
+  const E* Wn = reinterpret_cast<const E*>(p.Wn);
+  E* Ktn = reinterpret_cast<E*>(p.Ktn);
+  E* QgT = reinterpret_cast<E*>(p.QgT);
+  E* dOf = reinterpret_cast<E*>(p.dOf);
+  E* WnT = reinterpret_cast<E*>(p.WnT);
+  if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
+  __syncthreads();
+  const float gL = s_gam[63];
+  const float sc = p.scale;
+  const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
+  auto row_ptr = [&](const E* X, int row, int kb) { return X + ((size_t)(tok0 + row) * H + h) * D + 32 * kb; };
+  auto nat = [&](const E* X, int row, int kb) {
+    return row < L ? load_frag_row<E>(row_ptr(X, row, kb), lg) : zero_frag<E>();
+  };
+
+  // Ktn records (sb, kb = w): natural key rows scaled by exp(gamma_L - gamma_s)
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int s = 16 * sb + li;
+    f32x8 x = frag_to_f32<E>(nat(K, s, w));
+    const float f = __expf(gL - s_gam[s]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= f;
+    store_rec<E>(Ktn + (((size_t)ch * 4 + sb) * KB + w) * REC, lane, f32_to_frag<E>(x));
+  }
+
+  // transposes of this wave's slice of Q (scaled), dO and -W
+  frag_t<E> dof[2][2];  // F(dO; j, r) for jb = 2w + hs, rkb
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const frag_t<E> idh = hs ? id1 : id0;
+    f32x4 tq[4], td[4], tw[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + li;
+      tq[rb] = mma(nat(Q, r, w), idh, zero4());
+      td[rb] = mma(nat(dO, r, w), idh, zero4());
+      tw[rb] = mma(load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane), idh, zero4());
+      // tq lane holds Q[r = 16rb + 4lg + q][i = 32w + 16hs + li]
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tq[rb][q] *= sc * __expf(s_gam[16 * rb + 4 * lg + q]);
+    }
+    const int ib = 2 * w + hs;
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb) {
+      store_rec<E>(QgT + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, to_frag<E>(tq[2 * rkb], tq[2 * rkb + 1]));
+      dof[hs][rkb] = to_frag<E>(td[2 * rkb], td[2 * rkb + 1]);
+      store_rec<E>(dOf + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, dof[hs][rkb]);
+      store_rec<E>(WnT + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, to_frag<E>(tw[2 * rkb], tw[2 * rkb + 1]));
+    }
+  }
+
+  // P = scale (Q K^T) * D (lower incl. diagonal); lane holds P[r = 16rb + 4lg + q][s = 16sb + li]
+  f32x4 pt[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) pt[rb][sb] = zero4();
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+    for (int sb = 0; sb <= rb; ++sb) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mma(nat(Q, 16 * rb + li, kb), nat(K, 16 * sb + li, kb), acc);
+      const int s = 16 * sb + li;
+      const float gs = s_gam[s];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * rb + 4 * lg + q;
+        acc[q] = s <= r ? sc * acc[q] * __expf(s_gam[r] - gs) : 0.f;
+      }
+      pt[rb][sb] = acc;
+    }
+  }
+  // dVl[s][j] = sum_r P[r][s] dO[r][j]
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const int jb = 2 * w + hs;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        if (2 * rkb + 1 < sb) continue;
+        acc = mma(to_frag<E>(pt[2 * rkb][sb], pt[2 * rkb + 1][sb]), dof[hs][rkb], acc);
+      }
+      store_acc<float>(p.dVl + (((size_t)ch * NJ + jb) * 4 + sb) * AREC, lane, acc);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// K5: reverse state-gradient pass.  One wave per (sequence, head, 16-column
+// block jb of d_v); the d_k x 16 slice of H' stays in accumulator registers.
+// Per chunk (last to first): store H' (fragment-native), dV' = dVl + Kt H',
+// store dV', H' <- exp(gamma_L) H' + (scale Gam Q)^T dO - W^T dV'.
+template <typename E, int D>
+__global__ __launch_bounds__(64) void k_bwd_state(Params p) {
+  constexpr int NJ = D / 16, KB = D / 32;
+  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
+  if (unit >= p.N * p.H) return;
+  const int n = unit / p.H, h = unit - n * p.H;
+  const int4 st = p.seq_tab[n];
+  const int c0 = st.x, nc = st.y;
+  const size_t sbase = (size_t)unit * D * D;
+
+  f32x4 hs[NJ];
+#pragma unroll
+  for (int ib = 0; ib < NJ; ++ib) {
+    if (p.dht) {
+      const float* src = p.dht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+      hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+    } else {
+      hs[ib] = zero4();
+    }
+  }
+  const E* Ktn = reinterpret_cast<const E*>(p.Ktn);
+  const E* QgT = reinterpret_cast<const E*>(p.QgT);
+  const E* dOf = reinterpret_cast<const E*>(p.dOf);
+  const E* WnT = reinterpret_cast<const E*>(p.WnT);
+  E* HPf = reinterpret_cast<E*>(p.HPf);
+  E* dVf = reinterpret_cast<E*>(p.dVf);
+
+  for (int ci = nc - 1; ci >= 0; --ci) {
+    const size_t ch = (size_t)(c0 + ci) * p.H + h;
+    frag_t<E> hfr[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+    }
+    f32x4 dv[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      dv[sb] = load_acc<float>(p.dVl + ((ch * NJ + jb) * 4 + sb) * AREC, lane);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) dv[sb] = mma(load_rec<E>(Ktn + ((ch * 4 + sb) * KB + kb) * REC, lane), hfr[kb], dv[sb]);
+    }
+    frag_t<E> dvf[2], dof[2];
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb) {
+      dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
+      store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
+      dof[rkb] = load_rec<E>(dOf + ((ch * NJ + jb) * 2 + rkb) * REC, lane);
+    }
+    const float GL = __expf(p.gamma[ch * 64 + 63]);
+#pragma unroll
+    for (int ib = 0; ib < NJ; ++ib) {
+      f32x4 x = scale4(hs[ib], GL);
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        x = mma(load_rec<E>(QgT + ((ch * NJ + ib) * 2 + rkb) * REC, lane), dof[rkb], x);
+        x = mma(load_rec<E>(WnT + ((ch * NJ + ib) * 2 + rkb) * REC, lane), dvf[rkb], x);
+      }
+      hs[ib] = x;
+    }
+  }
+  if (p.dh0) {
+#pragma unroll
+    for (int ib = 0; ib < NJ; ++ib) {
+      float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+      dst[0] = hs[ib][0];
+      dst[D] = hs[ib][1];
+      dst[2 * D] = hs[ib][2];
+      dst[3 * D] = hs[ib][3];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// K6: per (chunk, head) gradients dq, dk, dv, dbeta, dg.  D/32 waves; wave w
+// owns feature columns [32w, 32w+32) of dq/dk (i) and dv (j).  Quantities
+// that need every column (dP, dW for dT, T, dT, dA, E) are shared through
+// LDS; sums over waves use per-wave slots so the result is deterministic.
+template <typename E, int D>
+struct BwdGradSmem {
+  static constexpr int KB = D / 32;
+  static constexpr int LDF = 68;
+  static constexpr int MAT = 64 * LDF * 4;             // fp32 64x64, padded rows
+  static constexpr int RECB = REC * (int)sizeof(E);
+  static constexpr int NREC = 4 * KB;                  // records of a 64 x D fragment set
+  static constexpr int SET = NREC * RECB;
+  static constexpr int UNI = (2 * SET > MAT) ? 2 * SET : MAT;  // dV'^T + dW, later M1
+  static constexpr int oAp = 0;
+  static constexpr int oT = oAp + MAT;
+  static constexpr int odP = oT + MAT;
+  static constexpr int oEE = odP + MAT;
+  static constexpr int oVt = oEE + MAT;
+  static constexpr int oU = oVt + SET;                 // sdVt | sdW, later sM1
+  static constexpr int odTt = oU + UNI;                // also the solve scratch
+  static constexpr int oSm = odTt + MAT;
+  static constexpr int NW = D / 32;
+  static constexpr int SMALL = (64 * 2 + NW * 64 * 2 + NW * 2) * 4;
+  static constexpr int BYTES = oSm + SMALL;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
+  using S = BwdGradSmem<E, D>;
+  constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDF = S::LDF;
+  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+  float* sAp = reinterpret_cast<float*>(smem + S::oAp);
+  float* sT = reinterpret_cast<float*>(smem + S::oT);
+  float* sdP = reinterpret_cast<float*>(smem + S::odP);
+  float* sEE = reinterpret_cast<float*>(smem + S::oEE);
+  E* sVt = reinterpret_cast<E*>(smem + S::oVt);
+  E* sdVt = reinterpret_cast<E*>(smem + S::oU);
+  E* sdW = reinterpret_cast<E*>(smem + S::oU + S::SET);
+  float* sM1 = reinterpret_cast<float*>(smem + S::oU);
+  float* sdTt = reinterpret_cast<float*>(smem + S::odTt);
+  float* sX = sdTt;
+  float* s_gam = reinterpret_cast<float*>(smem + S::oSm);
+  float* s_beta = s_gam + 64;
+  float* s_pg = s_beta + 64;          // [NW][64] dgamma partials
+  float* s_pb = s_pg + NW * 64;       // [NW][64] dbeta partials
+  float* s_misc = s_pb + NW * 64;     // [NW][2]: sum_s c_s, <h, H'>
+
+  const int ch = blockIdx.x;
+  const int H = p.H;
+  const int c = ch / H, h = ch - c * H;
+  const int4 ct = p.chunk_tab[c];
+  const int tok0 = ct.x, L = ct.y;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * NW;
+  const E* Q = reinterpret_cast<const E*>(p.q);
+  const E* K = reinterpret_cast<const E*>(p.k);
+  const E* V = reinterpret_cast<const E*>(p.v);
+  const E* dO = reinterpret_cast<const E*>(p.dO);
+  const E* Hf = reinterpret_cast<const E*>(p.Hf);
+  const E* Vf = reinterpret_cast<const E*>(p.Vf);
+  const E* HPf = reinterpret_cast<const E*>(p.HPf);
+  const E* dVf = reinterpret_cast<const E*>(p.dVf);
+  const float sc = p.scale;
+
+  auto row_ptr = [&](const E* X, int row, int kb) { return X + ((size_t)(tok0 + row) * H + h) * D + 32 * kb; };
+  auto nat = [&](const E* X, int row, int kb) {
+    return row < L ? load_frag_row<E>(row_ptr(X, row, kb), lg) : zero_frag<E>();
+  };
+  // fragment of a row-major fp32 64x64 LDS matrix: index rows 16ab.., contraction cols 32kb..
+  auto mfrag = [&](const float* M, int ab, int kb) {
+    const float* row = M + (16 * ab + li) * LDF + 32 * kb;
+    return to_frag<E>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
+  };
+  auto mfrag32 = [&](const float* M, int ab, int kb) {
+    const float* row = M + (16 * ab + li) * LDF + 32 * kb;
+    return to_frag<float>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
+  };
+  // same matrix read transposed: index = columns 16cb.., contraction = rows 32kb..
+  auto mfragT32 = [&](const float* M, int cb, int kb) {
+    f32x8 t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = M[(32 * kb + kslot(lg, e)) * LDF + 16 * cb + li];
+    return t;
+  };
+  auto mfragT = [&](const float* M, int cb, int kb) { return f32_to_frag<E>(mfragT32(M, cb, kb)); };
+  auto lrec = [&](const E* base, int a, int kb) { return load_rec<E>(base + (a * KB + kb) * REC, lane); };
+
+  // ---- setup
+  {
+    float gv = p.gamma[(size_t)ch * 64 + lane];
+    float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
+    if (w == 0) {
+      s_gam[lane] = gv;
+      s_beta[lane] = bv;
+    }
+    for (int e = tid; e < NW * 64 * 2 + NW * 2; e += NT) s_pg[e] = 0.f;  // s_pg, s_pb, s_misc
+    for (int e = tid; e < 64 * 64; e += NT) {
+      const int r = e >> 6, s = e & 63;
+      if ((s >> 4) > (r >> 4)) sT[r * LDF + s] = 0.f;
+      sEE[r * LDF + s] = 0.f;
+    }
+  }
+  __syncthreads();
+  const float gL = s_gam[63];
+  const float GL = __expf(gL);
+  const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
+
+  // ---- A' = (K K^T) * D (strict lower) and T = (I + diag(beta) A')^-1
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rr = TR[t], scb = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mma(nat(K, 16 * scb + li, kb), nat(K, 16 * rr + li, kb), acc);
+      const int r = 16 * rr + li;
+      const float gr = s_gam[r];
+      float4 out;
+      float* po = reinterpret_cast<float*>(&out);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s = 16 * scb + 4 * lg + q;
+        po[q] = s < r ? acc[q] * __expf(gr - s_gam[s]) : 0.f;
+      }
+      *reinterpret_cast<float4*>(&sAp[r * LDF + 16 * scb + 4 * lg]) = out;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int b0 = 16 * lg, j = li;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float br = s_beta[b0 + r];
+      float acc = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= br * sAp[(b0 + r) * LDF + b0 + s] * t[s];
+      t[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDF + b0 + j] = t[r];
+  }
+  __syncthreads();
+  for (int d = 1; d < 4; ++d) {
+    const int nblk = 4 - d;
+    for (int e = tid; e < nblk * 256; e += NT) {
+      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
+      const float br = s_beta[16 * a + r];
+      float x = 0.f;
+      for (int kk = 16 * b; kk < 16 * a; ++kk) x += sAp[(16 * a + r) * LDF + kk] * sT[kk * LDF + 16 * b + col];
+      sX[e] = br * x;
+    }
+    __syncthreads();
+    for (int e = tid; e < nblk * 256; e += NT) {
+      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
+      const float* xb = sX + (e / 256) * 256;
+      float x = 0.f;
+      for (int kk = 0; kk <= r; ++kk) x += sT[(16 * a + r) * LDF + 16 * a + kk] * xb[kk * 16 + col];
+      sT[(16 * a + r) * LDF + 16 * b + col] = -x;
+    }
+    __syncthreads();
+  }
+
+  // ---- transposes of this wave's column slice of V' and dV' into LDS:
+  //      sVt rec (sb, w) = F(V'; s, j), sdVt rec (rb, w) = F(dV'; r, j)
+  {
+#pragma unroll
+    for (int sbp = 0; sbp < 4; ++sbp) {
+      const frag_t<E> idh = (sbp & 1) ? id1 : id0;
+      const int skb = sbp >> 1;
+      f32x4 a0 = mma(load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w) * 2 + skb) * REC, lane), idh, zero4());
+      f32x4 a1 = mma(load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + 1) * 2 + skb) * REC, lane), idh, zero4());
+      store_rec<E>(sVt + (sbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
+      f32x4 b0 = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w) * 2 + skb) * REC, lane), idh, zero4());
+      f32x4 b1 = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + 1) * 2 + skb) * REC, lane), idh, zero4());
+      store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
+    }
+    // zero the blocks of dT^T that no tile writes (rows s of a higher block than r)
+    for (int e = tid; e < 64 * 64; e += NT) {
+      const int s = e >> 6, r = e & 63;
+      if ((s >> 4) > (r >> 4)) sdTt[s * LDF + r] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  float* pg = s_pg + w * 64;
+  float* pb = s_pb + w * 64;
+
+  // ---- dP = dO V'^T and P (lower tiles, round-robin): sdP = dP * D,
+  //      dgamma += rowsum(dP * P) - colsum(dP * P)
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rb = TR[t], sb = TS[t];
+      f32x4 dp = zero4(), qk = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        dp = mma(nat(dO, 16 * rb + li, kb), lrec(sVt, sb, kb), dp);
+        qk = mma(nat(Q, 16 * rb + li, kb), nat(K, 16 * sb + li, kb), qk);
+      }
+      // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
+      const int s = 16 * sb + li;
+      const float gs = s_gam[s];
+      float rs[4], cs = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * rb + 4 * lg + q;
+        const float Dm = s <= r ? __expf(s_gam[r] - gs) : 0.f;
+        const float dpd = dp[q] * Dm;
+        sdP[r * LDF + s] = dpd;
+        const float mo = dpd * sc * qk[q];
+        rs[q] = mo;
+        cs += mo;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rs[q] = sum_in_group(rs[q]);
+      cs = sum_groups(cs);
+      if (li == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pg[16 * rb + 4 * lg + q] += rs[q];
+      }
+      if (lg == 0) pg[s] -= cs;
+    }
+    // upper blocks of dP * D are zero
+    for (int e = tid; e < 64 * 64; e += NT) {
+      const int r = e >> 6, s = e & 63;
+      if ((s >> 4) > (r >> 4)) sdP[r * LDF + s] = 0.f;
+    }
+  }
+
+  // ---- transposes of h and H' for this wave's i-slice; dW = -dV' h^T
+  frag_t<E> hT[2][KB], hpT[2][KB];   // F(h; i, j), F(H'; i, j) for i-block 2w + hs
+  {
+    float hh = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      const frag_t<E> idh = hs ? id1 : id0;
+#pragma unroll
+      for (int jkb = 0; jkb < KB; ++jkb) {
+        const f32x4 a0 = mma(load_rec<E>(Hf + (((size_t)ch * NJ + 2 * jkb) * KB + w) * REC, lane), idh, zero4());
+        const f32x4 a1 = mma(load_rec<E>(Hf + (((size_t)ch * NJ + 2 * jkb + 1) * KB + w) * REC, lane), idh, zero4());
+        hT[hs][jkb] = to_frag<E>(a0, a1);
+        const f32x4 b0 = mma(load_rec<E>(HPf + (((size_t)ch * NJ + 2 * jkb) * KB + w) * REC, lane), idh, zero4());
+        const f32x4 b1 = mma(load_rec<E>(HPf + (((size_t)ch * NJ + 2 * jkb + 1) * KB + w) * REC, lane), idh, zero4());
+        hpT[hs][jkb] = to_frag<E>(b0, b1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hh += a0[q] * b0[q] + a1[q] * b1[q];
+      }
+    }
+    hh = sum_in_group(sum_groups(hh));
+    if (lane == 0) s_misc[2 * w + 1] = hh;
+  }
+  frag_t<E> dWir[2][2];  // F(dW; i, r) for i-block 2w + hs, rkb
+  {
+    f32x4 dw[4][2];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int jkb = 0; jkb < KB; ++jkb) acc = mma(lrec(sdVt, rb, jkb), hT[hs][jkb], acc);
+        dw[rb][hs] = -acc;   // lane holds dW[r = 16rb + 4lg + q][i = 32w + 16hs + li]
+      }
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) dWir[hs][rkb] = to_frag<E>(dw[2 * rkb][hs], dw[2 * rkb + 1][hs]);
+    // F(dW; r, i) records (rb, w) for the dT product
+#pragma unroll
+    for (int rbp = 0; rbp < 4; ++rbp) {
+      const frag_t<E> idh = (rbp & 1) ? id1 : id0;
+      const f32x4 a0 = mma(dWir[0][rbp >> 1], idh, zero4());
+      const f32x4 a1 = mma(dWir[1][rbp >> 1], idh, zero4());
+      store_rec<E>(sdW + (rbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
+    }
+  }
+  __syncthreads();
+
+  // ---- dT = dW Xw^T + dV' Xu^T (lower tiles, round-robin) -> sdTt[s][r], strict lower only
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rb = TR[t], sb = TS[t];
+      const int s = 16 * sb + li;
+      const float bs = s_beta[s], bgs = bs * __expf(s_gam[s]);
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x8 xw = frag_to_f32<E>(nat(K, s, kb));
+        f32x8 xu = frag_to_f32<E>(nat(V, s, kb));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          xw[e] *= bgs;
+          xu[e] *= bs;
+        }
+        acc = mma(lrec(sdW, rb, kb), f32_to_frag<E>(xw), acc);
+        acc = mma(lrec(sdVt, rb, kb), f32_to_frag<E>(xu), acc);
+      }
+      // lane holds dT[r = 16rb + 4lg + q][s]
+      float4 out;
+      float* po = reinterpret_cast<float*>(&out);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s ? acc[q] : 0.f;
+      *reinterpret_cast<float4*>(&sdTt[s * LDF + 16 * rb + 4 * lg]) = out;
+    }
+  }
+  __syncthreads();
+
+  // ---- M1 = T^T dT (fp32): M1[a][s] = sum_r T[r][a] dT[r][s]; tiles s-block <= a-block -> sM1[a][s]
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int ab = TR[t], sb = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        if (32 * rkb + 31 < 16 * ab) continue;   // T[r][a] = 0 for r < a
+        acc = mma(mfrag32(sdTt, sb, rkb), mfragT32(sT, ab, rkb), acc);
+      }
+      // lane holds M1[a = 16ab + li][s = 16sb + 4lg + q]
+      *reinterpret_cast<f32x4*>(&sM1[(16 * ab + li) * LDF + 16 * sb + 4 * lg]) = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int ab = TR[t], bb = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) {
+        if (32 * skb > 16 * bb + 15) continue;   // T[b][s] = 0 for s > b
+        acc = mma(mfrag32(sM1, ab, skb), mfrag32(sT, bb, skb), acc);
+      }
+      // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li]
+      const int b = 16 * bb + li;
+      const float gb = s_gam[b];
+      float rs_b[4], rs_g[4], cs = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = 16 * ab + 4 * lg + q;
+        float da = 0.f, ap = 0.f, Dm = 0.f;
+        if (a > b) {
+          da = -acc[q];
+          ap = sAp[a * LDF + b];
+          Dm = __expf(s_gam[a] - gb);
+        }
+        const float ba = s_beta[a];
+        rs_b[q] = da * ap;
+        const float ma = da * ba * ap;
+        rs_g[q] = ma;
+        cs += ma;
+        if (a > b) {
+          const float ev = da * ba * Dm;
+          sEE[a * LDF + b] = ev;
+          sEE[b * LDF + a] = ev;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rs_b[q] = sum_in_group(rs_b[q]);
+        rs_g[q] = sum_in_group(rs_g[q]);
+      }
+      cs = sum_groups(cs);
+      if (li == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          pb[16 * ab + 4 * lg + q] += rs_b[q];
+          pg[16 * ab + 4 * lg + q] += rs_g[q];
+        }
+      }
+      if (lg == 0) pg[b] -= cs;
+    }
+  }
+  __syncthreads();
+
+  // ---- per-wave outputs
+  // K and Q transposes for this wave's i-slice: F(K; i, s), F(Q; i, r)
+  frag_t<E> kT[2][2], qT[2][2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs) {
+    const frag_t<E> idh = hs ? id1 : id0;
+    f32x4 tk[4], tq[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      tk[sb] = mma(nat(K, 16 * sb + li, w), idh, zero4());
+      tq[sb] = mma(nat(Q, 16 * sb + li, w), idh, zero4());
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      kT[hs][kb2] = to_frag<E>(tk[2 * kb2], tk[2 * kb2 + 1]);
+      qT[hs][kb2] = to_frag<E>(tq[2 * kb2], tq[2 * kb2 + 1]);
+    }
+  }
+
+  // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s])
+  {
+    E* dQ = reinterpret_cast<E*>(p.dq);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + li;
+      f32x4 t1[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int jkb = 0; jkb < KB; ++jkb) {
+        const frag_t<E> dof = nat(dO, r, jkb);
+        t1[0] = mma(hT[0][jkb], dof, t1[0]);
+        t1[1] = mma(hT[1][jkb], dof, t1[1]);
+      }
+      // dgamma(r) += Gam_r sum_i (scale Q[r][i]) t1[i][r]
+      const f32x8 qn = frag_to_f32<E>(nat(Q, r, w));
+      float dot = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dot += qn[q] * t1[0][q] + qn[4 + q] * t1[1][q];
+      dot = sum_groups(dot);
+      const float Gr = __expf(s_gam[r]);
+      if (lg == 0) pg[r] += sc * Gr * dot;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        f32x4 acc = scale4(t1[hs], Gr);
+#pragma unroll
+        for (int skb = 0; skb < 2; ++skb) {
+          if (32 * skb > 16 * rb + 15) continue;
+          acc = mma(kT[hs][skb], mfrag(sdP, rb, skb), acc);
+        }
+        acc = scale4(acc, sc);
+        if (r < L)
+          *reinterpret_cast<quad_t<E>*>(dQ + ((size_t)(tok0 + r) * H + h) * D + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
+      }
+    }
+  }
+
+  // dK^T[i][s] = scale sum_r Q[r][i] dPD[r][s] + exp(gL - g_s) sum_j H'[i][j] V'[s][j]
+  //            + beta_s Gam_s sum_r dW[r][i] T[r][s] + sum_r K[r][i] (E + E^T)[s][r]
+  {
+    E* dK = reinterpret_cast<E*>(p.dk);
+    float csum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int s = 16 * sb + li;
+      const float gs = s_gam[s], Gs = __expf(gs), bs = s_beta[s], ks = __expf(gL - gs);
+      f32x4 ta[2], tb[2], tc[2], td[2];
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        ta[hs] = zero4();
+        tb[hs] = zero4();
+        tc[hs] = zero4();
+        td[hs] = zero4();
+      }
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s], T[r][s] vanish for r < s
+        const frag_t<E> dpT = mfragT(sdP, sb, rkb);
+        const frag_t<E> tT = mfragT(sT, sb, rkb);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          ta[hs] = mma(qT[hs][rkb], dpT, ta[hs]);
+          tc[hs] = mma(dWir[hs][rkb], tT, tc[hs]);
+        }
+      }
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        const frag_t<E> ee = mfrag(sEE, sb, rkb);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) td[hs] = mma(kT[hs][rkb], ee, td[hs]);
+      }
+#pragma unroll
+      for (int jkb = 0; jkb < KB; ++jkb) {
+        const frag_t<E> vt = lrec(sVt, sb, jkb);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) tb[hs] = mma(hpT[hs][jkb], vt, tb[hs]);
+      }
+      // per-s dots with k_s over this wave's i-slice: c_s and k_s . dXw_s
+      const f32x8 kn = frag_to_f32<E>(nat(K, s, w));
+      float dc = 0.f, dx = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dc += kn[q] * tb[0][q] + kn[4 + q] * tb[1][q];
+        dx += kn[q] * tc[0][q] + kn[4 + q] * tc[1][q];
+      }
+      dc = sum_groups(dc) * ks;   // c_s (partial)
+      dx = sum_groups(dx);
+      if (lg == 0) {
+        pg[s] += -dc + bs * Gs * dx;
+        pb[s] += Gs * dx;
+      }
+      csum += (lg == 0) ? dc : 0.f;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        f32x4 acc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = sc * ta[hs][q] + ks * tb[hs][q] + bs * Gs * tc[hs][q] + td[hs][q];
+        if (s < L)
+          *reinterpret_cast<quad_t<E>*>(dK + ((size_t)(tok0 + s) * H + h) * D + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
+      }
+    }
+    csum = sum_in_group(csum);
+    if (lane == 0) s_misc[2 * w] = csum;
+  }
+
+  // dV^T[j][s] = beta_s sum_r dV'[r][j] T[r][s]; dbeta_s += v_s . (T^T dV')_s
+  {
+    E* dV = reinterpret_cast<E*>(p.dv);
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int s = 16 * sb + li;
+      const float bs = s_beta[s];
+      f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        if (32 * rkb + 31 < 16 * sb) continue;
+        const frag_t<E> tT = mfragT(sT, sb, rkb);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs)
+          acc[hs] = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + hs) * 2 + rkb) * REC, lane), tT, acc[hs]);
+      }
+      const f32x8 vn = frag_to_f32<E>(nat(V, s, w));
+      float dot = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dot += vn[q] * acc[0][q] + vn[4 + q] * acc[1][q];
+      dot = sum_groups(dot);
+      if (lg == 0) pb[s] += dot;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+        if (s < L)
+          *reinterpret_cast<quad_t<E>*>(dV + ((size_t)(tok0 + s) * H + h) * D + 32 * w + 16 * hs + 4 * lg) =
+              to_quad<E>(scale4(acc[hs], bs));
+    }
+  }
+  __syncthreads();
+
+  // ---- dgamma -> dg (reverse chunk-local cumsum), dbeta
+  if (w == 0) {
+    const int r = lane;
+    float dgam = 0.f, db = 0.f, ctot = 0.f, hh = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      dgam += s_pg[ww * 64 + r];
+      db += s_pb[ww * 64 + r];
+      ctot += s_misc[2 * ww];
+      hh += s_misc[2 * ww + 1];
+    }
+    if (r == L - 1) dgam += ctot + GL * hh;
+    if (r >= L) dgam = 0.f;
+    // reverse inclusive scan over lanes
+    float x = dgam;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_down(x, off, 64);
+      if (r + off < 64) x += t;
+    }
+    if (r < L) {
+      p.dg[(size_t)(tok0 + r) * H + h] = x;
+      p.dbeta[(size_t)(tok0 + r) * H + h] = db;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+template <typename E, int D>
+static hipError_t bwd_prep_t(const Params& p, hipStream_t s) {
+  if (p.NC == 0) return hipSuccess;
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_bwd_prep<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+}
+template <typename E, int D>
+static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
+  if (p.N * p.H == 0) return hipSuccess;
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_bwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64), args, 0, s);
+}
+template <typename E, int D>
+static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {
+  if (p.NC == 0) return hipSuccess;
+  Params a = p;
+  void* args[] = {&a};
+  return hipLaunchKernel((const void*)k_bwd_grad<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+}
+
+// fp32 with D = 128 needs more LDS than a workgroup has for the gradient
+// kernel; the host rejects that combination before launching anything.
+#define GDN_BWD_DISPATCH(fn, ...)                                    \
+  do {                                                               \
+    if (is_bf16) {                                                   \
+      if (D == 64) return fn<bf16, 64>(__VA_ARGS__);                 \
+      if (D == 128) return fn<bf16, 128>(__VA_ARGS__);               \
+    } else {                                                         \
+      if (D == 64) return fn<float, 64>(__VA_ARGS__);                \
+    }                                                                \
+    return hipErrorInvalidValue;                                     \
+  } while (0)
+
+hipError_t launch_bwd_prep(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_BWD_DISPATCH(bwd_prep_t, p, s); }
+hipError_t launch_bwd_state(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_BWD_DISPATCH(bwd_state_t, p, s); }
+hipError_t launch_bwd_grad(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_BWD_DISPATCH(bwd_grad_t, p, s); }
+
 }  // namespace gdn

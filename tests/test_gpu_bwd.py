@@ -1,0 +1,119 @@
+"""GPU parity of the backward pass (HIP path through the C ABI) against the
+fp64 oracle's reverse-mode token loop, element by element, on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import linear_attention_gated_amd as gdn
+import oracle
+from gpu_util import TOL, dev_inputs, frob, maxrel, say, small_cfg, to_np
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def run_bwd(x, dht=None, scale=1.0, use_context=True):
+    d = dev_inputs(x)
+    dht_t = None if dht is None else torch.from_numpy(dht).float().cuda()
+    ctx = None
+    if use_context:
+        _, _, ctx = gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
+                            cu_seqlens=d["cu"], scale=scale, return_context=True)
+    r = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], initial_state=d["h0"],
+                dht=dht_t, cu_seqlens=d["cu"], scale=scale, context=ctx)
+    torch.cuda.synchronize()
+    return [to_np(t) for t in r]
+
+
+def ref_bwd(x, dht=None, scale=1.0):
+    return oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["h0"], dht,
+                      cu_seqlens=x["cu_seqlens"], scale=scale)
+
+
+def compare(x, dht=None, scale=1.0, label="", use_context=True):
+    say("case", label, "dtype", x["dtype"], "B", x["B"], "T", x["T"], "H", x["H"], "d", x["dk"],
+        "N", x["N"], "context", use_context)
+    got = run_bwd(x, dht, scale, use_context)
+    ref = ref_bwd(x, dht, scale)
+    tol = TOL[x["dtype"]]
+    bad = []
+    for name, a, b in zip(NAMES, got, ref):
+        mr, fr = maxrel(a, b), frob(a, b)
+        say("  %-6s maxrel %.3e  frob %.3e" % (name, mr, fr))
+        if not np.all(np.isfinite(a)):
+            bad.append(name + " non-finite")
+        elif mr > tol["maxrel"] or fr > tol["frob"]:
+            bad.append("%s maxrel %.2e frob %.2e" % (name, mr, fr))
+    assert not bad, bad
+    return got
+
+
+def test_config0_shape_fp32_backward():
+    cfg = gi.Config("c0_bwd", 1, 256, 2, 64, 64, "fp32", with_grad=True)
+    compare(gi.make_inputs(cfg, 0), label="c0 shape fwd+bwd fp32")
+
+
+SMALL = [
+    ("fp32", 64, 1, 200, 3, 0.0, False, 0.7),
+    ("fp32", 64, 2, 130, 2, 0.3, True, 1.0),
+    ("fp32", 64, 1, 1, 2, 0.5, True, 1.0),
+    ("bf16", 64, 2, 300, 2, 0.0, False, 1.0),
+    ("bf16", 128, 1, 257, 3, 0.2, True, 1.0),
+    ("bf16", 128, 1, 63, 1, 0.0, False, 0.125),
+    ("bf16", 128, 1, 64, 2, 0.0, True, 1.0),
+    ("bf16", 128, 2, 65, 2, 0.1, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,T,H,h0,with_dht,scale", SMALL)
+def test_small_dense(dtype, d, B, T, H, h0, with_dht, scale):
+    cfg = small_cfg(dtype, d, B=B, T=T, H=H, h0_std=h0, with_grad=True)
+    x = gi.make_inputs(cfg, 11)
+    dht = np.random.default_rng(3).standard_normal((x["N"], H, d, d)) * 0.1 if with_dht else None
+    compare(x, dht=dht, scale=scale, label="small")
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128)])
+def test_small_varlen(dtype, d):
+    cfg = small_cfg(dtype, d, H=2, h0_std=0.3, with_grad=True)
+    x = gi.make_inputs(cfg, 12, lengths=[1, 0, 63, 64, 65, 130, 0, 7])
+    dht = np.random.default_rng(4).standard_normal((x["N"], 2, d, d)) * 0.1
+    got = compare(x, dht=dht, label="varlen")
+    # empty sequences pass the state gradient through
+    assert np.array_equal(got[5][1], dht[1].astype(np.float32))
+    assert np.array_equal(got[5][6], dht[6].astype(np.float32))
+
+
+def test_recompute_equals_saved_context():
+    cfg = small_cfg("bf16", 128, T=200, H=2, h0_std=0.1, with_grad=True)
+    x = gi.make_inputs(cfg, 13)
+    a = run_bwd(x, use_context=True)
+    b = run_bwd(x, use_context=False)
+    for n, u, v in zip(NAMES, a, b):
+        assert np.array_equal(u, v), n
+
+
+def test_bitwise_deterministic_backward():
+    cfg = small_cfg("bf16", 128, T=190, H=3, with_grad=True)
+    x = gi.make_inputs(cfg, 14)
+    a = run_bwd(x)
+    b = run_bwd(x)
+    for n, u, v in zip(NAMES, a, b):
+        assert np.array_equal(u, v), n
+
+
+def test_fp32_head_dim_128_backward_rejected():
+    cfg = small_cfg("fp32", 128, T=64, H=1, with_grad=True)
+    x = gi.make_inputs(cfg, 15)
+    d = dev_inputs(x)
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
+    assert e.value.status == gdn.GDN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["metric", "c4"])
+def test_full_fwd_bwd(name):
+    x = gi.make_inputs(gi.CONFIGS[name], 0)
+    compare(x, label=name)
