@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""GDN forward+backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = gdn_fwd (with the final state, keeping its forward context) then
+gdn_bwd (reusing that context, no dh0) on the B=1, T=4096, H=16, d_k=d_v=128
+bf16 workload with synthetic seeded inputs resident in HBM.  W untimed steps,
+then K steps timed between two device synchronisations; value = tokens / s.
+A second timed region of K steps brackets every kernel with HIP events on
+the launch stream (through the library's gdn_profile_events hook) for the
+per-kernel averages and the roofline of the dominant kernel.  The fp64 CPU
+oracle is timed on the host beside it.  Prints one JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd+bwd tokens/s at T=4096,H=16,d=128 bf16; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+C = 64
+
+
+def kernel_bytes(D, E, units, state_units, with_ht=True):
+    """Algorithmic HBM bytes per launch of each kernel: each input it needs
+    read once and each output written once, at storage size.  Per
+    (chunk, head) unit unless noted; state kernels add their per-(sequence,
+    head) state I/O."""
+    per_unit = {
+        # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E)
+        "fwd_prep": 5 * C * D * E + 3 * C * 4,
+        # reads -W, Kt^T, U (3CD E), gamma_L; writes h (D^2 E), V' (CD E)
+        "fwd_state": 4 * C * D * E + D * D * E + 4,
+        # reads Q, K, V' (3CD E), h (D^2 E), gamma; writes O (CD E)
+        "fwd_out": 4 * C * D * E + D * D * E + C * 4,
+        # reads Q, K, dO, -W (4CD E), gamma; writes Kt, QgT, dOf, -W^T (4CD E), dV'loc (CD fp32)
+        "bwd_prep": 8 * C * D * E + C * D * 4 + C * 4,
+        # reads Kt, QgT, dOf, -W^T (4CD E), dV'loc (CD fp32), gamma_L; writes H' (D^2 E), dV' (CD E)
+        "bwd_state": 5 * C * D * E + C * D * 4 + D * D * E + 4,
+        # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), gamma, beta;
+        # writes dQ, dK, dV (3CD E), dg, dbeta
+        "bwd_grad": 9 * C * D * E + 2 * D * D * E + 4 * C * 4,
+    }
+    out = {k: v * units for k, v in per_unit.items()}
+    if with_ht:
+        out["fwd_state"] += state_units * D * D * 4
+    return out, per_unit
+
+
+def kernel_flops(D, units):
+    """Algorithmic flops per launch (2mnk per product, triangular operands at
+    one half, no recompute, no transposes)."""
+    per_unit = {
+        "fwd_prep": C * C * D + C ** 3 // 3 + 2 * C * C * D,
+        "fwd_state": 4 * C * D * D,
+        "fwd_out": 2 * C * D * D + 2 * C * C * D,
+        "bwd_prep": 2 * C * C * D,
+        "bwd_state": 2 * C * D * D + 4 * C * D * D,
+        "bwd_grad": 8 * C * D * D + 8 * C * C * D + 2 * C ** 3 // 3,
+    }
+    return {k: v * units for k, v in per_unit.items()}
+
+
+def sources_sha():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "linear_attention_gated_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM traffic of `kernel` from committed rocprofv3 counter runs, or None
+    if there are none or the kernel sources changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("sources_sha") != sources_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(x, budget_s=10.0, max_reps=20):
+    import oracle
+    nthreads = min(16, os.cpu_count() or 1)
+    used = oracle.threads_used(x["N"], x["H"], nthreads)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads)
+        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], nthreads=nthreads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= max_reps:
+            break
+    tokens = x["B"] * x["T"]
+    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%d complete fwd+bwd passes of the B=1,T=4096,H=16,d=128 workload "
+                      "(fp64 token recurrence; %.1f s wall)" % (reps, el)}
+
+
+class HipEvents:
+    """A few hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev[i] = h
+        self.n = n
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.ev[i])
+
+
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copy calibration: %d x %d bytes" % (reps, nbytes), file=sys.stderr)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-profile-pass", action="store_true",
+                    help="skip the second, event-bracketed timing region")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the operator's sequences and heads "
+              "would shard across GPUs without any exchange, but no multi-GPU path is built); "
+              "got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gdn_inputs as gi
+    import linear_attention_gated_amd as gdn
+
+    dev = torch.device("cuda:0")
+    cfg = gi.CONFIGS["metric"]
+    x = gi.make_inputs(cfg, 0)
+    B, T, H, D = x["B"], x["T"], x["H"], x["dk"]
+
+    def t(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    q, k, v, do = (t(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
+    p = gdn.make_problem(q, v)
+    L = gdn.lib()
+    wsf = torch.empty(L.gdn_fwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(L.gdn_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+
+    def step():
+        o, ht, ctx = gdn.fwd(q, k, v, g, beta, return_context=True, workspace=wsf)
+        return gdn.bwd(q, k, v, g, beta, do, context=ctx, need_dh0=False, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = 1e3 * el / args.steps
+    value = B * T * args.steps / el
+
+    kernels = {}
+    roofline = None
+    step_roof = None
+    units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
+    if not args.no_profile_pass:
+        launches_per_step = 8
+        n = launches_per_step * args.steps
+        evs = HipEvents(2 * n)
+        L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        cnt = L.gdn_profile_count()
+        L.gdn_profile_events(None, 0)
+        tot = {}
+        num = {}
+        for i in range(min(cnt, n)):
+            name = L.gdn_profile_name(i).decode()
+            ms = evs.elapsed_ms(2 * i, 2 * i + 1)
+            tot[name] = tot.get(name, 0.0) + ms
+            num[name] = num.get(name, 0) + 1
+        evs.close()
+        kbytes, per_unit_b = kernel_bytes(D, 2, units, B * H)
+        kflops = kernel_flops(D, units)
+        for name in tot:
+            avg_us = 1e3 * tot[name] / num[name]
+            kernels[name] = {"avg_us": round(avg_us, 2), "launches_per_step": num[name] / args.steps}
+            if name in kbytes:
+                kernels[name]["achieved_GBps"] = round(kbytes[name] / (avg_us * 1e-6) / 1e9, 1)
+                kernels[name]["achieved_TFLOPs"] = round(kflops[name] / (avg_us * 1e-6) / 1e12, 2)
+        dom = max((k_ for k_ in tot if k_ in kbytes), key=lambda k_: tot[k_])
+        a_gbs = kbytes[dom] / (1e-3 * tot[dom] / num[dom]) / 1e9
+        tr = traffic_for(dom)
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": tr, "algorithmic_bytes_per_launch": kbytes[dom],
+                    "units_per_launch": units, "bytes_per_unit": per_unit_b[dom]}
+        # whole step: the operator's own input/output bytes per token and head
+        step_bytes = (1032 + 1808) * B * T * H + B * H * D * D * 4
+        step_flops = (140629 + 297643) * B * T * H
+        step_roof = {"bytes": step_bytes, "achieved_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "flops": step_flops,
+                     "achieved_TFLOPs": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                     "mfma_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                     "kernel_sum_us": round(sum(1e3 * tot[k_] / args.steps for k_ in tot), 1)}
+
+    if args.copy_calib:
+        copy_calibration(torch, dev)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64", "B": B, "T": T, "H": H,
+                   "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,
+        "sources_sha": sources_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,7 +30,8 @@
  *
  * Ownership and execution:
  *  - The caller owns every buffer.  The library never allocates, frees or
- *    synchronises device memory; it keeps no global state and is reentrant.
+ *    synchronises device memory and is reentrant; its only state is
+ *    thread-local (the last error message and the timing diagnostics below).
  *  - All device work is enqueued on the caller's stream (hipStream_t passed
  *    as void*, NULL = the null stream); the calls return without waiting.
  *  - Inputs are read-only.  Outputs are fully overwritten (never
@@ -129,6 +130,21 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                    const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
                    float* dh0, const void* fwd_workspace, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* ---- Timing diagnostics ------------------------------------------------
+ * gdn_profile_events: bracket each kernel launched by the following
+ * gdn_fwd / gdn_bwd calls made on this thread with caller-created HIP events
+ * (hipEvent_t passed as void*): events[2i] is recorded on the call's stream
+ * just before launch i and events[2i+1] just after it, for the first n_pairs
+ * launches; later launches run unbracketed.  events == NULL or n_pairs <= 0
+ * turns bracketing off.  The events stay owned by the caller.  The state is
+ * thread-local, holds no device memory, and restarts the launch count.
+ * Returns 0.
+ * gdn_profile_count: launches bracketed since the last gdn_profile_events.
+ * gdn_profile_name: static kernel name of bracketed launch i ("" if none). */
+int gdn_profile_events(void* const* events, int n_pairs);
+int gdn_profile_count(void);
+const char* gdn_profile_name(int i);
 
 /* Static name of a status code. */
 const char* gdn_status_string(gdn_status s);

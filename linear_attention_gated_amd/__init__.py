@@ -27,7 +27,8 @@ GDN_OK, GDN_ERR_INVALID_ARGUMENT, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE_TOO_SMA
 GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_fwd",
-            "gdn_bwd", "gdn_status_string", "gdn_last_error_message")
+            "gdn_bwd", "gdn_status_string", "gdn_last_error_message", "gdn_profile_events",
+            "gdn_profile_count", "gdn_profile_name")
 
 
 class GdnProblem(ctypes.Structure):
@@ -69,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_status_string.argtypes = [ctypes.c_int]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error_message.restype = ctypes.c_char_p
+        L.gdn_profile_events.argtypes = [ctypes.c_void_p, ctypes.c_int]
+        L.gdn_profile_events.restype = ctypes.c_int
+        L.gdn_profile_count.restype = ctypes.c_int
+        L.gdn_profile_name.argtypes = [ctypes.c_int]
+        L.gdn_profile_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 

@@ -26,6 +26,33 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Optional per-launch event bracketing (timing diagnostics), per thread.
+struct ProfileState {
+  void* const* events = nullptr;
+  int pairs = 0;
+  int count = 0;
+  const char* names[512] = {};
+};
+thread_local ProfileState g_prof;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& f) {
+  ProfileState& P = g_prof;
+  const bool rec = P.events && P.count < P.pairs;
+  if (rec) {
+    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(P.events[2 * P.count]), s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = f();
+  if (rec) {
+    hipError_t e2 = hipEventRecord(reinterpret_cast<hipEvent_t>(P.events[2 * P.count + 1]), s);
+    if (P.count < 512) P.names[P.count] = name;
+    ++P.count;
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
+}
+
 gdn_status fail(gdn_status s, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -201,6 +228,20 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
 
+int gdn_profile_events(void* const* events, int n_pairs) {
+  g_prof.events = (events && n_pairs > 0) ? events : nullptr;
+  g_prof.pairs = (events && n_pairs > 0) ? n_pairs : 0;
+  g_prof.count = 0;
+  return 0;
+}
+
+int gdn_profile_count(void) { return g_prof.count; }
+
+const char* gdn_profile_name(int i) {
+  if (i < 0 || i >= g_prof.count || i >= 512 || !g_prof.names[i]) return "";
+  return g_prof.names[i];
+}
+
 size_t gdn_fwd_workspace_bytes(const gdn_problem* p) {
   try {
     Layout L;
@@ -248,10 +289,10 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0; P.o = o; P.ht = ht;
     const int D = (int)L.D;
     hipError_t e;
-    if ((e = gdn::launch_plan(P, s)) != hipSuccess) return hip_fail(e, "plan launch");
-    if ((e = gdn::launch_fwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_prep launch");
-    if ((e = gdn::launch_fwd_state(P, D, L.bf16, true, s)) != hipSuccess) return hip_fail(e, "fwd_state launch");
-    if ((e = gdn::launch_fwd_out(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_out launch");
+    if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+    if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
+    if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
+    if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
     return GDN_OK;
   } catch (...) {
     return fail(GDN_ERR_HIP, "unexpected exception in gdn_fwd");
@@ -302,13 +343,13 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     const int D = (int)L.D;
     hipError_t e;
     if (!fwd_workspace) {
-      if ((e = gdn::launch_plan(P, s)) != hipSuccess) return hip_fail(e, "plan launch");
-      if ((e = gdn::launch_fwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "fwd_prep launch");
-      if ((e = gdn::launch_fwd_state(P, D, L.bf16, false, s)) != hipSuccess) return hip_fail(e, "fwd_state launch");
+      if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+      if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
+      if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, false, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     }
-    if ((e = gdn::launch_bwd_prep(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_prep launch");
-    if ((e = gdn::launch_bwd_state(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_state launch");
-    if ((e = gdn::launch_bwd_grad(P, D, L.bf16, s)) != hipSuccess) return hip_fail(e, "bwd_grad launch");
+    if ((e = timed("bwd_prep", s, [&] { return gdn::launch_bwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "bwd_prep launch");
+    if ((e = timed("bwd_state", s, [&] { return gdn::launch_bwd_state(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "bwd_state launch");
+    if ((e = timed("bwd_grad", s, [&] { return gdn::launch_bwd_grad(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "bwd_grad launch");
     return GDN_OK;
   } catch (...) {
     return fail(GDN_ERR_HIP, "unexpected exception in gdn_bwd");
