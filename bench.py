@@ -223,6 +223,9 @@ def main():
         torch.cuda.synchronize()
         cnt = L.gdn_profile_count()
         L.gdn_profile_events(None, 0)
+        print("profile pass: %d launches bracketed" % cnt, file=sys.stderr)
+        if cnt == 0:
+            raise RuntimeError("the event-bracketed pass recorded no kernel launches")
         tot = {}
         num = {}
         for i in range(min(cnt, n)):

@@ -136,11 +136,11 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
  * gdn_fwd / gdn_bwd calls made on this thread with caller-created HIP events
  * (hipEvent_t passed as void*): events[2i] is recorded on the call's stream
  * just before launch i and events[2i+1] just after it, for the first n_pairs
- * launches; later launches run unbracketed.  events == NULL or n_pairs <= 0
- * turns bracketing off.  The events stay owned by the caller.  The state is
- * thread-local, holds no device memory, and restarts the launch count.
- * Returns 0.
- * gdn_profile_count: launches bracketed since the last gdn_profile_events.
+ * launches; later launches run unbracketed.  Enabling restarts the launch
+ * count.  events == NULL or n_pairs <= 0 turns bracketing off and leaves the
+ * record of the last run readable.  The events stay owned by the caller.
+ * The state is thread-local and holds no device memory.  Returns 0.
+ * gdn_profile_count: launches bracketed since bracketing was last enabled.
  * gdn_profile_name: static kernel name of bracketed launch i ("" if none). */
 int gdn_profile_events(void* const* events, int n_pairs);
 int gdn_profile_count(void);

@@ -229,9 +229,15 @@ const char* gdn_status_string(gdn_status s) {
 const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
 
 int gdn_profile_events(void* const* events, int n_pairs) {
-  g_prof.events = (events && n_pairs > 0) ? events : nullptr;
-  g_prof.pairs = (events && n_pairs > 0) ? n_pairs : 0;
-  g_prof.count = 0;
+  if (events && n_pairs > 0) {
+    g_prof.events = events;
+    g_prof.pairs = n_pairs;
+    g_prof.count = 0;
+  } else {
+    // stop bracketing; the record of the last run stays readable
+    g_prof.events = nullptr;
+    g_prof.pairs = 0;
+  }
   return 0;
 }
 
