@@ -73,7 +73,7 @@ struct Layout {
   // byte offsets into a workspace
   size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0;
   size_t fwd_bytes = 0;
-  size_t QgT = 0, dOf = 0, WnT = 0, Ktn = 0, HPf = 0, dVf = 0, dVl = 0;
+  size_t Z = 0, WnT = 0, Ktn = 0, HPf = 0, dVf = 0, dVl = 0;
   size_t bwd_bytes = 0;
 };
 
@@ -140,8 +140,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->Hf = take(e * ch * D * D);
   L->Vf = take(e * ch * 64 * D);
   L->fwd_bytes = off;
-  L->QgT = take(e * ch * 64 * D);
-  L->dOf = take(e * ch * 64 * D);
+  L->Z = take(sizeof(float) * ch * D * D);
   L->WnT = take(e * ch * 64 * D);
   L->Ktn = take(e * ch * 64 * D);
   L->HPf = take(e * ch * D * D);
@@ -344,7 +343,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     gdn::Params P = base_params(p, L, ctx);
     P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0;
     P.dO = d_o; P.dht = dht; P.dq = dq; P.dk = dk; P.dv = dv; P.dg = dg; P.dbeta = dbeta; P.dh0 = dh0;
-    P.QgT = ws + L.QgT; P.dOf = ws + L.dOf; P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
+    P.Z = reinterpret_cast<float*>(ws + L.Z); P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
     P.HPf = ws + L.HPf; P.dVf = ws + L.dVf; P.dVl = reinterpret_cast<float*>(ws + L.dVl);
     const int D = (int)L.D;
     hipError_t e;

@@ -5,6 +5,7 @@
 // chunk), and Q scaled by `scale`:
 //   dV'  = P^T dO + Kt H'                  P = (Q K^T) * D, lower incl. diagonal
 //   dh   = exp(gamma_L) H' + (Gam Q)^T dO - W^T dV'     (becomes H' of the previous chunk)
+//          (Z = (Gam Q)^T dO depends only on the chunk and is precomputed in K4)
 //   dP   = dO V'^T (lower)
 //   dQ   = Gam dO h^T + (dP * D) K
 //   dK   = (dP * D)^T Q + diag(exp(gamma_L - gamma)) V' H'^T + diag(beta Gam) T^T dW
@@ -22,18 +23,21 @@
 // backward folded in (K6).
 #include "frag.h"
 #include "gdn_internal.h"
+#include "ring.h"
 
 namespace gdn {
 
 // --------------------------------------------------------------------------
 // K4: per (chunk, head), D/32 waves; wave w owns feature columns [32w, 32w+32).
-// Writes the fragment-native operands of the reverse pass:
-//   Ktn = F(Kt; s, i), QgT = F(scale*Gam*Q; i, r), dOf = F(dO; j, r),
-//   WnT = F(-W; i, r), and dVl = P^T dO (accumulator records, fp32).
+// Writes the operands of the reverse pass:
+//   Ktn = F(Kt; s, i), WnT = F(-W; i, r)            (fragment-native)
+//   Z   = (scale Gam Q)^T dO   [jb][ib] accumulator records, fp32
+//   dVl = P^T dO               [jb][sb] accumulator records, fp32
 template <typename E, int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   constexpr int KB = D / 32, NJ = D / 16;
   __shared__ float s_gam[64];
+  __shared__ __attribute__((aligned(16))) E s_dof[NJ * 2 * REC];   // F(dO; j, r) records [jb][rkb]
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
@@ -45,8 +49,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   const E* dO = reinterpret_cast<const E*>(p.dO);
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
   E* Ktn = reinterpret_cast<E*>(p.Ktn);
-  E* QgT = reinterpret_cast<E*>(p.QgT);
-  E* dOf = reinterpret_cast<E*>(p.dOf);
   E* WnT = reinterpret_cast<E*>(p.WnT);
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
   __syncthreads();
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   }
 
   // transposes of this wave's slice of Q (scaled), dO and -W
-  frag_t<E> dof[2][2];  // F(dO; j, r) for jb = 2w + hs, rkb
+  frag_t<E> dof[2][2], qg[2][2];  // F(dO; j, r), F(scale Gam Q; i, r) for block 2w + hs, rkb
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     const frag_t<E> idh = hs ? id1 : id0;
@@ -88,10 +90,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
     const int ib = 2 * w + hs;
 #pragma unroll
     for (int rkb = 0; rkb < 2; ++rkb) {
-      store_rec<E>(QgT + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, to_frag<E>(tq[2 * rkb], tq[2 * rkb + 1]));
+      qg[hs][rkb] = to_frag<E>(tq[2 * rkb], tq[2 * rkb + 1]);
       dof[hs][rkb] = to_frag<E>(td[2 * rkb], td[2 * rkb + 1]);
-      store_rec<E>(dOf + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, dof[hs][rkb]);
+      store_rec<E>(s_dof + (ib * 2 + rkb) * REC, lane, dof[hs][rkb]);
       store_rec<E>(WnT + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, to_frag<E>(tw[2 * rkb], tw[2 * rkb + 1]));
+    }
+  }
+  __syncthreads();
+  // Z[i][j] = sum_r (scale Gam_r Q[r][i]) dO[r][j] for this wave's i-blocks, all j-blocks
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    const frag_t<E> d0 = load_rec<E>(s_dof + (jb * 2 + 0) * REC, lane);
+    const frag_t<E> d1 = load_rec<E>(s_dof + (jb * 2 + 1) * REC, lane);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      f32x4 acc = mma(qg[hs][0], d0, zero4());
+      acc = mma(qg[hs][1], d1, acc);
+      store_acc<float>(p.Z + (((size_t)ch * NJ + jb) * NJ + 2 * w + hs) * AREC, lane, acc);
     }
   }
 
@@ -136,14 +151,31 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
 }
 
 // --------------------------------------------------------------------------
-// K5: reverse state-gradient pass.  One wave per (sequence, head, 16-column
-// block jb of d_v); the d_k x 16 slice of H' stays in accumulator registers.
-// Per chunk (last to first): store H' (fragment-native), dV' = dVl + Kt H',
-// store dV', H' <- exp(gamma_L) H' + (scale Gam Q)^T dO - W^T dV'.
+// K5: reverse state-gradient pass.  One compute wave per (sequence, head,
+// 16-column block jb of d_v); the d_k x 16 slice of H' stays in accumulator
+// registers.  The chunk operands (Kt, -W^T, this block of Z and dVl, gamma)
+// are streamed through an LDS ring by loader waves (ring.h), last chunk first.
+// Per chunk: store H' (fragment-native), dV' = dVl + Kt H', store dV',
+// H' <- exp(gamma_L) H' + Z - W^T dV'.
 template <typename E, int D>
-__global__ __launch_bounds__(64) void k_bwd_state(Params p) {
-  constexpr int NJ = D / 16, KB = D / 32;
-  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+struct BwdRing {
+  static constexpr int KB = D / 32, NJ = D / 16;
+  static constexpr int RECB = REC * (int)sizeof(E);
+  static constexpr int oK = 0;
+  static constexpr int oW = oK + 4 * KB * RECB;
+  static constexpr int oZ = oW + NJ * 2 * RECB;
+  static constexpr int oV = oZ + NJ * AREC * 4;
+  static constexpr int oG = oV + 4 * AREC * 4;
+  static constexpr int SLOT = oG + 256;
+  static constexpr int S = ring_slots(SLOT);
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p) {
+  using R = BwdRing<E, D>;
+  constexpr int NJ = D / 16, KB = D / 32, S = R::S;
+  __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
   if (unit >= p.N * p.H) return;
@@ -151,59 +183,90 @@ __global__ __launch_bounds__(64) void k_bwd_state(Params p) {
   const int4 st = p.seq_tab[n];
   const int c0 = st.x, nc = st.y;
   const size_t sbase = (size_t)unit * D * D;
-
-  f32x4 hs[NJ];
-#pragma unroll
-  for (int ib = 0; ib < NJ; ++ib) {
-    if (p.dht) {
-      const float* src = p.dht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-      hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
-    } else {
-      hs[ib] = zero4();
-    }
-  }
   const E* Ktn = reinterpret_cast<const E*>(p.Ktn);
-  const E* QgT = reinterpret_cast<const E*>(p.QgT);
-  const E* dOf = reinterpret_cast<const E*>(p.dOf);
   const E* WnT = reinterpret_cast<const E*>(p.WnT);
   E* HPf = reinterpret_cast<E*>(p.HPf);
   E* dVf = reinterpret_cast<E*>(p.dVf);
 
-  for (int ci = nc - 1; ci >= 0; --ci) {
-    const size_t ch = (size_t)(c0 + ci) * p.H + h;
-    frag_t<E> hfr[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
-      store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
-    }
-    f32x4 dv[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      dv[sb] = load_acc<float>(p.dVl + ((ch * NJ + jb) * 4 + sb) * AREC, lane);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) dv[sb] = mma(load_rec<E>(Ktn + ((ch * 4 + sb) * KB + kb) * REC, lane), hfr[kb], dv[sb]);
-    }
-    frag_t<E> dvf[2], dof[2];
-#pragma unroll
-    for (int rkb = 0; rkb < 2; ++rkb) {
-      dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
-      store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
-      dof[rkb] = load_rec<E>(dOf + ((ch * NJ + jb) * 2 + rkb) * REC, lane);
-    }
-    const float GL = __expf(p.gamma[ch * 64 + 63]);
+  // step t handles chunk nc - 1 - t
+  auto issue = [&](int t) {
+    const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
+    char* sl = ring + (t % S) * R::SLOT;
+    dma_kib(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane);
+    dma_kib(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane);
+    dma_kib(p.Z + (ch * NJ + jb) * NJ * AREC, sl + R::oZ, NJ * AREC * 4, lane);
+    dma_kib(p.dVl + (ch * NJ + jb) * 4 * AREC, sl + R::oV, 4 * AREC * 4, lane);
+    dma_256(p.gamma + ch * 64, sl + R::oG, lane);
+  };
+  if (w >= 1 && w - 1 < nc) issue(w - 1);
+
+  f32x4 hs[NJ];
+  if (w == 0) {
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
-      f32x4 x = scale4(hs[ib], GL);
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        x = mma(load_rec<E>(QgT + ((ch * NJ + ib) * 2 + rkb) * REC, lane), dof[rkb], x);
-        x = mma(load_rec<E>(WnT + ((ch * NJ + ib) * 2 + rkb) * REC, lane), dvf[rkb], x);
+      if (p.dht) {
+        const float* src = p.dht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+      } else {
+        hs[ib] = zero4();
       }
-      hs[ib] = x;
     }
   }
-  if (p.dh0) {
+
+  for (int t = 0; t < nc; ++t) {
+    const bool mine = w >= 1 && (t % (S - 1)) == w - 1;
+    if (mine) wait_vmem();
+    ring_barrier();
+    if (w == 0) {
+      const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
+      const char* sl = ring + (t % S) * R::SLOT;
+      // all of this step's LDS operands first, then the products
+      frag_t<E> kn[4][KB], wt[NJ][2];
+      f32x4 dv[4], z[NJ];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kn[sb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (sb * KB + kb) * REC, lane);
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) dv[sb] = load_acc<float>(reinterpret_cast<const float*>(sl + R::oV) + sb * AREC, lane);
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib)
+#pragma unroll
+        for (int rkb = 0; rkb < 2; ++rkb)
+          wt[ib][rkb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (ib * 2 + rkb) * REC, lane);
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib) z[ib] = load_acc<float>(reinterpret_cast<const float*>(sl + R::oZ) + ib * AREC, lane);
+      const float GL = __expf(reinterpret_cast<const float*>(sl + R::oG)[63]);
+      __builtin_amdgcn_sched_barrier(0);
+      frag_t<E> hfr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      // dV' = dVl + Kt H'
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) dv[sb] = mma(kn[sb][kb], hfr[kb], dv[sb]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      frag_t<E> dvf[2];
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
+      // H' <- exp(gamma_L) H' + Z - W^T dV'
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL) + z[ib];
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb)
+#pragma unroll
+        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(wt[ib][rkb], dvf[rkb], hs[ib]);
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
+      wait_lds();
+    } else if (mine && t + S - 1 < nc) {
+      issue(t + S - 1);
+    }
+  }
+  if (w == 0 && p.dh0) {
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
       float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
@@ -805,7 +868,7 @@ static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
   if (p.N * p.H == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_bwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64), args, 0, s);
+  return hipLaunchKernel((const void*)k_bwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D>::S), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {

@@ -14,6 +14,7 @@
 // output step; the equations are derived from the token recurrence.
 #include "frag.h"
 #include "gdn_internal.h"
+#include "ring.h"
 
 namespace gdn {
 
@@ -299,15 +300,32 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
 }
 
 // --------------------------------------------------------------------------
-// K2: sequential state pass.  One wave per (sequence, head, 16-column block
-// jb of d_v); the columns of the state are independent, so a wave needs no
-// communication: its d_k x 16 state stays in accumulator registers.
+// K2: sequential state pass.  One compute wave per (sequence, head, 16-column
+// block jb of d_v); the columns of the state are independent, so the compute
+// wave needs no communication: its d_k x 16 state stays in accumulator
+// registers.  The chunk operands (-W, Kt^T, this block of U, gamma) are
+// streamed through an LDS ring by loader waves (ring.h).
 // Per chunk: store the entering state (fragment-native), V' = U - W h,
 // store V', h <- exp(gamma_L) h + Kt^T V'.
 template <typename E, int D>
-__global__ __launch_bounds__(64) void k_fwd_state(Params p, int write_ht) {
-  constexpr int NJ = D / 16, KB = D / 32;
-  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+struct FwdRing {
+  static constexpr int KB = D / 32, NJ = D / 16;
+  static constexpr int RECB = REC * (int)sizeof(E);
+  static constexpr int oW = 0;
+  static constexpr int oK = oW + 4 * KB * RECB;
+  static constexpr int oU = oK + NJ * 2 * RECB;
+  static constexpr int UB = 4 * AREC * (int)sizeof(E);
+  static constexpr int oG = oU + UB;
+  static constexpr int SLOT = oG + 256;
+  static constexpr int S = ring_slots(SLOT);
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p, int write_ht) {
+  using R = FwdRing<E, D>;
+  constexpr int NJ = D / 16, KB = D / 32, S = R::S;
+  __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
   if (unit >= p.N * p.H) return;
@@ -315,56 +333,89 @@ __global__ __launch_bounds__(64) void k_fwd_state(Params p, int write_ht) {
   const int4 st = p.seq_tab[n];
   const int c0 = st.x, nc = st.y;
   const size_t sbase = (size_t)unit * D * D;
-
-  f32x4 hs[NJ];
-#pragma unroll
-  for (int ib = 0; ib < NJ; ++ib) {
-    if (p.h0) {
-      const float* src = p.h0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-      hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
-    } else {
-      hs[ib] = zero4();
-    }
-  }
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
   const E* Ktf = reinterpret_cast<const E*>(p.Ktf);
   const E* Ua = reinterpret_cast<const E*>(p.Ua);
   E* Hf = reinterpret_cast<E*>(p.Hf);
   E* Vf = reinterpret_cast<E*>(p.Vf);
 
-  for (int ci = 0; ci < nc; ++ci) {
+  auto issue = [&](int ci) {
     const size_t ch = (size_t)(c0 + ci) * p.H + h;
-    frag_t<E> hfr[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
-      store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
-    }
-    f32x4 vp[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) vp[rb] = load_acc<E>(Ua + ((ch * NJ + jb) * 4 + rb) * AREC, lane);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        vp[rb] = mma(load_rec<E>(Wn + ((ch * 4 + rb) * KB + kb) * REC, lane), hfr[kb], vp[rb]);
-    frag_t<E> vfr[2];
-#pragma unroll
-    for (int skb = 0; skb < 2; ++skb) {
-      vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
-      store_rec<E>(Vf + ((ch * NJ + jb) * 2 + skb) * REC, lane, vfr[skb]);
-    }
-    const float GL = __expf(p.gamma[ch * 64 + 63]);
+    char* sl = ring + (ci % S) * R::SLOT;
+    dma_kib(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane);
+    dma_kib(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane);
+    dma_kib(Ua + (ch * NJ + jb) * 4 * AREC, sl + R::oU, R::UB, lane);
+    dma_256(p.gamma + ch * 64, sl + R::oG, lane);
+  };
+  if (w >= 1 && w - 1 < nc) issue(w - 1);
+
+  f32x4 hs[NJ];
+  if (w == 0) {
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
-      f32x4 x = scale4(hs[ib], GL);
-#pragma unroll
-      for (int skb = 0; skb < 2; ++skb)
-        x = mma(load_rec<E>(Ktf + ((ch * NJ + ib) * 2 + skb) * REC, lane), vfr[skb], x);
-      hs[ib] = x;
+      if (p.h0) {
+        const float* src = p.h0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+      } else {
+        hs[ib] = zero4();
+      }
     }
   }
-  if (write_ht && p.ht) {
+
+  for (int ci = 0; ci < nc; ++ci) {
+    const bool mine = w >= 1 && (ci % (S - 1)) == w - 1;
+    if (mine) wait_vmem();
+    ring_barrier();
+    if (w == 0) {
+      const size_t ch = (size_t)(c0 + ci) * p.H + h;
+      const char* sl = ring + (ci % S) * R::SLOT;
+      // all of this step's LDS operands first, then the products
+      frag_t<E> wf[4][KB], kf[NJ][2];
+      f32x4 vp[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          wf[rb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (rb * KB + kb) * REC, lane);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        vp[rb] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oU) + rb * AREC, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      // Kt^T reads stay in flight while the V' products run
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib)
+#pragma unroll
+        for (int skb = 0; skb < 2; ++skb)
+          kf[ib][skb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (ib * 2 + skb) * REC, lane);
+      const float GL = __expf(reinterpret_cast<const float*>(sl + R::oG)[63]);
+      __builtin_amdgcn_sched_barrier(0);
+      frag_t<E> hfr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      // V' = U - W h: contraction outermost so consecutive MFMAs are independent
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) vp[rb] = mma(wf[rb][kb], hfr[kb], vp[rb]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      frag_t<E> vfr[2];
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL);
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb)
+#pragma unroll
+        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(kf[ib][skb], vfr[skb], hs[ib]);
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) store_rec<E>(Vf + ((ch * NJ + jb) * 2 + skb) * REC, lane, vfr[skb]);
+      wait_lds();
+    } else if (mine && ci + S - 1 < nc) {
+      issue(ci + S - 1);
+    }
+  }
+  if (w == 0 && write_ht && p.ht) {
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
       float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
@@ -462,7 +513,7 @@ static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
   Params a = p;
   int wh = write_ht ? 1 : 0;
   void* args[] = {&a, &wh};
-  return hipLaunchKernel((const void*)k_fwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64), args, 0, s);
+  return hipLaunchKernel((const void*)k_fwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D>::S), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t fwd_out_t(const Params& p, hipStream_t s) {

@@ -17,8 +17,7 @@ constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 //   Ua  acc U[r][j]      [D/16][4]        WY values (accumulator records)
 //   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
 //   Vf  F(V'; j, s)      [D/16][2]        corrected values
-//   QgT F(s*Gam*Q; i, r) [D/16][2]        backward: scaled queries, transposed
-//   dOf F(dO; j, r)      [D/16][2]        backward: upstream grad, transposed
+//   Z   acc Z[i][j]      [D/16 jb][D/16 ib] fp32  backward: (scale Gam Q)^T dO
 //   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
 //   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
 //   dVl acc dV'loc[s][j] [D/16][4] fp32   backward: intra-chunk part of dV'
@@ -46,8 +45,8 @@ struct Params {
 
   float* gamma;           // [NC][H][64] chunk-local cumulative log decay
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
-  void *QgT, *dOf, *WnT, *Ktn, *HPf, *dVf;
-  float* dVl;
+  void *WnT, *Ktn, *HPf, *dVf;
+  float *Z, *dVl;
 };
 
 // Launchers (each returns the first launch error, hipSuccess otherwise).
