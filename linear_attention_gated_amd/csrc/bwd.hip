@@ -24,6 +24,7 @@
 #include "frag.h"
 #include "gdn_internal.h"
 #include "ring.h"
+#include "tri.h"
 
 namespace gdn {
 
@@ -319,7 +320,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   E* sdW = reinterpret_cast<E*>(smem + S::oU + S::SET);
   float* sM1 = reinterpret_cast<float*>(smem + S::oU);
   float* sdTt = reinterpret_cast<float*>(smem + S::odTt);
-  float* sX = sdTt;
   float* s_gam = reinterpret_cast<float*>(smem + S::oSm);
   float* s_beta = s_gam + 64;
   float* s_pg = s_beta + 64;          // [NW][64] dgamma partials
@@ -376,11 +376,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       s_beta[lane] = bv;
     }
     for (int e = tid; e < NW * 64 * 2 + NW * 2; e += NT) s_pg[e] = 0.f;  // s_pg, s_pb, s_misc
-    for (int e = tid; e < 64 * 64; e += NT) {
-      const int r = e >> 6, s = e & 63;
-      if ((s >> 4) > (r >> 4)) sT[r * LDF + s] = 0.f;
-      sEE[r * LDF + s] = 0.f;
-    }
+    for (int e = tid; e < 64 * 64; e += NT) sEE[(e >> 6) * LDF + (e & 63)] = 0.f;
   }
   __syncthreads();
   const float gL = s_gam[63];
@@ -411,40 +407,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     }
   }
   __syncthreads();
-  if (w == 0) {
-    const int b0 = 16 * lg, j = li;
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float br = s_beta[b0 + r];
-      float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) acc -= br * sAp[(b0 + r) * LDF + b0 + s] * t[s];
-      t[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDF + b0 + j] = t[r];
-  }
-  __syncthreads();
-  for (int d = 1; d < 4; ++d) {
-    const int nblk = 4 - d;
-    for (int e = tid; e < nblk * 256; e += NT) {
-      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
-      const float br = s_beta[16 * a + r];
-      float x = 0.f;
-      for (int kk = 16 * b; kk < 16 * a; ++kk) x += sAp[(16 * a + r) * LDF + kk] * sT[kk * LDF + 16 * b + col];
-      sX[e] = br * x;
-    }
-    __syncthreads();
-    for (int e = tid; e < nblk * 256; e += NT) {
-      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
-      const float* xb = sX + (e / 256) * 256;
-      float x = 0.f;
-      for (int kk = 0; kk <= r; ++kk) x += sT[(16 * a + r) * LDF + 16 * a + kk] * xb[kk * 16 + col];
-      sT[(16 * a + r) * LDF + 16 * b + col] = -x;
-    }
-    __syncthreads();
-  }
+  tri_inverse64(sAp, s_beta, sT, LDF, NW);   // ends with a barrier
 
   // ---- transposes of this wave's column slice of V' and dV' into LDS:
   //      sVt rec (sb, w) = F(V'; s, j), sdVt rec (rb, w) = F(dV'; r, j)

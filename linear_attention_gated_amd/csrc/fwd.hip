@@ -15,6 +15,7 @@
 #include "frag.h"
 #include "gdn_internal.h"
 #include "ring.h"
+#include "tri.h"
 
 namespace gdn {
 
@@ -89,7 +90,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   constexpr int LDA = 68;
   __shared__ float sA[64 * LDA];
   __shared__ float sT[64 * LDA];
-  __shared__ float sX[3 * 256];
   __shared__ float s_gam[64], s_beta[64];
 
   const int ch = blockIdx.x;
@@ -113,11 +113,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
     s_gam[lane] = gam;
     s_beta[lane] = bv;
     p.gamma[(size_t)ch * 64 + lane] = gam;
-  }
-  // upper blocks of T are zero
-  for (int e = tid; e < 64 * 64; e += 64 * NW) {
-    const int r = e >> 6, s = e & 63;
-    if ((s >> 4) > (r >> 4)) sT[r * LDA + s] = 0.f;
   }
 
   // natural key fragments F(K; s, i) for all row blocks
@@ -158,41 +153,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   }
   __syncthreads();
 
-  // T = (I + A)^-1.  Diagonal 16x16 blocks by forward substitution (wave 0,
-  // lane = (block lg, column li)), then the off-diagonal blocks by levels:
-  // T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb.
-  if (w == 0) {
-    const int b0 = 16 * lg, j = li;
-    float t[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) acc -= sA[(b0 + r) * LDA + b0 + s] * t[s];
-      t[r] = acc;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sT[(b0 + r) * LDA + b0 + j] = t[r];
-  }
-  __syncthreads();
-  for (int d = 1; d < 4; ++d) {
-    const int nblk = 4 - d;
-    for (int e = tid; e < nblk * 256; e += 64 * NW) {
-      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
-      float x = 0.f;
-      for (int kk = 16 * b; kk < 16 * a; ++kk) x += sA[(16 * a + r) * LDA + kk] * sT[kk * LDA + 16 * b + col];
-      sX[e] = x;
-    }
-    __syncthreads();
-    for (int e = tid; e < nblk * 256; e += 64 * NW) {
-      const int a = d + e / 256, b = a - d, r = (e & 255) >> 4, col = e & 15;
-      const float* xb = sX + (e / 256) * 256;
-      float x = 0.f;
-      for (int kk = 0; kk <= r; ++kk) x += sT[(16 * a + r) * LDA + 16 * a + kk] * xb[kk * 16 + col];
-      sT[(16 * a + r) * LDA + 16 * b + col] = -x;
-    }
-    __syncthreads();
-  }
+  // T = (I + A)^-1 (ends with a barrier)
+  tri_inverse64(sA, nullptr, sT, LDA, NW);
 
   // T fragments F(T; r, s) (lower triangular: (rb <= 1, skb = 1) is zero)
   frag_t<E> tf[4][2];
