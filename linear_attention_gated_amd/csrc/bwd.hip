@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
-  const int4 ct = p.chunk_tab[c];
+  const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const E* Q = reinterpret_cast<const E*>(p.q);
@@ -181,7 +181,7 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
   const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
   if (unit >= p.N * p.H) return;
   const int n = unit / p.H, h = unit - n * p.H;
-  const int4 st = p.seq_tab[n];
+  const int4 st = seq_info(p, n);
   const int c0 = st.x, nc = st.y;
   const size_t sbase = (size_t)unit * D * D;
   const E* Ktn = reinterpret_cast<const E*>(p.Ktn);
@@ -287,39 +287,48 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
 template <typename E, int D>
 struct BwdGradSmem {
   static constexpr int KB = D / 32;
-  static constexpr int LDF = 68;
-  static constexpr int MAT = 64 * LDF * 4;             // fp32 64x64, padded rows
-  static constexpr int RECB = REC * (int)sizeof(E);
-  static constexpr int NREC = 4 * KB;                  // records of a 64 x D fragment set
-  static constexpr int SET = NREC * RECB;
-  static constexpr int UNI = (2 * SET > MAT) ? 2 * SET : MAT;  // dV'^T + dW, later M1
-  static constexpr int oAp = 0;
-  static constexpr int oT = oAp + MAT;
-  static constexpr int odP = oT + MAT;
-  static constexpr int oEE = odP + MAT;
-  static constexpr int oVt = oEE + MAT;
-  static constexpr int oU = oVt + SET;                 // sdVt | sdW, later sM1
-  static constexpr int odTt = oU + UNI;                // also the solve scratch
-  static constexpr int oSm = odTt + MAT;
   static constexpr int NW = D / 32;
+  static constexpr int LDF = 68;                        // fp32 64x64 matrices, padded rows
+  static constexpr int MAT = 64 * LDF * 4;
+  static constexpr int LDE = sizeof(E) == 2 ? 72 : 68;  // operand-type 64x64 matrix
+  static constexpr int PMAT = 64 * LDE * (int)sizeof(E);
+  static constexpr int RECB = REC * (int)sizeof(E);
+  static constexpr int SET = 4 * KB * RECB;             // records of a 64 x D fragment set
+  static constexpr int UNI = (2 * SET > MAT) ? 2 * SET : MAT;  // dV'^T + dW, later M1
+  static constexpr int TILE = NatTile<E, D>::BYTES;
+  static constexpr int oAp = 0;                         // A' = (K K^T) * D, later E + E^T
+  static constexpr int oT = oAp + MAT;
+  static constexpr int odP = oT + MAT;                  // dP * D
+  static constexpr int oVt = odP + PMAT;
+  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1
+  static constexpr int odTt = oU + UNI;
+  static constexpr int oQ = odTt + MAT;                 // staged natural tiles
+  static constexpr int oK = oQ + TILE;
+  static constexpr int oSm = oK + TILE;
   static constexpr int SMALL = (64 * 2 + NW * 64 * 2 + NW * 2) * 4;
-  static constexpr int BYTES = oSm + SMALL;
+  static constexpr int BASE = oSm + SMALL;
+  static constexpr bool kStageDO = BASE + TILE <= 160 * 1024;
+  static constexpr int odO = BASE;
+  static constexpr int BYTES = BASE + (kStageDO ? TILE : 0);
 };
 
 template <typename E, int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   using S = BwdGradSmem<E, D>;
-  constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDF = S::LDF;
+  constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDF = S::LDF, LDE = S::LDE;
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   float* sAp = reinterpret_cast<float*>(smem + S::oAp);
+  float* sEE = sAp;
   float* sT = reinterpret_cast<float*>(smem + S::oT);
-  float* sdP = reinterpret_cast<float*>(smem + S::odP);
-  float* sEE = reinterpret_cast<float*>(smem + S::oEE);
+  E* sdP = reinterpret_cast<E*>(smem + S::odP);
   E* sVt = reinterpret_cast<E*>(smem + S::oVt);
   E* sdVt = reinterpret_cast<E*>(smem + S::oU);
   E* sdW = reinterpret_cast<E*>(smem + S::oU + S::SET);
   float* sM1 = reinterpret_cast<float*>(smem + S::oU);
   float* sdTt = reinterpret_cast<float*>(smem + S::odTt);
+  char* tQ = smem + S::oQ;
+  char* tK = smem + S::oK;
+  char* tO = smem + S::odO;
   float* s_gam = reinterpret_cast<float*>(smem + S::oSm);
   float* s_beta = s_gam + 64;
   float* s_pg = s_beta + 64;          // [NW][64] dgamma partials
@@ -329,7 +338,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
-  const int4 ct = p.chunk_tab[c];
+  const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const int tid = threadIdx.x;
@@ -343,21 +352,25 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   const E* HPf = reinterpret_cast<const E*>(p.HPf);
   const E* dVf = reinterpret_cast<const E*>(p.dVf);
   const float sc = p.scale;
+  const size_t rowstride = (size_t)H * D;
+  const size_t base = ((size_t)tok0 * H + h) * D;
 
-  auto row_ptr = [&](const E* X, int row, int kb) { return X + ((size_t)(tok0 + row) * H + h) * D + 32 * kb; };
-  auto nat = [&](const E* X, int row, int kb) {
-    return row < L ? load_frag_row<E>(row_ptr(X, row, kb), lg) : zero_frag<E>();
+  auto gnat = [&](const E* X, int row, int kb) {
+    return row < L ? load_frag_row<E>(X + base + (size_t)row * rowstride + 32 * kb, lg) : zero_frag<E>();
   };
-  // fragment of a row-major fp32 64x64 LDS matrix: index rows 16ab.., contraction cols 32kb..
-  auto mfrag = [&](const float* M, int ab, int kb) {
-    const float* row = M + (16 * ab + li) * LDF + 32 * kb;
-    return to_frag<E>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
+  auto qf = [&](int ab, int kb) { return tile_frag<E, D>(tQ, ab, kb, li, lg); };
+  auto kf = [&](int ab, int kb) { return tile_frag<E, D>(tK, ab, kb, li, lg); };
+  auto of = [&](int ab, int kb) {
+    if constexpr (S::kStageDO) return tile_frag<E, D>(tO, ab, kb, li, lg);
+    else return gnat(dO, 16 * ab + li, kb);
   };
+  // fp32 LDS matrix fragments: index rows 16ab.., contraction cols 32kb..
   auto mfrag32 = [&](const float* M, int ab, int kb) {
     const float* row = M + (16 * ab + li) * LDF + 32 * kb;
     return to_frag<float>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
   };
-  // same matrix read transposed: index = columns 16cb.., contraction = rows 32kb..
+  auto mfrag = [&](const float* M, int ab, int kb) { return f32_to_frag<E>(frag_to_f32<float>(mfrag32(M, ab, kb))); };
+  // the same read transposed: index = columns 16cb.., contraction = rows 32kb..
   auto mfragT32 = [&](const float* M, int cb, int kb) {
     f32x8 t;
 #pragma unroll
@@ -365,69 +378,94 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     return t;
   };
   auto mfragT = [&](const float* M, int cb, int kb) { return f32_to_frag<E>(mfragT32(M, cb, kb)); };
-  auto lrec = [&](const E* base, int a, int kb) { return load_rec<E>(base + (a * KB + kb) * REC, lane); };
+  // operand-type dP*D matrix
+  auto pfrag = [&](int ab, int kb) {
+    const E* row = sdP + (16 * ab + li) * LDE + 32 * kb;
+    return load_frag_row<E>(row, lg);
+  };
+  auto pfragT = [&](int cb, int kb) {
+    frag_t<E> t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = sdP[(32 * kb + kslot(lg, e)) * LDE + 16 * cb + li];
+    return t;
+  };
+  auto lrec = [&](const E* b, int a, int kb) { return load_rec<E>(b + (a * KB + kb) * REC, lane); };
+  constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+  constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
-  // ---- setup
+  // ---- setup: decays, staged tiles, and the records the transposes need
   {
-    float gv = p.gamma[(size_t)ch * 64 + lane];
-    float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
+    const float gv = p.gamma[(size_t)ch * 64 + lane];
+    const float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
     if (w == 0) {
       s_gam[lane] = gv;
       s_beta[lane] = bv;
     }
     for (int e = tid; e < NW * 64 * 2 + NW * 2; e += NT) s_pg[e] = 0.f;  // s_pg, s_pb, s_misc
-    for (int e = tid; e < 64 * 64; e += NT) sEE[(e >> 6) * LDF + (e & 63)] = 0.f;
+    stage_tile<E, D>(tQ, Q + base, rowstride, L, tid, NT);
+    stage_tile<E, D>(tK, K + base, rowstride, L, tid, NT);
+    if constexpr (S::kStageDO) stage_tile<E, D>(tO, dO + base, rowstride, L, tid, NT);
   }
+  frag_t<E> vrec[2][2], drec[2][2];   // V', dV' records of this wave's column blocks
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb) {
+      vrec[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
+      drec[hs][skb] = load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
+    }
   __syncthreads();
   const float gL = s_gam[63];
   const float GL = __expf(gL);
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
 
   // ---- A' = (K K^T) * D (strict lower) and T = (I + diag(beta) A')^-1
-  {
-    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      if (t % NW != w) continue;
-      const int rr = TR[t], scb = TS[t];
-      f32x4 acc = zero4();
+  for (int t = 0; t < 10; ++t) {
+    if (t % NW != w) continue;
+    const int rr = TR[t], scb = TS[t];
+    f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc = mma(nat(K, 16 * scb + li, kb), nat(K, 16 * rr + li, kb), acc);
-      const int r = 16 * rr + li;
-      const float gr = s_gam[r];
-      float4 out;
-      float* po = reinterpret_cast<float*>(&out);
+    for (int kb = 0; kb < KB; ++kb) acc = mma(kf(scb, kb), kf(rr, kb), acc);
+    const int r = 16 * rr + li;
+    const float gr = s_gam[r];
+    float4 out;
+    float* po = reinterpret_cast<float*>(&out);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s = 16 * scb + 4 * lg + q;
-        po[q] = s < r ? acc[q] * __expf(gr - s_gam[s]) : 0.f;
-      }
-      *reinterpret_cast<float4*>(&sAp[r * LDF + 16 * scb + 4 * lg]) = out;
+    for (int q = 0; q < 4; ++q) {
+      const int s_ = 16 * scb + 4 * lg + q;
+      po[q] = s_ < r ? acc[q] * __expf(gr - s_gam[s_]) : 0.f;
     }
+    *reinterpret_cast<float4*>(&sAp[r * LDF + 16 * scb + 4 * lg]) = out;
   }
   __syncthreads();
   tri_inverse64(sAp, s_beta, sT, LDF, NW);   // ends with a barrier
 
   // ---- transposes of this wave's column slice of V' and dV' into LDS:
   //      sVt rec (sb, w) = F(V'; s, j), sdVt rec (rb, w) = F(dV'; r, j)
-  {
 #pragma unroll
-    for (int sbp = 0; sbp < 4; ++sbp) {
-      const frag_t<E> idh = (sbp & 1) ? id1 : id0;
-      const int skb = sbp >> 1;
-      f32x4 a0 = mma(load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w) * 2 + skb) * REC, lane), idh, zero4());
-      f32x4 a1 = mma(load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + 1) * 2 + skb) * REC, lane), idh, zero4());
-      store_rec<E>(sVt + (sbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
-      f32x4 b0 = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w) * 2 + skb) * REC, lane), idh, zero4());
-      f32x4 b1 = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + 1) * 2 + skb) * REC, lane), idh, zero4());
-      store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
-    }
-    // zero the blocks of dT^T that no tile writes (rows s of a higher block than r)
-    for (int e = tid; e < 64 * 64; e += NT) {
-      const int s = e >> 6, r = e & 63;
-      if ((s >> 4) > (r >> 4)) sdTt[s * LDF + r] = 0.f;
-    }
+  for (int sbp = 0; sbp < 4; ++sbp) {
+    const frag_t<E> idh = (sbp & 1) ? id1 : id0;
+    const int skb = sbp >> 1;
+    const f32x4 a0 = mma(vrec[0][skb], idh, zero4());
+    const f32x4 a1 = mma(vrec[1][skb], idh, zero4());
+    store_rec<E>(sVt + (sbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
+    const f32x4 b0 = mma(drec[0][skb], idh, zero4());
+    const f32x4 b1 = mma(drec[1][skb], idh, zero4());
+    store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
+  }
+  // zero the blocks no tile writes: dT^T rows of a higher block than the column, dP*D upper blocks
+  for (int e = tid; e < 64 * 64; e += NT) {
+    const int r = e >> 6, s_ = e & 63;
+    if ((r >> 4) > (s_ >> 4)) sdTt[r * LDF + s_] = 0.f;
+    if ((s_ >> 4) > (r >> 4)) sdP[r * LDE + s_] = (E)0.f;
+  }
+  // records of h and H' for this wave's i-slice (used after the next barrier)
+  frag_t<E> hrec[NJ], hprec[NJ];
+#pragma unroll
+  for (int jb = 0; jb < NJ; ++jb) {
+    hrec[jb] = load_rec<E>(Hf + (((size_t)ch * NJ + jb) * KB + w) * REC, lane);
+    hprec[jb] = load_rec<E>(HPf + (((size_t)ch * NJ + jb) * KB + w) * REC, lane);
   }
   __syncthreads();
 
@@ -436,47 +474,38 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
 
   // ---- dP = dO V'^T and P (lower tiles, round-robin): sdP = dP * D,
   //      dgamma += rowsum(dP * P) - colsum(dP * P)
-  {
-    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      if (t % NW != w) continue;
-      const int rb = TR[t], sb = TS[t];
-      f32x4 dp = zero4(), qk = zero4();
+  for (int t = 0; t < 10; ++t) {
+    if (t % NW != w) continue;
+    const int rb = TR[t], sb = TS[t];
+    f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        dp = mma(nat(dO, 16 * rb + li, kb), lrec(sVt, sb, kb), dp);
-        qk = mma(nat(Q, 16 * rb + li, kb), nat(K, 16 * sb + li, kb), qk);
-      }
-      // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
-      const int s = 16 * sb + li;
-      const float gs = s_gam[s];
-      float rs[4], cs = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 16 * rb + 4 * lg + q;
-        const float Dm = s <= r ? __expf(s_gam[r] - gs) : 0.f;
-        const float dpd = dp[q] * Dm;
-        sdP[r * LDF + s] = dpd;
-        const float mo = dpd * sc * qk[q];
-        rs[q] = mo;
-        cs += mo;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rs[q] = sum_in_group(rs[q]);
-      cs = sum_groups(cs);
-      if (li == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pg[16 * rb + 4 * lg + q] += rs[q];
-      }
-      if (lg == 0) pg[s] -= cs;
+    for (int kb = 0; kb < KB; ++kb) {
+      dp = mma(of(rb, kb), lrec(sVt, sb, kb), dp);
+      qk = mma(qf(rb, kb), kf(sb, kb), qk);
     }
-    // upper blocks of dP * D are zero
-    for (int e = tid; e < 64 * 64; e += NT) {
-      const int r = e >> 6, s = e & 63;
-      if ((s >> 4) > (r >> 4)) sdP[r * LDF + s] = 0.f;
+    // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
+    const int s_ = 16 * sb + li;
+    const float gs = s_gam[s_];
+    float rs[4], cs = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * rb + 4 * lg + q;
+      const float Dm = s_ <= r ? __expf(s_gam[r] - gs) : 0.f;
+      const float dpd = dp[q] * Dm;
+      sdP[r * LDE + s_] = (E)dpd;
+      const float mo = dpd * sc * qk[q];
+      rs[q] = mo;
+      cs += mo;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rs[q] = sum_in_group(rs[q]);
+    cs = sum_groups(cs);
+    if (li == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pg[16 * rb + 4 * lg + q] += rs[q];
+    }
+    if (lg == 0) pg[s_] -= cs;
   }
 
   // ---- transposes of h and H' for this wave's i-slice; dW = -dV' h^T
@@ -488,11 +517,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       const frag_t<E> idh = hs ? id1 : id0;
 #pragma unroll
       for (int jkb = 0; jkb < KB; ++jkb) {
-        const f32x4 a0 = mma(load_rec<E>(Hf + (((size_t)ch * NJ + 2 * jkb) * KB + w) * REC, lane), idh, zero4());
-        const f32x4 a1 = mma(load_rec<E>(Hf + (((size_t)ch * NJ + 2 * jkb + 1) * KB + w) * REC, lane), idh, zero4());
+        const f32x4 a0 = mma(hrec[2 * jkb], idh, zero4());
+        const f32x4 a1 = mma(hrec[2 * jkb + 1], idh, zero4());
         hT[hs][jkb] = to_frag<E>(a0, a1);
-        const f32x4 b0 = mma(load_rec<E>(HPf + (((size_t)ch * NJ + 2 * jkb) * KB + w) * REC, lane), idh, zero4());
-        const f32x4 b1 = mma(load_rec<E>(HPf + (((size_t)ch * NJ + 2 * jkb + 1) * KB + w) * REC, lane), idh, zero4());
+        const f32x4 b0 = mma(hprec[2 * jkb], idh, zero4());
+        const f32x4 b1 = mma(hprec[2 * jkb + 1], idh, zero4());
         hpT[hs][jkb] = to_frag<E>(b0, b1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) hh += a0[q] * b0[q] + a1[q] * b1[q];
@@ -526,115 +555,123 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       store_rec<E>(sdW + (rbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
     }
   }
+  // value rows for the dT product (all row blocks, all column blocks)
+  frag_t<E> vn[4][KB];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) vn[sb][kb] = gnat(V, 16 * sb + li, kb);
   __syncthreads();
 
   // ---- dT = dW Xw^T + dV' Xu^T (lower tiles, round-robin) -> sdTt[s][r], strict lower only
-  {
-    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      if (t % NW != w) continue;
-      const int rb = TR[t], sb = TS[t];
-      const int s = 16 * sb + li;
-      const float bs = s_beta[s], bgs = bs * __expf(s_gam[s]);
-      f32x4 acc = zero4();
+  for (int t = 0; t < 10; ++t) {
+    if (t % NW != w) continue;
+    const int rb = TR[t], sb = TS[t];
+    const int s_ = 16 * sb + li;
+    const float bs = s_beta[s_], bgs = bs * __expf(s_gam[s_]);
+    f32x4 acc = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x8 xw = frag_to_f32<E>(nat(K, s, kb));
-        f32x8 xu = frag_to_f32<E>(nat(V, s, kb));
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x8 xw = frag_to_f32<E>(kf(sb, kb));
+      f32x8 xu = frag_to_f32<E>(vn[sb][kb]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          xw[e] *= bgs;
-          xu[e] *= bs;
-        }
-        acc = mma(lrec(sdW, rb, kb), f32_to_frag<E>(xw), acc);
-        acc = mma(lrec(sdVt, rb, kb), f32_to_frag<E>(xu), acc);
+      for (int e = 0; e < 8; ++e) {
+        xw[e] *= bgs;
+        xu[e] *= bs;
       }
-      // lane holds dT[r = 16rb + 4lg + q][s]
-      float4 out;
-      float* po = reinterpret_cast<float*>(&out);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s ? acc[q] : 0.f;
-      *reinterpret_cast<float4*>(&sdTt[s * LDF + 16 * rb + 4 * lg]) = out;
+      acc = mma(lrec(sdW, rb, kb), f32_to_frag<E>(xw), acc);
+      acc = mma(lrec(sdVt, rb, kb), f32_to_frag<E>(xu), acc);
     }
+    // lane holds dT[r = 16rb + 4lg + q][s]
+    float4 out;
+    float* po = reinterpret_cast<float*>(&out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s_ ? acc[q] : 0.f;
+    *reinterpret_cast<float4*>(&sdTt[s_ * LDF + 16 * rb + 4 * lg]) = out;
   }
   __syncthreads();
 
   // ---- M1 = T^T dT (fp32): M1[a][s] = sum_r T[r][a] dT[r][s]; tiles s-block <= a-block -> sM1[a][s]
-  {
-    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+  for (int e = tid; e < 64 * 64; e += NT) {   // blocks no tile writes are read as zero later
+    const int a = e >> 6, s_ = e & 63;
+    if ((s_ >> 4) > (a >> 4)) sM1[a * LDF + s_] = 0.f;
+  }
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      if (t % NW != w) continue;
-      const int ab = TR[t], sb = TS[t];
-      f32x4 acc = zero4();
+  for (int t = 0; t < 10; ++t) {
+    if (t % NW != w) continue;
+    const int ab = TR[t], sb = TS[t];
+    f32x4 acc = zero4();
 #pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        if (32 * rkb + 31 < 16 * ab) continue;   // T[r][a] = 0 for r < a
-        acc = mma(mfrag32(sdTt, sb, rkb), mfragT32(sT, ab, rkb), acc);
-      }
-      // lane holds M1[a = 16ab + li][s = 16sb + 4lg + q]
-      *reinterpret_cast<f32x4*>(&sM1[(16 * ab + li) * LDF + 16 * sb + 4 * lg]) = acc;
+    for (int rkb = 0; rkb < 2; ++rkb) {
+      if (32 * rkb + 31 < 16 * ab) continue;   // T[r][a] = 0 for r < a
+      acc = mma(mfrag32(sdTt, sb, rkb), mfragT32(sT, ab, rkb), acc);
     }
+    // lane holds M1[a = 16ab + li][s = 16sb + 4lg + q]
+    *reinterpret_cast<f32x4*>(&sM1[(16 * ab + li) * LDF + 16 * sb + 4 * lg]) = acc;
   }
   __syncthreads();
 
-  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
-  {
-    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE (over A')
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      if (t % NW != w) continue;
-      const int ab = TR[t], bb = TS[t];
-      f32x4 acc = zero4();
+  for (int t = 0; t < 10; ++t) {
+    if (t % NW != w) continue;
+    const int ab = TR[t], bb = TS[t];
+    f32x4 acc = zero4();
 #pragma unroll
-      for (int skb = 0; skb < 2; ++skb) {
-        if (32 * skb > 16 * bb + 15) continue;   // T[b][s] = 0 for s > b
-        acc = mma(mfrag32(sM1, ab, skb), mfrag32(sT, bb, skb), acc);
-      }
-      // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li]
-      const int b = 16 * bb + li;
-      const float gb = s_gam[b];
-      float rs_b[4], rs_g[4], cs = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int a = 16 * ab + 4 * lg + q;
-        float da = 0.f, ap = 0.f, Dm = 0.f;
-        if (a > b) {
-          da = -acc[q];
-          ap = sAp[a * LDF + b];
-          Dm = __expf(s_gam[a] - gb);
-        }
-        const float ba = s_beta[a];
-        rs_b[q] = da * ap;
-        const float ma = da * ba * ap;
-        rs_g[q] = ma;
-        cs += ma;
-        if (a > b) {
-          const float ev = da * ba * Dm;
-          sEE[a * LDF + b] = ev;
-          sEE[b * LDF + a] = ev;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        rs_b[q] = sum_in_group(rs_b[q]);
-        rs_g[q] = sum_in_group(rs_g[q]);
-      }
-      cs = sum_groups(cs);
-      if (li == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          pb[16 * ab + 4 * lg + q] += rs_b[q];
-          pg[16 * ab + 4 * lg + q] += rs_g[q];
-        }
-      }
-      if (lg == 0) pg[b] -= cs;
+    for (int skb = 0; skb < 2; ++skb) {
+      if (32 * skb > 16 * bb + 15) continue;   // T[b][s] = 0 for s > b
+      acc = mma(mfrag32(sM1, ab, skb), mfrag32(sT, bb, skb), acc);
     }
+    // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li]
+    const int b = 16 * bb + li;
+    const float gb = s_gam[b];
+    float rs_b[4], rs_g[4], cs = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = 16 * ab + 4 * lg + q;
+      float da = 0.f, ap = 0.f, Dm = 0.f;
+      if (a > b) {
+        da = -acc[q];
+        ap = sAp[a * LDF + b];
+        Dm = __expf(s_gam[a] - gb);
+      }
+      const float ba = s_beta[a];
+      rs_b[q] = da * ap;
+      const float ma = da * ba * ap;
+      rs_g[q] = ma;
+      cs += ma;
+      if (a > b) {
+        // this lane alone reads A'[a][b]; the write below replaces it with E[a][b],
+        // and the mirrored write lands in the upper triangle, which holds no A'
+        const float ev = da * ba * Dm;
+        sEE[a * LDF + b] = ev;
+        sEE[b * LDF + a] = ev;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rs_b[q] = sum_in_group(rs_b[q]);
+      rs_g[q] = sum_in_group(rs_g[q]);
+    }
+    cs = sum_groups(cs);
+    if (li == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pb[16 * ab + 4 * lg + q] += rs_b[q];
+        pg[16 * ab + 4 * lg + q] += rs_g[q];
+      }
+    }
+    if (lg == 0) pg[b] -= cs;
   }
+  // operands of the output phase that come from global memory
+  frag_t<E> dvr[2][2], vw[4];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb) dvr[hs][rkb] = drec[hs][rkb];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, 16 * sb + li, w);
   __syncthreads();
 
   // ---- per-wave outputs
@@ -646,8 +683,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     f32x4 tk[4], tq[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      tk[sb] = mma(nat(K, 16 * sb + li, w), idh, zero4());
-      tq[sb] = mma(nat(Q, 16 * sb + li, w), idh, zero4());
+      tk[sb] = mma(kf(sb, w), idh, zero4());
+      tq[sb] = mma(qf(sb, w), idh, zero4());
     }
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -665,12 +702,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       f32x4 t1[2] = {zero4(), zero4()};
 #pragma unroll
       for (int jkb = 0; jkb < KB; ++jkb) {
-        const frag_t<E> dof = nat(dO, r, jkb);
+        const frag_t<E> dof = of(rb, jkb);
         t1[0] = mma(hT[0][jkb], dof, t1[0]);
         t1[1] = mma(hT[1][jkb], dof, t1[1]);
       }
       // dgamma(r) += Gam_r sum_i (scale Q[r][i]) t1[i][r]
-      const f32x8 qn = frag_to_f32<E>(nat(Q, r, w));
+      const f32x8 qn = frag_to_f32<E>(qf(rb, w));
       float dot = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) dot += qn[q] * t1[0][q] + qn[4 + q] * t1[1][q];
@@ -683,11 +720,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
 #pragma unroll
         for (int skb = 0; skb < 2; ++skb) {
           if (32 * skb > 16 * rb + 15) continue;
-          acc = mma(kT[hs][skb], mfrag(sdP, rb, skb), acc);
+          acc = mma(kT[hs][skb], pfrag(rb, skb), acc);
         }
         acc = scale4(acc, sc);
         if (r < L)
-          *reinterpret_cast<quad_t<E>*>(dQ + ((size_t)(tok0 + r) * H + h) * D + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
+          *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
       }
     }
   }
@@ -699,8 +736,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     float csum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      const int s = 16 * sb + li;
-      const float gs = s_gam[s], Gs = __expf(gs), bs = s_beta[s], ks = __expf(gL - gs);
+      const int s_ = 16 * sb + li;
+      const float gs = s_gam[s_], Gs = __expf(gs), bs = s_beta[s_], ks = __expf(gL - gs);
       f32x4 ta[2], tb[2], tc[2], td[2];
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
@@ -712,7 +749,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) {
         if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s], T[r][s] vanish for r < s
-        const frag_t<E> dpT = mfragT(sdP, sb, rkb);
+        const frag_t<E> dpT = pfragT(sb, rkb);
         const frag_t<E> tT = mfragT(sT, sb, rkb);
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
@@ -733,7 +770,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
         for (int hs = 0; hs < 2; ++hs) tb[hs] = mma(hpT[hs][jkb], vt, tb[hs]);
       }
       // per-s dots with k_s over this wave's i-slice: c_s and k_s . dXw_s
-      const f32x8 kn = frag_to_f32<E>(nat(K, s, w));
+      const f32x8 kn = frag_to_f32<E>(kf(sb, w));
       float dc = 0.f, dx = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -743,8 +780,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       dc = sum_groups(dc) * ks;   // c_s (partial)
       dx = sum_groups(dx);
       if (lg == 0) {
-        pg[s] += -dc + bs * Gs * dx;
-        pb[s] += Gs * dx;
+        pg[s_] += -dc + bs * Gs * dx;
+        pb[s_] += Gs * dx;
       }
       csum += (lg == 0) ? dc : 0.f;
 #pragma unroll
@@ -752,8 +789,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
         f32x4 acc;
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] = sc * ta[hs][q] + ks * tb[hs][q] + bs * Gs * tc[hs][q] + td[hs][q];
-        if (s < L)
-          *reinterpret_cast<quad_t<E>*>(dK + ((size_t)(tok0 + s) * H + h) * D + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
+        if (s_ < L)
+          *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
       }
     }
     csum = sum_in_group(csum);
@@ -765,27 +802,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     E* dV = reinterpret_cast<E*>(p.dv);
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      const int s = 16 * sb + li;
-      const float bs = s_beta[s];
+      const int s_ = 16 * sb + li;
+      const float bs = s_beta[s_];
       f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) {
         if (32 * rkb + 31 < 16 * sb) continue;
         const frag_t<E> tT = mfragT(sT, sb, rkb);
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs)
-          acc[hs] = mma(load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + hs) * 2 + rkb) * REC, lane), tT, acc[hs]);
+        for (int hs = 0; hs < 2; ++hs) acc[hs] = mma(dvr[hs][rkb], tT, acc[hs]);
       }
-      const f32x8 vn = frag_to_f32<E>(nat(V, s, w));
+      const f32x8 vv = frag_to_f32<E>(vw[sb]);
       float dot = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dot += vn[q] * acc[0][q] + vn[4 + q] * acc[1][q];
+      for (int q = 0; q < 4; ++q) dot += vv[q] * acc[0][q] + vv[4 + q] * acc[1][q];
       dot = sum_groups(dot);
-      if (lg == 0) pb[s] += dot;
+      if (lg == 0) pb[s_] += dot;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
-        if (s < L)
-          *reinterpret_cast<quad_t<E>*>(dV + ((size_t)(tok0 + s) * H + h) * D + 32 * w + 16 * hs + 4 * lg) =
+        if (s_ < L)
+          *reinterpret_cast<quad_t<E>*>(dV + base + (size_t)s_ * rowstride + 32 * w + 16 * hs + 4 * lg) =
               to_quad<E>(scale4(acc[hs], bs));
     }
   }
@@ -808,8 +844,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     float x = dgam;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_down(x, off, 64);
-      if (r + off < 64) x += t;
+      const float tt = __shfl_down(x, off, 64);
+      if (r + off < 64) x += tt;
     }
     if (r < L) {
       p.dg[(size_t)(tok0 + r) * H + h] = x;

@@ -168,3 +168,47 @@ __device__ __forceinline__ float sum_in_group(float x) {
 }
 
 }  // namespace gdn
+
+namespace gdn {
+
+// ---- natural tiles staged in LDS ----------------------------------------
+// A 64 x D tile of a token-major tensor (rows = tokens of one chunk, one
+// head) in LDS: row r at r * RB bytes (RB = D * sizeof(E)), its 16-byte
+// chunks XOR-swizzled by the row (chunk c stored at c ^ (r % NCH)) so that
+// the 16 rows of a fragment read hit distinct banks.
+template <typename E, int D>
+struct NatTile {
+  static constexpr int RB = D * (int)sizeof(E);
+  static constexpr int NCH = RB / 16;
+  static constexpr int BYTES = 64 * RB;
+  __device__ static __forceinline__ int off(int r, int byte) {
+    return r * RB + ((((byte >> 4) ^ (r & (NCH - 1))) << 4) | (byte & 15));
+  }
+};
+
+// All `nthreads` threads copy rows [0, L) of X (row r at src + r * rstride
+// elements) into the tile; rows >= L become zero.  No barrier.
+template <typename E, int D>
+__device__ __forceinline__ void stage_tile(char* tile, const E* src, size_t rstride, int L, int tid, int nthreads) {
+  using T = NatTile<E, D>;
+  for (int q = tid; q < 64 * T::NCH; q += nthreads) {
+    const int r = q / T::NCH, cidx = q - r * T::NCH;
+    int4 v = make_int4(0, 0, 0, 0);
+    if (r < L) v = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * cidx);
+    *reinterpret_cast<int4*>(tile + T::off(r, 16 * cidx)) = v;
+  }
+}
+
+// Natural fragment F(X; s, i) (index row 16*ab + li, contraction 32*kb..) from a staged tile.
+template <typename E, int D>
+__device__ __forceinline__ frag_t<E> tile_frag(const char* tile, int ab, int kb, int li, int lg) {
+  using T = NatTile<E, D>;
+  const int r = 16 * ab + li;
+  const int b0 = (32 * kb + 4 * lg) * (int)sizeof(E);
+  const int b1 = (32 * kb + 16 + 4 * lg) * (int)sizeof(E);
+  const quad_t<E> a = *reinterpret_cast<const quad_t<E>*>(tile + T::off(r, b0));
+  const quad_t<E> b = *reinterpret_cast<const quad_t<E>*>(tile + T::off(r, b1));
+  return join<E>(a, b);
+}
+
+}  // namespace gdn

@@ -20,7 +20,7 @@
 namespace gdn {
 
 // --------------------------------------------------------------------------
-// Planner: chunk table and sequence table from cu_seqlens (or dense B x T).
+// Planner: chunk table and sequence table from cu_seqlens (packed input only).
 // One workgroup: a scan over sequences for the first-chunk offsets, then a
 // binary search per chunk.
 __global__ __launch_bounds__(1024) void k_plan(Params p) {
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
-  const int4 ct = p.chunk_tab[c];
+  const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const int tid = threadIdx.x;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
   const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
   if (unit >= p.N * p.H) return;
   const int n = unit / p.H, h = unit - n * p.H;
-  const int4 st = p.seq_tab[n];
+  const int4 st = seq_info(p, n);
   const int c0 = st.x, nc = st.y;
   const size_t sbase = (size_t)unit * D * D;
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Params p) {
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
-  const int4 ct = p.chunk_tab[c];
+  const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const E* Q = reinterpret_cast<const E*>(p.q);
@@ -457,6 +457,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Params p) {
 
 // --------------------------------------------------------------------------
 hipError_t launch_plan(const Params& p, hipStream_t s) {
+  if (!p.cu) return hipSuccess;  // dense: chunk and sequence info are arithmetic
   Params a = p;
   void* args[] = {&a};
   return hipLaunchKernel((const void*)k_plan, dim3(1), dim3(1024), args, 0, s);

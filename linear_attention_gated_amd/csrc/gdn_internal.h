@@ -49,6 +49,22 @@ struct Params {
   float *Z, *dVl;
 };
 
+// Chunk c: (first token, length, sequence, index in sequence).  Dense
+// problems (no cu_seqlens) are arithmetic; packed problems read the table
+// the planner built.
+__device__ __forceinline__ int4 chunk_info(const Params& p, int c) {
+  if (p.cu) return p.chunk_tab[c];
+  const int ncs = (p.dense_T + 63) / 64;
+  const int n = c / ncs, j = c - n * ncs;
+  return make_int4(n * p.dense_T + 64 * j, min(64, p.dense_T - 64 * j), n, j);
+}
+// Sequence n: (first chunk, chunk count, first token, length).
+__device__ __forceinline__ int4 seq_info(const Params& p, int n) {
+  if (p.cu) return p.seq_tab[n];
+  const int ncs = (p.dense_T + 63) / 64;
+  return make_int4(n * ncs, ncs, n * p.dense_T, p.dense_T);
+}
+
 // Launchers (each returns the first launch error, hipSuccess otherwise).
 hipError_t launch_plan(const Params& p, hipStream_t s);
 hipError_t launch_fwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
