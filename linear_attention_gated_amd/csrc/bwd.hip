@@ -35,44 +35,72 @@ namespace gdn {
 //   Z   = (scale Gam Q)^T dO   [jb][ib] accumulator records, fp32
 //   dVl = P^T dO               [jb][sb] accumulator records, fp32
 template <typename E, int D>
+struct BwdPrepSmem {
+  static constexpr int NJ = D / 16;
+  static constexpr int TILE = NatTile<E, D>::BYTES;
+  static constexpr int LDE = sizeof(E) == 2 ? 72 : 68;
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + TILE;
+  static constexpr int oO = oK + TILE;
+  static constexpr int oDof = oO + TILE;                         // F(dO; j, r) records [jb][rkb]
+  static constexpr int oPT = oDof + NJ * 2 * REC * (int)sizeof(E);  // P^T [s][r], operand type
+  static constexpr int oG = oPT + 64 * LDE * (int)sizeof(E);
+  static constexpr int BYTES = oG + 256;
+};
+
+template <typename E, int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
-  constexpr int KB = D / 32, NJ = D / 16;
-  __shared__ float s_gam[64];
-  __shared__ __attribute__((aligned(16))) E s_dof[NJ * 2 * REC];   // F(dO; j, r) records [jb][rkb]
+  using S = BwdPrepSmem<E, D>;
+  constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDE = S::LDE;
+  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+  char* tQ = smem + S::oQ;
+  char* tK = smem + S::oK;
+  char* tO = smem + S::oO;
+  E* s_dof = reinterpret_cast<E*>(smem + S::oDof);
+  E* sPT = reinterpret_cast<E*>(smem + S::oPT);
+  float* s_gam = reinterpret_cast<float*>(smem + S::oG);
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
   const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
-  const E* Q = reinterpret_cast<const E*>(p.q);
-  const E* K = reinterpret_cast<const E*>(p.k);
-  const E* dO = reinterpret_cast<const E*>(p.dO);
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * NW;
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
   E* Ktn = reinterpret_cast<E*>(p.Ktn);
   E* WnT = reinterpret_cast<E*>(p.WnT);
+  const size_t rowstride = (size_t)H * D;
+  const size_t base = ((size_t)tok0 * H + h) * D;
+  const float sc = p.scale;
+
+  // ---- stage Q, K, dO; the -W records of this wave's i-slice
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
+  stage_tile<E, D>(tQ, reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NT);
+  stage_tile<E, D>(tK, reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NT);
+  stage_tile<E, D>(tO, reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid, NT);
+  frag_t<E> wrec[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
   __syncthreads();
   const float gL = s_gam[63];
-  const float sc = p.scale;
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
-  auto row_ptr = [&](const E* X, int row, int kb) { return X + ((size_t)(tok0 + row) * H + h) * D + 32 * kb; };
-  auto nat = [&](const E* X, int row, int kb) {
-    return row < L ? load_frag_row<E>(row_ptr(X, row, kb), lg) : zero_frag<E>();
-  };
+  auto qf = [&](int ab, int kb) { return tile_frag<E, D>(tQ, ab, kb, li, lg); };
+  auto kf = [&](int ab, int kb) { return tile_frag<E, D>(tK, ab, kb, li, lg); };
+  auto of = [&](int ab, int kb) { return tile_frag<E, D>(tO, ab, kb, li, lg); };
 
   // Ktn records (sb, kb = w): natural key rows scaled by exp(gamma_L - gamma_s)
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
-    const int s = 16 * sb + li;
-    f32x8 x = frag_to_f32<E>(nat(K, s, w));
-    const float f = __expf(gL - s_gam[s]);
+    const int s_ = 16 * sb + li;
+    f32x8 x = frag_to_f32<E>(kf(sb, w));
+    const float f = __expf(gL - s_gam[s_]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= f;
     store_rec<E>(Ktn + (((size_t)ch * 4 + sb) * KB + w) * REC, lane, f32_to_frag<E>(x));
   }
 
-  // transposes of this wave's slice of Q (scaled), dO and -W
+  // transposes of this wave's slice of Q (scaled by scale * Gam), dO and -W
   frag_t<E> dof[2][2], qg[2][2];  // F(dO; j, r), F(scale Gam Q; i, r) for block 2w + hs, rkb
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
@@ -80,10 +108,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
     f32x4 tq[4], td[4], tw[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
-      const int r = 16 * rb + li;
-      tq[rb] = mma(nat(Q, r, w), idh, zero4());
-      td[rb] = mma(nat(dO, r, w), idh, zero4());
-      tw[rb] = mma(load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane), idh, zero4());
+      tq[rb] = mma(qf(rb, w), idh, zero4());
+      td[rb] = mma(of(rb, w), idh, zero4());
+      tw[rb] = mma(wrec[rb], idh, zero4());
       // tq lane holds Q[r = 16rb + 4lg + q][i = 32w + 16hs + li]
 #pragma unroll
       for (int q = 0; q < 4; ++q) tq[rb][q] *= sc * __expf(s_gam[16 * rb + 4 * lg + q]);
@@ -97,7 +124,36 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
       store_rec<E>(WnT + (((size_t)ch * NJ + ib) * 2 + rkb) * REC, lane, to_frag<E>(tw[2 * rkb], tw[2 * rkb + 1]));
     }
   }
+
+  // P = scale (Q K^T) * D, lower incl. diagonal, one tile per wave in turn -> sPT[s][r]
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    // upper blocks of P^T (r-block < s-block) are zero
+    for (int e = tid; e < 64 * 64; e += NT) {
+      const int s_ = e >> 6, r = e & 63;
+      if ((s_ >> 4) > (r >> 4)) sPT[s_ * LDE + r] = (E)0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rb = TR[t], sb = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mma(qf(rb, kb), kf(sb, kb), acc);
+      const int s_ = 16 * sb + li;
+      const float gs = s_gam[s_];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 16 * rb + 4 * lg + q;
+        acc[q] = s_ <= r ? sc * acc[q] * __expf(s_gam[r] - gs) : 0.f;
+      }
+      // lane holds P[r = 16rb + 4lg + q][s]: four consecutive r of row s of P^T
+      *reinterpret_cast<quad_t<E>*>(sPT + s_ * LDE + 16 * rb + 4 * lg) = to_quad<E>(acc);
+    }
+  }
   __syncthreads();
+
   // Z[i][j] = sum_r (scale Gam_r Q[r][i]) dO[r][j] for this wave's i-blocks, all j-blocks
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
@@ -110,44 +166,20 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
       store_acc<float>(p.Z + (((size_t)ch * NJ + jb) * NJ + 2 * w + hs) * AREC, lane, acc);
     }
   }
-
-  // P = scale (Q K^T) * D (lower incl. diagonal); lane holds P[r = 16rb + 4lg + q][s = 16sb + li]
-  f32x4 pt[4][4];
+  // dVl[s][j] = sum_r P[r][s] dO[r][j] for this wave's j-blocks
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int sb = 0; sb < 4; ++sb) {
+    f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) pt[rb][sb] = zero4();
+    for (int rkb = 0; rkb < 2; ++rkb) {
+      if (2 * rkb + 1 < sb) continue;   // P[r][s] = 0 for r < s
+      const frag_t<E> pf = load_frag_row<E>(sPT + (16 * sb + li) * LDE + 32 * rkb, lg);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-    for (int sb = 0; sb <= rb; ++sb) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc = mma(nat(Q, 16 * rb + li, kb), nat(K, 16 * sb + li, kb), acc);
-      const int s = 16 * sb + li;
-      const float gs = s_gam[s];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 16 * rb + 4 * lg + q;
-        acc[q] = s <= r ? sc * acc[q] * __expf(s_gam[r] - gs) : 0.f;
-      }
-      pt[rb][sb] = acc;
+      for (int hs = 0; hs < 2; ++hs) acc[hs] = mma(pf, dof[hs][rkb], acc[hs]);
     }
-  }
-  // dVl[s][j] = sum_r P[r][s] dO[r][j]
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const int jb = 2 * w + hs;
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        if (2 * rkb + 1 < sb) continue;
-        acc = mma(to_frag<E>(pt[2 * rkb][sb], pt[2 * rkb + 1][sb]), dof[hs][rkb], acc);
-      }
-      store_acc<float>(p.dVl + (((size_t)ch * NJ + jb) * 4 + sb) * AREC, lane, acc);
-    }
+    for (int hs = 0; hs < 2; ++hs)
+      store_acc<float>(p.dVl + (((size_t)ch * NJ + 2 * w + hs) * 4 + sb) * AREC, lane, acc[hs]);
   }
 }
 

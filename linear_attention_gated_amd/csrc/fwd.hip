@@ -390,68 +390,109 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
 }
 
 // --------------------------------------------------------------------------
-// K3: output.  Per (chunk, head), 4 waves; wave w computes rows [16w, 16w+16).
+// K3: output.  Per (chunk, head), D/32 waves.  Q and K are staged in LDS
+// once; the masked P = scale (Q K^T) * D is computed one tile per wave in
+// turn into LDS; wave w then writes output columns [32w, 32w + 32):
 //   O^T[j][r] = Gam_r sum_i h[i][j] Q[r][i] + sum_s V'[s][j] P[r][s]
+// reading only its own column blocks of h and V'.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void k_fwd_out(Params p) {
-  constexpr int NJ = D / 16, KB = D / 32;
+struct FwdOutSmem {
+  static constexpr int TILE = NatTile<E, D>::BYTES;
+  static constexpr int LDE = sizeof(E) == 2 ? 72 : 68;
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + TILE;
+  static constexpr int oP = oK + TILE;                  // P[r][s], operand type
+  static constexpr int oG = oP + 64 * LDE * (int)sizeof(E);
+  static constexpr int BYTES = oG + 256;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
+  using S = FwdOutSmem<E, D>;
+  constexpr int NJ = D / 16, KB = D / 32, NW = D / 32, LDE = S::LDE;
+  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+  char* tQ = smem + S::oQ;
+  char* tK = smem + S::oK;
+  E* sP = reinterpret_cast<E*>(smem + S::oP);
+  float* s_gam = reinterpret_cast<float*>(smem + S::oG);
   const int ch = blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
   const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
-  const E* Q = reinterpret_cast<const E*>(p.q);
-  const E* K = reinterpret_cast<const E*>(p.k);
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * NW;
   const E* Hf = reinterpret_cast<const E*>(p.Hf);
   const E* Vf = reinterpret_cast<const E*>(p.Vf);
   E* O = reinterpret_cast<E*>(p.o);
-  const float* gam = p.gamma + (size_t)ch * 64;
+  const size_t rowstride = (size_t)H * D;
+  const size_t base = ((size_t)tok0 * H + h) * D;
 
-  const int r = 16 * w + li;
-  const float gr = gam[r];
-  frag_t<E> qf[KB];
+  if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
+  stage_tile<E, D>(tQ, reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NT);
+  stage_tile<E, D>(tK, reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NT);
+  // this wave's column blocks of h and V'
+  frag_t<E> hr[2][KB], vr[2][2];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-    qf[kb] = r < L ? load_frag_row<E>(Q + ((size_t)(tok0 + r) * H + h) * D + 32 * kb, lg) : zero_frag<E>();
-
-  // P^T tiles for s-blocks <= w: lane holds P[r][s = 16sb + 4lg + q]
-  f32x4 pt[4];
+  for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    pt[sb] = zero4();
-    if (sb > w) continue;
-    const int srow = 16 * sb + li;
-    f32x4 acc = zero4();
+    for (int kb = 0; kb < KB; ++kb) hr[hs][kb] = load_rec<E>(Hf + (((size_t)ch * NJ + 2 * w + hs) * KB + kb) * REC, lane);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const frag_t<E> kfr = srow < L ? load_frag_row<E>(K + ((size_t)(tok0 + srow) * H + h) * D + 32 * kb, lg)
-                                     : zero_frag<E>();
-      acc = mma(kfr, qf[kb], acc);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int s = 16 * sb + 4 * lg + q;
-      acc[q] = s <= r ? acc[q] * __expf(gr - gam[s]) : 0.f;
-    }
-    pt[sb] = acc;
+    for (int skb = 0; skb < 2; ++skb) vr[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
   }
-  const frag_t<E> pf0 = to_frag<E>(pt[0], pt[1]);
-  const frag_t<E> pf1 = to_frag<E>(pt[2], pt[3]);
-  const float Gr = __expf(gr);
-  const bool has1 = w >= 2;
+  // upper blocks of P are zero
+  for (int e = tid; e < 64 * 64; e += NT) {
+    const int r = e >> 6, s_ = e & 63;
+    if ((s_ >> 4) > (r >> 4)) sP[r * LDE + s_] = (E)0.f;
+  }
+  __syncthreads();
+
+  // P tiles (r-block rb, s-block sb <= rb), one per wave in turn
+  {
+    constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % NW != w) continue;
+      const int rb = TR[t], sb = TS[t];
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        acc = mma(tile_frag<E, D>(tK, sb, kb, li, lg), tile_frag<E, D>(tQ, rb, kb, li, lg), acc);
+      // lane holds (Q K^T)[r = 16rb + li][s = 16sb + 4lg + q]
+      const int r = 16 * rb + li;
+      const float gr = s_gam[r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s_ = 16 * sb + 4 * lg + q;
+        acc[q] = s_ <= r ? p.scale * acc[q] * __expf(gr - s_gam[s_]) : 0.f;
+      }
+      *reinterpret_cast<quad_t<E>*>(sP + r * LDE + 16 * sb + 4 * lg) = to_quad<E>(acc);
+    }
+  }
+  __syncthreads();
 
 #pragma unroll
-  for (int jb = 0; jb < NJ; ++jb) {
-    f32x4 acc = zero4();
+  for (int rb = 0; rb < 4; ++rb) {
+    const int r = 16 * rb + li;
+    const float Gr = p.scale * __expf(s_gam[r]);
+    frag_t<E> qfr[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) acc = mma(load_rec<E>(Hf + (((size_t)ch * NJ + jb) * KB + kb) * REC, lane), qf[kb], acc);
-    acc = scale4(acc, Gr);
-    acc = mma(load_rec<E>(Vf + (((size_t)ch * NJ + jb) * 2 + 0) * REC, lane), pf0, acc);
-    if (has1) acc = mma(load_rec<E>(Vf + (((size_t)ch * NJ + jb) * 2 + 1) * REC, lane), pf1, acc);
-    acc = scale4(acc, p.scale);
-    if (r < L)
-      *reinterpret_cast<quad_t<E>*>(O + ((size_t)(tok0 + r) * H + h) * D + 16 * jb + 4 * lg) = to_quad<E>(acc);
+    for (int kb = 0; kb < KB; ++kb) qfr[kb] = tile_frag<E, D>(tQ, rb, kb, li, lg);
+    const frag_t<E> pf0 = load_frag_row<E>(sP + r * LDE, lg);
+    const frag_t<E> pf1 = load_frag_row<E>(sP + r * LDE + 32, lg);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mma(hr[hs][kb], qfr[kb], acc);
+      acc = scale4(acc, Gr);
+      acc = mma(vr[hs][0], pf0, acc);
+      if (rb >= 2) acc = mma(vr[hs][1], pf1, acc);
+      if (r < L)
+        *reinterpret_cast<quad_t<E>*>(O + base + (size_t)r * rowstride + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
+    }
   }
 }
 
@@ -483,7 +524,7 @@ static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_fwd_out<E, D>, dim3(p.NC * p.H), dim3(256), args, 0, s);
+  return hipLaunchKernel((const void*)k_fwd_out<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 
 #define GDN_DISPATCH(fn, ...)                                        \
