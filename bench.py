@@ -42,10 +42,10 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         "fwd_state": 4 * C * D * E + D * D * E + 4,
         # reads Q, K, V' (3CD E), h (D^2 E), gamma; writes O (CD E)
         "fwd_out": 4 * C * D * E + D * D * E + C * 4,
-        # reads Q, K, dO, -W (4CD E), gamma; writes Kt, QgT, dOf, -W^T (4CD E), dV'loc (CD fp32)
-        "bwd_prep": 8 * C * D * E + C * D * 4 + C * 4,
-        # reads Kt, QgT, dOf, -W^T (4CD E), dV'loc (CD fp32), gamma_L; writes H' (D^2 E), dV' (CD E)
-        "bwd_state": 5 * C * D * E + C * D * 4 + D * D * E + 4,
+        # reads Q, K, dO, -W (4CD E), gamma; writes Kt, -W^T (2CD E), Z (D^2 fp32), dV'loc (CD fp32)
+        "bwd_prep": 6 * C * D * E + D * D * 4 + C * D * 4 + C * 4,
+        # reads Kt, -W^T (2CD E), Z (D^2 fp32), dV'loc (CD fp32), gamma; writes H' (D^2 E), dV' (CD E)
+        "bwd_state": 3 * C * D * E + D * D * 4 + C * D * 4 + D * D * E + C * 4,
         # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), gamma, beta;
         # writes dQ, dK, dV (3CD E), dg, dbeta
         "bwd_grad": 9 * C * D * E + 2 * D * D * E + 4 * C * 4,
@@ -63,8 +63,8 @@ def kernel_flops(D, units):
         "fwd_prep": C * C * D + C ** 3 // 3 + 2 * C * C * D,
         "fwd_state": 4 * C * D * D,
         "fwd_out": 2 * C * D * D + 2 * C * C * D,
-        "bwd_prep": 2 * C * C * D,
-        "bwd_state": 2 * C * D * D + 4 * C * D * D,
+        "bwd_prep": 2 * C * C * D + 2 * C * D * D,
+        "bwd_state": 4 * C * D * D,
         "bwd_grad": 8 * C * D * D + 8 * C * C * D + 2 * C ** 3 // 3,
     }
     return {k: v * units for k, v in per_unit.items()}
@@ -81,20 +81,26 @@ def sources_sha():
 
 
 def traffic_for(kernel):
-    """HBM traffic of `kernel` from committed rocprofv3 counter runs, or None
-    if there are none or the kernel sources changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE from rocprofv3
+    counter runs, scaled by a plain device copy of known size), read from the
+    committed summary; None if there is none or the kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_fwdbwd_T4096_H16_d128_bf16.txt")
     try:
-        with open(path) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+        lines = open(path).read().splitlines()
+    except OSError:
         return None
-    if t.get("sources_sha") != sources_sha():
+    sha = None
+    found = None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 2 and f[0] == "sources_sha":
+            sha = f[1]
+        if len(f) == 6 and f[0] == "traffic" and f[1] == kernel:
+            found = float(f[3]) + float(f[5])
+    if sha != sources_sha() or found is None:
         return None
-    k = t.get("kernels", {}).get(kernel)
-    if not k:
-        return None
-    return k.get("bytes_per_launch")
+    return round(found)
 
 
 def cpu_baseline(x, budget_s=10.0, max_reps=20):
