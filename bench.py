@@ -36,8 +36,8 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
     (chunk, head) unit unless noted; state kernels add their per-(sequence,
     head) state I/O."""
     per_unit = {
-        # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E)
-        "fwd_prep": 5 * C * D * E + 3 * C * 4,
+        # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E), T (C^2 fp32)
+        "fwd_prep": 5 * C * D * E + 3 * C * 4 + C * C * 4,
         # reads -W, Kt^T, U (3CD E), gamma_L; writes h (D^2 E), V' (CD E)
         "fwd_state": 4 * C * D * E + D * D * E + 4,
         # reads Q, K, V' (3CD E), h (D^2 E), gamma; writes O (CD E)
@@ -46,9 +46,9 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         "bwd_prep": 6 * C * D * E + D * D * 4 + C * D * 4 + C * 4,
         # reads Kt, -W^T (2CD E), Z (D^2 fp32), dV'loc (CD fp32), gamma; writes H' (D^2 E), dV' (CD E)
         "bwd_state": 3 * C * D * E + D * D * 4 + C * D * 4 + D * D * E + C * 4,
-        # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), gamma, beta;
+        # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), T (C^2 fp32), gamma, beta;
         # writes dQ, dK, dV (3CD E), dg, dbeta
-        "bwd_grad": 9 * C * D * E + 2 * D * D * E + 4 * C * 4,
+        "bwd_grad": 9 * C * D * E + 2 * D * D * E + C * C * 4 + 4 * C * 4,
     }
     out = {k: v * units for k, v in per_unit.items()}
     if with_ht:

@@ -71,7 +71,7 @@ struct Layout {
   bool varlen = false, bf16 = false;
   size_t esz = 0;
   // byte offsets into a workspace
-  size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0;
+  size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0, Tm = 0;
   size_t fwd_bytes = 0;
   size_t Z = 0, WnT = 0, Ktn = 0, HPf = 0, dVf = 0, dVl = 0;
   size_t bwd_bytes = 0;
@@ -139,6 +139,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->Ua = take(e * ch * 64 * D);
   L->Hf = take(e * ch * D * D);
   L->Vf = take(e * ch * 64 * D);
+  L->Tm = take(sizeof(float) * ch * 64 * 64);
   L->fwd_bytes = off;
   L->Z = take(sizeof(float) * ch * D * D);
   L->WnT = take(e * ch * 64 * D);
@@ -201,6 +202,7 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Ua = ws + L.Ua;
   P.Hf = ws + L.Hf;
   P.Vf = ws + L.Vf;
+  P.Tm = reinterpret_cast<float*>(ws + L.Tm);
   return P;
 }
 

@@ -24,7 +24,6 @@
 #include "frag.h"
 #include "gdn_internal.h"
 #include "ring.h"
-#include "tri.h"
 
 namespace gdn {
 
@@ -328,8 +327,8 @@ struct BwdGradSmem {
   static constexpr int SET = 4 * KB * RECB;             // records of a 64 x D fragment set
   static constexpr int UNI = (2 * SET > MAT) ? 2 * SET : MAT;  // dV'^T + dW, later M1
   static constexpr int TILE = NatTile<E, D>::BYTES;
-  static constexpr int oAp = 0;                         // A' = (K K^T) * D, later E + E^T
-  static constexpr int oT = oAp + MAT;
+  static constexpr int oEE = 0;                         // E + E^T
+  static constexpr int oT = oEE + MAT;                  // T, from the forward context
   static constexpr int odP = oT + MAT;                  // dP * D
   static constexpr int oVt = odP + PMAT;
   static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1
@@ -349,8 +348,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   using S = BwdGradSmem<E, D>;
   constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDF = S::LDF, LDE = S::LDE;
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
-  float* sAp = reinterpret_cast<float*>(smem + S::oAp);
-  float* sEE = sAp;
+  float* sEE = reinterpret_cast<float*>(smem + S::oEE);
   float* sT = reinterpret_cast<float*>(smem + S::oT);
   E* sdP = reinterpret_cast<E*>(smem + S::odP);
   E* sVt = reinterpret_cast<E*>(smem + S::oVt);
@@ -433,10 +431,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       s_gam[lane] = gv;
       s_beta[lane] = bv;
     }
-    for (int e = tid; e < NW * 64 * 2 + NW * 2; e += NT) s_pg[e] = 0.f;  // s_pg, s_pb, s_misc
     stage_tile<E, D>(tQ, Q + base, rowstride, L, tid, NT);
     stage_tile<E, D>(tK, K + base, rowstride, L, tid, NT);
     if constexpr (S::kStageDO) stage_tile<E, D>(tO, dO + base, rowstride, L, tid, NT);
+    // T = (I + diag(beta) A')^-1 as the forward solved it
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int r = e >> 4, c4 = e & 15;
+      *reinterpret_cast<float4*>(&sT[r * LDF + 4 * c4]) =
+          *reinterpret_cast<const float4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4);
+    }
   }
   frag_t<E> vrec[2][2], drec[2][2];   // V', dV' records of this wave's column blocks
 #pragma unroll
@@ -451,27 +454,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   const float GL = __expf(gL);
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
 
-  // ---- A' = (K K^T) * D (strict lower) and T = (I + diag(beta) A')^-1
-#pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (t % NW != w) continue;
-    const int rr = TR[t], scb = TS[t];
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) acc = mma(kf(scb, kb), kf(rr, kb), acc);
-    const int r = 16 * rr + li;
-    const float gr = s_gam[r];
-    float4 out;
-    float* po = reinterpret_cast<float*>(&out);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int s_ = 16 * scb + 4 * lg + q;
-      po[q] = s_ < r ? acc[q] * __expf(gr - s_gam[s_]) : 0.f;
-    }
-    *reinterpret_cast<float4*>(&sAp[r * LDF + 16 * scb + 4 * lg]) = out;
-  }
-  __syncthreads();
-  tri_inverse64(sAp, s_beta, sT, LDF, NW);   // ends with a barrier
 
   // ---- transposes of this wave's column slice of V' and dV' into LDS:
   //      sVt rec (sb, w) = F(V'; s, j), sdVt rec (rb, w) = F(dV'; r, j)
@@ -486,11 +468,21 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     const f32x4 b1 = mma(drec[1][skb], idh, zero4());
     store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
   }
-  // zero the blocks no tile writes: dT^T rows of a higher block than the column, dP*D upper blocks
-  for (int e = tid; e < 64 * 64; e += NT) {
-    const int r = e >> 6, s_ = e & 63;
-    if ((r >> 4) > (s_ >> 4)) sdTt[r * LDF + s_] = 0.f;
-    if ((s_ >> 4) > (r >> 4)) sdP[r * LDE + s_] = (E)0.f;
+  // zero the blocks no tile writes: the six blocks (br > bc) of dT^T and the
+  // six blocks (bc > br) of dP*D, 16 bytes per store
+  {
+    constexpr int PR = 16 * (int)sizeof(E) / 16;   // 16-byte pieces per row of a block
+    for (int e = tid; e < 6 * 64; e += NT) {
+      const int b = e >> 6, rr = (e >> 2) & 15, c4 = e & 3;
+      const int br = b < 1 ? 1 : (b < 3 ? 2 : 3), bc = b - br * (br - 1) / 2;
+      *reinterpret_cast<float4*>(&sdTt[(16 * br + rr) * LDF + 16 * bc + 4 * c4]) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int e = tid; e < 6 * 16 * PR; e += NT) {
+      const int b = e / (16 * PR), rem = e - b * 16 * PR, rr = rem / PR, pc = rem - rr * PR;
+      const int br = b < 1 ? 1 : (b < 3 ? 2 : 3), bc = b - br * (br - 1) / 2;
+      *reinterpret_cast<int4*>(reinterpret_cast<char*>(sdP + (16 * bc + rr) * LDE + 16 * br) + 16 * pc) =
+          make_int4(0, 0, 0, 0);
+    }
   }
   // records of h and H' for this wave's i-slice (used after the next barrier)
   frag_t<E> hrec[NJ], hprec[NJ];
@@ -501,8 +493,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   }
   __syncthreads();
 
-  float* pg = s_pg + w * 64;
-  float* pb = s_pb + w * 64;
+  // Per-token partial sums of dgamma and dbeta stay in registers until the
+  // end.  Column-indexed values (token 16 blk + li, equal in the four lane
+  // groups) land in lane 16 blk + li; row-indexed values (token 16 blk +
+  // 4 lg + q, equal in the 16 lanes of group lg) in lane (li = 4 blk + q, lg).
+  float dgc = 0.f, dgr = 0.f, dbc = 0.f, dbr = 0.f;
+  auto add_col = [&](float& acc, int blk, float v) { acc += (lg == blk) ? v : 0.f; };
+  auto add_row = [&](float& acc, int blk, const float* v4) {
+    const int q = li & 3;
+    const float x = q == 0 ? v4[0] : (q == 1 ? v4[1] : (q == 2 ? v4[2] : v4[3]));
+    acc += ((li >> 2) == blk) ? x : 0.f;
+  };
 
   // ---- dP = dO V'^T and P (lower tiles, round-robin): sdP = dP * D,
   //      dgamma += rowsum(dP * P) - colsum(dP * P)
@@ -533,11 +534,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) rs[q] = sum_in_group(rs[q]);
     cs = sum_groups(cs);
-    if (li == 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pg[16 * rb + 4 * lg + q] += rs[q];
-    }
-    if (lg == 0) pg[s_] -= cs;
+    add_row(dgr, rb, rs);
+    add_col(dgc, sb, -cs);
   }
 
   // ---- transposes of h and H' for this wave's i-slice; dW = -dV' h^T
@@ -600,26 +598,21 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   for (int t = 0; t < 10; ++t) {
     if (t % NW != w) continue;
     const int rb = TR[t], sb = TS[t];
+    // Xw = diag(beta Gam) K and Xu = diag(beta) V scale the columns s of the
+    // tile, so the products run on the unscaled rows
     const int s_ = 16 * sb + li;
     const float bs = s_beta[s_], bgs = bs * __expf(s_gam[s_]);
-    f32x4 acc = zero4();
+    f32x4 aw = zero4(), au = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x8 xw = frag_to_f32<E>(kf(sb, kb));
-      f32x8 xu = frag_to_f32<E>(vn[sb][kb]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xw[e] *= bgs;
-        xu[e] *= bs;
-      }
-      acc = mma(lrec(sdW, rb, kb), f32_to_frag<E>(xw), acc);
-      acc = mma(lrec(sdVt, rb, kb), f32_to_frag<E>(xu), acc);
+      aw = mma(lrec(sdW, rb, kb), kf(sb, kb), aw);
+      au = mma(lrec(sdVt, rb, kb), vn[sb][kb], au);
     }
     // lane holds dT[r = 16rb + 4lg + q][s]
     float4 out;
     float* po = reinterpret_cast<float*>(&out);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s_ ? acc[q] : 0.f;
+    for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s_ ? bgs * aw[q] + bs * au[q] : 0.f;
     *reinterpret_cast<float4*>(&sdTt[s_ * LDF + 16 * rb + 4 * lg]) = out;
   }
   __syncthreads();
@@ -649,13 +642,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   for (int t = 0; t < 10; ++t) {
     if (t % NW != w) continue;
     const int ab = TR[t], bb = TS[t];
-    f32x4 acc = zero4();
+    f32x4 acc = zero4(), kk = zero4();
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb) {
       if (32 * skb > 16 * bb + 15) continue;   // T[b][s] = 0 for s > b
       acc = mma(mfrag32(sM1, ab, skb), mfrag32(sT, bb, skb), acc);
     }
-    // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li]
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kk = mma(kf(ab, kb), kf(bb, kb), kk);
+    // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li] and (K K^T)[a][b]
     const int b = 16 * bb + li;
     const float gb = s_gam[b];
     float rs_b[4], rs_g[4], cs = 0.f;
@@ -665,20 +660,21 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       float da = 0.f, ap = 0.f, Dm = 0.f;
       if (a > b) {
         da = -acc[q];
-        ap = sAp[a * LDF + b];
         Dm = __expf(s_gam[a] - gb);
+        ap = kk[q] * Dm;   // A'[a][b]
       }
       const float ba = s_beta[a];
       rs_b[q] = da * ap;
       const float ma = da * ba * ap;
       rs_g[q] = ma;
       cs += ma;
+      // E + E^T: E strictly lower, so the diagonal is zero
+      const float ev = da * ba * Dm;
       if (a > b) {
-        // this lane alone reads A'[a][b]; the write below replaces it with E[a][b],
-        // and the mirrored write lands in the upper triangle, which holds no A'
-        const float ev = da * ba * Dm;
         sEE[a * LDF + b] = ev;
         sEE[b * LDF + a] = ev;
+      } else if (a == b) {
+        sEE[a * LDF + a] = 0.f;
       }
     }
 #pragma unroll
@@ -687,14 +683,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       rs_g[q] = sum_in_group(rs_g[q]);
     }
     cs = sum_groups(cs);
-    if (li == 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        pb[16 * ab + 4 * lg + q] += rs_b[q];
-        pg[16 * ab + 4 * lg + q] += rs_g[q];
-      }
-    }
-    if (lg == 0) pg[b] -= cs;
+    add_row(dbr, ab, rs_b);
+    add_row(dgr, ab, rs_g);
+    add_col(dgc, bb, -cs);
   }
   // operands of the output phase that come from global memory
   frag_t<E> dvr[2][2], vw[4];
@@ -745,7 +736,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       for (int q = 0; q < 4; ++q) dot += qn[q] * t1[0][q] + qn[4 + q] * t1[1][q];
       dot = sum_groups(dot);
       const float Gr = __expf(s_gam[r]);
-      if (lg == 0) pg[r] += sc * Gr * dot;
+      add_col(dgc, rb, sc * Gr * dot);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         f32x4 acc = scale4(t1[hs], Gr);
@@ -811,10 +802,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       }
       dc = sum_groups(dc) * ks;   // c_s (partial)
       dx = sum_groups(dx);
-      if (lg == 0) {
-        pg[s_] += -dc + bs * Gs * dx;
-        pb[s_] += Gs * dx;
-      }
+      add_col(dgc, sb, -dc + bs * Gs * dx);
+      add_col(dbc, sb, Gs * dx);
       csum += (lg == 0) ? dc : 0.f;
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
@@ -849,13 +838,24 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) dot += vv[q] * acc[0][q] + vv[4 + q] * acc[1][q];
       dot = sum_groups(dot);
-      if (lg == 0) pb[s_] += dot;
+      add_col(dbc, sb, dot);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
         if (s_ < L)
           *reinterpret_cast<quad_t<E>*>(dV + base + (size_t)s_ * rowstride + 32 * w + 16 * hs + 4 * lg) =
               to_quad<E>(scale4(acc[hs], bs));
     }
+  }
+  {
+    // this wave's slots: the row-indexed sums are stored, the column-indexed
+    // ones added (one wave's LDS accesses complete in order)
+    float* pg = s_pg + w * 64;
+    float* pb = s_pb + w * 64;
+    const int tr = 16 * (li >> 2) + 4 * lg + (li & 3);
+    pg[tr] = dgr;
+    pb[tr] = dbr;
+    pg[lane] += dgc;
+    pb[lane] += dbc;
   }
   __syncthreads();
 

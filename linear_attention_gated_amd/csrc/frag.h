@@ -152,18 +152,27 @@ __device__ __forceinline__ float wave_incl_scan(float x, int lane) {
   return x;
 }
 
-// Sum over the four lane groups (lanes li, li+16, li+32, li+48).
-__device__ __forceinline__ float sum_groups(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+// Cross-lane reductions on the VALU (no LDS crossbar traffic).  Every lane
+// ends with the same bits: each step adds a value to its mirror image, and
+// both partners add the same two operands.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// Sum over the 16 lanes of a group.
+// Sum over the four lane groups (lanes li, li+16, li+32, li+48): the
+// permlane16 swap pairs rows 2k and 2k+1, the permlane32 swap the halves.
+__device__ __forceinline__ float sum_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Sum over the 16 lanes of a group: DPP quad permutes (lane ^ 1, lane ^ 2),
+// then the half-row mirror (quad q <-> q ^ 1) and the row mirror (halves).
 __device__ __forceinline__ float sum_in_group(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
   return x;
 }
 

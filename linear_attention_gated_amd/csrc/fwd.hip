@@ -80,9 +80,9 @@ __global__ __launch_bounds__(1024) void k_plan(Params p) {
 }
 
 // --------------------------------------------------------------------------
-// K1: per (chunk, head): gamma, A, T = (I + A)^-1, and the fragment-native
-// operands of the state pass: -W, Kt^T, U.  D/32 waves; wave w owns feature
-// columns [32w, 32w + 32).
+// K1: per (chunk, head): gamma, A, T = (I + A)^-1 (also stored for the
+// backward), and the fragment-native operands of the state pass: -W, Kt^T,
+// U.  D/32 waves; wave w owns feature columns [32w, 32w + 32).
 template <typename E, int D>
 __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   constexpr int NW = D / 32;
@@ -153,8 +153,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   }
   __syncthreads();
 
-  // T = (I + A)^-1 (ends with a barrier)
+  // T = (I + A)^-1 (ends with a barrier); kept for the backward
   tri_inverse64(sA, nullptr, sT, LDA, NW);
+  for (int e = tid; e < 64 * 16; e += 64 * NW) {
+    const int r = e >> 4, c4 = e & 15;
+    *reinterpret_cast<float4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4) =
+        *reinterpret_cast<const float4*>(&sT[r * LDA + 4 * c4]);
+  }
 
   // T fragments F(T; r, s) (lower triangular: (rb <= 1, skb = 1) is zero)
   frag_t<E> tf[4][2];

@@ -17,6 +17,7 @@ constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 //   Ua  acc U[r][j]      [D/16][4]        WY values (accumulator records)
 //   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
 //   Vf  F(V'; j, s)      [D/16][2]        corrected values
+//   Tm  T[r][s] fp32     64 x 64 row-major  (I + A)^-1, upper blocks zero
 //   Z   acc Z[i][j]      [D/16 jb][D/16 ib] fp32  backward: (scale Gam Q)^T dO
 //   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
 //   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
@@ -45,6 +46,7 @@ struct Params {
 
   float* gamma;           // [NC][H][64] chunk-local cumulative log decay
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
+  float* Tm;
   void *WnT, *Ktn, *HPf, *dVf;
   float *Z, *dVl;
 };
