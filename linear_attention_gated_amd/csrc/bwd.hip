@@ -75,9 +75,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
 
   // ---- stage Q, K, dO; the -W records of this wave's i-slice
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
-  stage_tile<E, D>(tQ, reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NT);
-  stage_tile<E, D>(tK, reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NT);
-  stage_tile<E, D>(tO, reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid, NT);
+  {
+    TileStage<E, D, NT> sq, sk, so;
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
+    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid);
+    so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
+    sq.store(tQ, tid);
+    sk.store(tK, tid);
+    so.store(tO, tid);
+  }
   frag_t<E> wrec[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
@@ -431,14 +437,25 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       s_gam[lane] = gv;
       s_beta[lane] = bv;
     }
-    stage_tile<E, D>(tQ, Q + base, rowstride, L, tid, NT);
-    stage_tile<E, D>(tK, K + base, rowstride, L, tid, NT);
-    if constexpr (S::kStageDO) stage_tile<E, D>(tO, dO + base, rowstride, L, tid, NT);
+    TileStage<E, D, NT> sq, sk, so;
+    sq.load(Q + base, rowstride, L, tid);
+    sk.load(K + base, rowstride, L, tid);
+    if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
     // T = (I + diag(beta) A')^-1 as the forward solved it
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int r = e >> 4, c4 = e & 15;
-      *reinterpret_cast<float4*>(&sT[r * LDF + 4 * c4]) =
-          *reinterpret_cast<const float4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4);
+    constexpr int TPER = 64 * 16 / NT;
+    f32x4 tv[TPER];
+#pragma unroll
+    for (int k = 0; k < TPER; ++k) {
+      const int e = tid + k * NT, r = e >> 4, c4 = e & 15;
+      tv[k] = *reinterpret_cast<const f32x4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4);
+    }
+    sq.store(tQ, tid);
+    sk.store(tK, tid);
+    if constexpr (S::kStageDO) so.store(tO, tid);
+#pragma unroll
+    for (int k = 0; k < TPER; ++k) {
+      const int e = tid + k * NT, r = e >> 4, c4 = e & 15;
+      *reinterpret_cast<f32x4*>(&sT[r * LDF + 4 * c4]) = tv[k];
     }
   }
   frag_t<E> vrec[2][2], drec[2][2];   // V', dV' records of this wave's column blocks

@@ -39,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 template <typename E> struct VecT;
 template <> struct VecT<bf16> { using x8 = bf16x8; using x4 = bf16x4; };
@@ -195,18 +196,33 @@ struct NatTile {
   }
 };
 
-// All `nthreads` threads copy rows [0, L) of X (row r at src + r * rstride
-// elements) into the tile; rows >= L become zero.  No barrier.
-template <typename E, int D>
-__device__ __forceinline__ void stage_tile(char* tile, const E* src, size_t rstride, int L, int tid, int nthreads) {
+// One thread's share of a staged tile, NTHR threads per tile: load() issues
+// every global read of rows [0, L) of X (row r at src + r * rstride
+// elements; rows >= L read as zero), store() writes the swizzled LDS tile.
+// Loading several tiles before storing any keeps all their reads in flight.
+template <typename E, int D, int NTHR>
+struct TileStage {
   using T = NatTile<E, D>;
-  for (int q = tid; q < 64 * T::NCH; q += nthreads) {
-    const int r = q / T::NCH, cidx = q - r * T::NCH;
-    int4 v = make_int4(0, 0, 0, 0);
-    if (r < L) v = *reinterpret_cast<const int4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * cidx);
-    *reinterpret_cast<int4*>(tile + T::off(r, 16 * cidx)) = v;
+  static constexpr int N = 64 * T::NCH;   // 16-byte pieces of the tile
+  static_assert(N % NTHR == 0, "tile pieces must divide over the threads");
+  static constexpr int PER = N / NTHR;
+  i32x4 v[PER];
+  __device__ __forceinline__ void load(const E* src, size_t rstride, int L, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
+      v[k] = i32x4{0, 0, 0, 0};
+      if (r < L) v[k] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * c);
+    }
   }
-}
+  __device__ __forceinline__ void store(char* tile, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
+      *reinterpret_cast<i32x4*>(tile + T::off(r, 16 * c)) = v[k];
+    }
+  }
+};
 
 // Natural fragment F(X; s, i) (index row 16*ab + li, contraction 32*kb..) from a staged tile.
 template <typename E, int D>

@@ -435,8 +435,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   const size_t base = ((size_t)tok0 * H + h) * D;
 
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
-  stage_tile<E, D>(tQ, reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NT);
-  stage_tile<E, D>(tK, reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NT);
+  {
+    TileStage<E, D, NT> sq, sk;
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
+    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid);
+    sq.store(tQ, tid);
+    sk.store(tK, tid);
+  }
   // this wave's column blocks of h and V'
   frag_t<E> hr[2][KB], vr[2][2];
 #pragma unroll
