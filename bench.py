@@ -42,10 +42,10 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         "fwd_state": 4 * C * D * E + D * D * E + 4,
         # reads Q, K, V' (3CD E), h (D^2 E), gamma; writes O (CD E)
         "fwd_out": 4 * C * D * E + D * D * E + C * 4,
-        # reads Q, K, dO, -W (4CD E), gamma; writes Kt, -W^T (2CD E), Z (D^2 fp32), dV'loc (CD fp32)
-        "bwd_prep": 6 * C * D * E + D * D * 4 + C * D * 4 + C * 4,
-        # reads Kt, -W^T (2CD E), Z (D^2 fp32), dV'loc (CD fp32), gamma; writes H' (D^2 E), dV' (CD E)
-        "bwd_state": 3 * C * D * E + D * D * 4 + C * D * 4 + D * D * E + C * 4,
+        # reads Q, K, dO, -W (4CD E), gamma; writes Kt, -W^T (2CD E), Z (D^2 E), dV'loc (CD E)
+        "bwd_prep": 7 * C * D * E + D * D * E + C * 4,
+        # reads Kt, -W^T (2CD E), Z (D^2 E), dV'loc (CD E), gamma; writes H' (D^2 E), dV' (CD E)
+        "bwd_state": 4 * C * D * E + 2 * D * D * E + C * 4,
         # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), T (C^2 fp32), gamma, beta;
         # writes dQ, dK, dV (3CD E), dg, dbeta
         "bwd_grad": 9 * C * D * E + 2 * D * D * E + C * C * 4 + 4 * C * 4,

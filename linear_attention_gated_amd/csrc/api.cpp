@@ -141,12 +141,12 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->Vf = take(e * ch * 64 * D);
   L->Tm = take(sizeof(float) * ch * 64 * 64);
   L->fwd_bytes = off;
-  L->Z = take(sizeof(float) * ch * D * D);
+  L->Z = take(e * ch * D * D);
   L->WnT = take(e * ch * 64 * D);
   L->Ktn = take(e * ch * 64 * D);
   L->HPf = take(e * ch * D * D);
   L->dVf = take(e * ch * 64 * D);
-  L->dVl = take(sizeof(float) * ch * 64 * D);
+  L->dVl = take(e * ch * 64 * D);
   L->bwd_bytes = off;
   return GDN_OK;
 }
@@ -345,8 +345,8 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     gdn::Params P = base_params(p, L, ctx);
     P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0;
     P.dO = d_o; P.dht = dht; P.dq = dq; P.dk = dk; P.dv = dv; P.dg = dg; P.dbeta = dbeta; P.dh0 = dh0;
-    P.Z = reinterpret_cast<float*>(ws + L.Z); P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
-    P.HPf = ws + L.HPf; P.dVf = ws + L.dVf; P.dVl = reinterpret_cast<float*>(ws + L.dVl);
+    P.Z = ws + L.Z; P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
+    P.HPf = ws + L.HPf; P.dVf = ws + L.dVf; P.dVl = ws + L.dVl;
     const int D = (int)L.D;
     hipError_t e;
     if (!fwd_workspace) {

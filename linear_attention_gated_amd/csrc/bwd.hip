@@ -134,11 +134,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   {
     constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
     constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    // upper blocks of P^T (r-block < s-block) are zero
-    for (int e = tid; e < 64 * 64; e += NT) {
-      const int s_ = e >> 6, r = e & 63;
-      if ((s_ >> 4) > (r >> 4)) sPT[s_ * LDE + r] = (E)0.f;
-    }
+    // blocks of P^T with s-block > r-block are zero
+    zero_off_blocks<E, false>(sPT, LDE, tid, NT);
 #pragma unroll
     for (int t = 0; t < 10; ++t) {
       if (t % NW != w) continue;
@@ -168,7 +165,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
     for (int hs = 0; hs < 2; ++hs) {
       f32x4 acc = mma(qg[hs][0], d0, zero4());
       acc = mma(qg[hs][1], d1, acc);
-      store_acc<float>(p.Z + (((size_t)ch * NJ + jb) * NJ + 2 * w + hs) * AREC, lane, acc);
+      store_acc<E>(reinterpret_cast<E*>(p.Z) + (((size_t)ch * NJ + jb) * NJ + 2 * w + hs) * AREC, lane, acc);
     }
   }
   // dVl[s][j] = sum_r P[r][s] dO[r][j] for this wave's j-blocks
@@ -184,7 +181,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
     }
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
-      store_acc<float>(p.dVl + (((size_t)ch * NJ + 2 * w + hs) * 4 + sb) * AREC, lane, acc[hs]);
+      store_acc<E>(reinterpret_cast<E*>(p.dVl) + (((size_t)ch * NJ + 2 * w + hs) * 4 + sb) * AREC, lane, acc[hs]);
   }
 }
 
@@ -202,8 +199,8 @@ struct BwdRing {
   static constexpr int oK = 0;
   static constexpr int oW = oK + 4 * KB * RECB;
   static constexpr int oZ = oW + NJ * 2 * RECB;
-  static constexpr int oV = oZ + NJ * AREC * 4;
-  static constexpr int oG = oV + 4 * AREC * 4;
+  static constexpr int oV = oZ + NJ * AREC * (int)sizeof(E);
+  static constexpr int oG = oV + 4 * AREC * (int)sizeof(E);
   static constexpr int SLOT = oG + 256;
   static constexpr int S = ring_slots(SLOT);
 };
@@ -232,8 +229,8 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
     char* sl = ring + (t % S) * R::SLOT;
     dma_kib(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane);
     dma_kib(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane);
-    dma_kib(p.Z + (ch * NJ + jb) * NJ * AREC, sl + R::oZ, NJ * AREC * 4, lane);
-    dma_kib(p.dVl + (ch * NJ + jb) * 4 * AREC, sl + R::oV, 4 * AREC * 4, lane);
+    dma_kib(reinterpret_cast<const E*>(p.Z) + (ch * NJ + jb) * NJ * AREC, sl + R::oZ, NJ * AREC * (int)sizeof(E), lane);
+    dma_kib(reinterpret_cast<const E*>(p.dVl) + (ch * NJ + jb) * 4 * AREC, sl + R::oV, 4 * AREC * (int)sizeof(E), lane);
     dma_256(p.gamma + ch * 64, sl + R::oG, lane);
   };
   if (w >= 1 && w - 1 < nc) issue(w - 1);
@@ -267,14 +264,14 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         for (int kb = 0; kb < KB; ++kb)
           kn[sb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (sb * KB + kb) * REC, lane);
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) dv[sb] = load_acc<float>(reinterpret_cast<const float*>(sl + R::oV) + sb * AREC, lane);
+      for (int sb = 0; sb < 4; ++sb) dv[sb] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oV) + sb * AREC, lane);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib)
 #pragma unroll
         for (int rkb = 0; rkb < 2; ++rkb)
           wt[ib][rkb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (ib * 2 + rkb) * REC, lane);
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) z[ib] = load_acc<float>(reinterpret_cast<const float*>(sl + R::oZ) + ib * AREC, lane);
+      for (int ib = 0; ib < NJ; ++ib) z[ib] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oZ) + ib * AREC, lane);
       const float GL = __expf(reinterpret_cast<const float*>(sl + R::oG)[63]);
       __builtin_amdgcn_sched_barrier(0);
       frag_t<E> hfr[KB];
@@ -485,22 +482,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     const f32x4 b1 = mma(drec[1][skb], idh, zero4());
     store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
   }
-  // zero the blocks no tile writes: the six blocks (br > bc) of dT^T and the
-  // six blocks (bc > br) of dP*D, 16 bytes per store
-  {
-    constexpr int PR = 16 * (int)sizeof(E) / 16;   // 16-byte pieces per row of a block
-    for (int e = tid; e < 6 * 64; e += NT) {
-      const int b = e >> 6, rr = (e >> 2) & 15, c4 = e & 3;
-      const int br = b < 1 ? 1 : (b < 3 ? 2 : 3), bc = b - br * (br - 1) / 2;
-      *reinterpret_cast<float4*>(&sdTt[(16 * br + rr) * LDF + 16 * bc + 4 * c4]) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    for (int e = tid; e < 6 * 16 * PR; e += NT) {
-      const int b = e / (16 * PR), rem = e - b * 16 * PR, rr = rem / PR, pc = rem - rr * PR;
-      const int br = b < 1 ? 1 : (b < 3 ? 2 : 3), bc = b - br * (br - 1) / 2;
-      *reinterpret_cast<int4*>(reinterpret_cast<char*>(sdP + (16 * bc + rr) * LDE + 16 * br) + 16 * pc) =
-          make_int4(0, 0, 0, 0);
-    }
-  }
+  // zero the blocks no tile writes: dT^T below the block diagonal, dP*D above
+  zero_off_blocks<float, false>(sdTt, LDF, tid, NT);
+  zero_off_blocks<E, true>(sdP, LDE, tid, NT);
   // records of h and H' for this wave's i-slice (used after the next barrier)
   frag_t<E> hrec[NJ], hprec[NJ];
 #pragma unroll
@@ -635,10 +619,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   __syncthreads();
 
   // ---- M1 = T^T dT (fp32): M1[a][s] = sum_r T[r][a] dT[r][s]; tiles s-block <= a-block -> sM1[a][s]
-  for (int e = tid; e < 64 * 64; e += NT) {   // blocks no tile writes are read as zero later
-    const int a = e >> 6, s_ = e & 63;
-    if ((s_ >> 4) > (a >> 4)) sM1[a * LDF + s_] = 0.f;
-  }
+  zero_off_blocks<float, true>(sM1, LDF, tid, NT);   // blocks no tile writes are read as zero later
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
     if (t % NW != w) continue;

@@ -224,6 +224,22 @@ struct TileStage {
   }
 };
 
+// Zero the six 16 x 16 blocks strictly above (UPPER: column block > row
+// block) or strictly below the block diagonal of a 64 x 64 LDS matrix of X
+// (row stride ld elements, rows 16-byte aligned), one 16-byte store per
+// piece, spread over nthr threads.  No barrier.
+template <typename X, bool UPPER>
+__device__ __forceinline__ void zero_off_blocks(X* M, int ld, int tid, int nthr) {
+  constexpr int PR = 16 * (int)sizeof(X) / 16;   // pieces per block row
+  constexpr int N = 6 * 16 * PR;
+  for (int e = tid; e < N; e += nthr) {
+    const int b = e / (16 * PR), rem = e - b * 16 * PR, rr = rem / PR, pc = rem - rr * PR;
+    const int hi = b < 1 ? 1 : (b < 3 ? 2 : 3), lo = b - hi * (hi - 1) / 2;
+    const int br = UPPER ? lo : hi, bc = UPPER ? hi : lo;
+    *reinterpret_cast<i32x4*>(reinterpret_cast<char*>(M + (16 * br + rr) * ld + 16 * bc) + 16 * pc) = i32x4{0, 0, 0, 0};
+  }
+}
+
 // Natural fragment F(X; s, i) (index row 16*ab + li, contraction 32*kb..) from a staged tile.
 template <typename E, int D>
 __device__ __forceinline__ frag_t<E> tile_frag(const char* tile, int ab, int kb, int li, int lg) {

@@ -84,12 +84,12 @@ __global__ __launch_bounds__(1024) void k_plan(Params p) {
 // backward), and the fragment-native operands of the state pass: -W, Kt^T,
 // U.  D/32 waves; wave w owns feature columns [32w, 32w + 32).
 template <typename E, int D>
-__global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
+__global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 1))) void k_fwd_prep(Params p) {
   constexpr int NW = D / 32;
   constexpr int KB = D / 32;
   constexpr int LDA = 68;
-  __shared__ float sA[64 * LDA];
-  __shared__ float sT[64 * LDA];
+  __shared__ __attribute__((aligned(16))) float sA[64 * LDA];
+  __shared__ __attribute__((aligned(16))) float sT[64 * LDA];
   __shared__ float s_gam[64], s_beta[64];
 
   const int ch = blockIdx.x;
@@ -115,8 +115,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
     p.gamma[(size_t)ch * 64 + lane] = gam;
   }
 
-  // natural key fragments F(K; s, i) for all row blocks
-  frag_t<E> kf[4][KB];
+  // natural key fragments F(K; s, i) for all row blocks, and this wave's
+  // value columns (used after the solve; their reads overlap it)
+  frag_t<E> kf[4][KB], vfw[4];
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
     const int row = 16 * sb + li;
@@ -124,6 +125,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
     for (int kb = 0; kb < KB; ++kb)
       kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
                            : zero_frag<E>();
+    vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
+                      : zero_frag<E>();
   }
   __syncthreads();
 
@@ -151,6 +154,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
       *reinterpret_cast<float4*>(&sA[r * LDA + 16 * sc + 4 * lg]) = out;
     }
   }
+  // this wave's key columns F(K; s, i in 32w..32w+31)
+  frag_t<E> kw[4];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    kw[sb] = kf[sb][0];
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb)
+      if (kb == w) kw[sb] = kf[sb][kb];
+  }
   __syncthreads();
 
   // T = (I + A)^-1 (ends with a barrier); kept for the backward
@@ -161,17 +173,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
         *reinterpret_cast<const float4*>(&sT[r * LDA + 4 * c4]);
   }
 
-  // T fragments F(T; r, s) (lower triangular: (rb <= 1, skb = 1) is zero)
-  frag_t<E> tf[4][2];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int skb = 0; skb < 2; ++skb) {
-      const float* row = sT + (16 * rb + li) * LDA + 32 * skb;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * lg);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg);
-      tf[rb][skb] = to_frag<E>(a, b);
-    }
+  // T fragments F(T; r, s), read where used (lower triangular: (rb <= 1, skb = 1) is zero)
+  auto tfrag = [&](int rb, int skb) {
+    const float* row = sT + (16 * rb + li) * LDA + 32 * skb;
+    return to_frag<E>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
+  };
 
   const float gL = s_gam[63];
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
@@ -181,26 +187,20 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   f32x4 kt[4][2];
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
-    const int row = 16 * sb + li;
-    const frag_t<E> kw = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
-                                 : zero_frag<E>();
-    kt[sb][0] = mma(kw, id0, zero4());
-    kt[sb][1] = mma(kw, id1, zero4());
+    kt[sb][0] = mma(kw[sb], id0, zero4());
+    kt[sb][1] = mma(kw[sb], id1, zero4());
   }
-  // per-row scales for rows s = 16sb + 4lg + q
-  float sc_w[4][4], sc_k[4][4], sc_u[4][4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb)
+  // per-row scales of rows s = 16sb + 4lg + q: beta Gam (W), exp(gL - gamma) (Kt), beta (U)
+  auto rowscale = [&](f32x4 x, int sb, int kind) {
+    f32x4 y;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int s = 16 * sb + 4 * lg + q;
-      const float gs = s_gam[s], bs = s_beta[s];
-      sc_w[sb][q] = bs * __expf(gs);
-      sc_k[sb][q] = __expf(gL - gs);
-      sc_u[sb][q] = bs;
+      const float gs = s_gam[s];
+      const float f = kind == 0 ? s_beta[s] * __expf(gs) : (kind == 1 ? __expf(gL - gs) : s_beta[s]);
+      y[q] = x[q] * f;
     }
-  auto rowscale = [](f32x4 x, const float* s4) {
-    return f32x4{x[0] * s4[0], x[1] * s4[1], x[2] * s4[2], x[3] * s4[3]};
+    return y;
   };
 
   E* Ktf = reinterpret_cast<E*>(p.Ktf);
@@ -213,10 +213,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
   for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb) {
-      xw[hs][skb] = to_frag<E>(rowscale(kt[2 * skb][hs], sc_w[2 * skb]),
-                               rowscale(kt[2 * skb + 1][hs], sc_w[2 * skb + 1]));
-      const frag_t<E> kk = to_frag<E>(rowscale(kt[2 * skb][hs], sc_k[2 * skb]),
-                                      rowscale(kt[2 * skb + 1][hs], sc_k[2 * skb + 1]));
+      xw[hs][skb] = to_frag<E>(rowscale(kt[2 * skb][hs], 2 * skb, 0), rowscale(kt[2 * skb + 1][hs], 2 * skb + 1, 0));
+      const frag_t<E> kk = to_frag<E>(rowscale(kt[2 * skb][hs], 2 * skb, 1), rowscale(kt[2 * skb + 1][hs], 2 * skb + 1, 1));
       const int ib = 2 * w + hs;
       store_rec<E>(Ktf + ((rec_ch * NJ + ib) * 2 + skb) * REC, lane, kk);
     }
@@ -228,20 +226,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb) {
       if (rb <= 1 && skb == 1) continue;
-      wt0 = mma(xw[0][skb], tf[rb][skb], wt0);
-      wt1 = mma(xw[1][skb], tf[rb][skb], wt1);
+      const frag_t<E> tf = tfrag(rb, skb);
+      wt0 = mma(xw[0][skb], tf, wt0);
+      wt1 = mma(xw[1][skb], tf, wt1);
     }
     store_rec<E>(Wn + ((rec_ch * 4 + rb) * KB + w) * REC, lane, to_frag<E>(-wt0, -wt1));
   }
 
   // V transposes and U = T diag(beta) V
-  frag_t<E> vfw[4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    const int row = 16 * sb + li;
-    vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
-                      : zero_frag<E>();
-  }
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
     const frag_t<E> idh = hs ? id1 : id0;
@@ -251,7 +243,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
     frag_t<E> xu[2];
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb)
-      xu[skb] = to_frag<E>(rowscale(vt[2 * skb], sc_u[2 * skb]), rowscale(vt[2 * skb + 1], sc_u[2 * skb + 1]));
+      xu[skb] = to_frag<E>(rowscale(vt[2 * skb], 2 * skb, 2), rowscale(vt[2 * skb + 1], 2 * skb + 1, 2));
     const int jb = 2 * w + hs;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -259,7 +251,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_prep(Params p) {
 #pragma unroll
       for (int skb = 0; skb < 2; ++skb) {
         if (rb <= 1 && skb == 1) continue;
-        u = mma(tf[rb][skb], xu[skb], u);
+        u = mma(tfrag(rb, skb), xu[skb], u);
       }
       store_acc<E>(Ua + ((rec_ch * NJ + jb) * 4 + rb) * AREC, lane, u);
     }
@@ -452,10 +444,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
     for (int skb = 0; skb < 2; ++skb) vr[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
   }
   // upper blocks of P are zero
-  for (int e = tid; e < 64 * 64; e += NT) {
-    const int r = e >> 6, s_ = e & 63;
-    if ((s_ >> 4) > (r >> 4)) sP[r * LDE + s_] = (E)0.f;
-  }
+  zero_off_blocks<E, true>(sP, LDE, tid, NT);
   __syncthreads();
 
   // P tiles (r-block rb, s-block sb <= rb), one per wave in turn

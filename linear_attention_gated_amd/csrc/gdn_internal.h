@@ -18,10 +18,10 @@ constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 //   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
 //   Vf  F(V'; j, s)      [D/16][2]        corrected values
 //   Tm  T[r][s] fp32     64 x 64 row-major  (I + A)^-1, upper blocks zero
-//   Z   acc Z[i][j]      [D/16 jb][D/16 ib] fp32  backward: (scale Gam Q)^T dO
+//   Z   acc Z[i][j]      [D/16 jb][D/16 ib]  backward: (scale Gam Q)^T dO
 //   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
 //   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
-//   dVl acc dV'loc[s][j] [D/16][4] fp32   backward: intra-chunk part of dV'
+//   dVl acc dV'loc[s][j] [D/16][4]        backward: intra-chunk part of dV'
 //   HPf F(H'; j, i)      [D/16][D/32]     backward: state gradient after the chunk
 //   dVf F(dV'; j, r)     [D/16][2]        backward: gradient of V'
 struct Params {
@@ -48,7 +48,7 @@ struct Params {
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
   float* Tm;
   void *WnT, *Ktn, *HPf, *dVf;
-  float *Z, *dVl;
+  void *Z, *dVl;
 };
 
 // Chunk c: (first token, length, sequence, index in sequence).  Dense

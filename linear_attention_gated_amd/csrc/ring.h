@@ -42,9 +42,9 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Number of slots that fit in ~150 KiB of LDS, between 2 and 4.
+// Number of slots that fit in the 160 KiB of LDS, between 2 and 4.
 constexpr int ring_slots(int slot_bytes) {
-  return (150 * 1024 / slot_bytes) >= 4 ? 4 : ((150 * 1024 / slot_bytes) >= 3 ? 3 : 2);
+  return (160 * 1024 / slot_bytes) >= 4 ? 4 : ((160 * 1024 / slot_bytes) >= 3 ? 3 : 2);
 }
 
 }  // namespace gdn

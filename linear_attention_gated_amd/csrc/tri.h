@@ -45,11 +45,7 @@ __device__ __forceinline__ void store_acc16(float* M, int ld, int r0, int c0, in
 // zero).  All `nw` waves of the workgroup call this; it ends with a barrier.
 __device__ inline void tri_inverse64(const float* M, const float* rs, float* T, int ld, int nw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
-  // zero the strictly upper blocks
-  for (int e = threadIdx.x; e < 64 * 64; e += 64 * nw) {
-    const int r = e >> 6, s = e & 63;
-    if ((s >> 4) > (r >> 4)) T[r * ld + s] = 0.f;
-  }
+  zero_off_blocks<float, true>(T, ld, threadIdx.x, 64 * nw);
   // diagonal blocks
   for (int b = w; b < 4; b += nw) {
     const int o = 16 * b;
