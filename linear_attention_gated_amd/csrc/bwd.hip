@@ -235,8 +235,8 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
   };
   if (w >= 1 && w - 1 < nc) issue(w - 1);
 
-  f32x4 hs[NJ];
   if (w == 0) {
+    f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
       if (p.dht) {
@@ -246,69 +246,108 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         hs[ib] = zero4();
       }
     }
-  }
-
-  for (int t = 0; t < nc; ++t) {
-    const bool mine = w >= 1 && (t % (S - 1)) == w - 1;
-    if (mine) wait_vmem();
-    ring_barrier();
-    if (w == 0) {
-      const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
-      const char* sl = ring + (t % S) * R::SLOT;
-      // all of this step's LDS operands first, then the products
+    // One chunk's LDS operands.  Where registers allow (bf16, or d = 64),
+    // two sets alternate: the next chunk's set is read from its slot while
+    // this chunk's second product runs.
+    constexpr bool kPipe = sizeof(E) == 2 || D <= 64;
+    // Values are kept as read (dVl and Z in the storage type, raw gamma_L)
+    // and converted where the step uses them, so nothing in the step waits
+    // for the reads of the next set.
+    struct Ops {
       frag_t<E> kn[4][KB], wt[NJ][2];
-      f32x4 dv[4], z[NJ];
+      quad_t<E> dv[4], z[NJ];
+      float gL;
+    };
+    auto read_ops = [&](Ops& o, int t) {
+      const char* sl = ring + (t % S) * R::SLOT;
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          kn[sb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (sb * KB + kb) * REC, lane);
+          o.kn[sb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (sb * KB + kb) * REC, lane);
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) dv[sb] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oV) + sb * AREC, lane);
+      for (int sb = 0; sb < 4; ++sb) o.dv[sb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oV) + sb * AREC + 4 * lane);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib)
 #pragma unroll
         for (int rkb = 0; rkb < 2; ++rkb)
-          wt[ib][rkb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (ib * 2 + rkb) * REC, lane);
+          o.wt[ib][rkb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (ib * 2 + rkb) * REC, lane);
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) z[ib] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oZ) + ib * AREC, lane);
-      const float GL = __expf(reinterpret_cast<const float*>(sl + R::oG)[63]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ib = 0; ib < NJ; ++ib) o.z[ib] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oZ) + ib * AREC + 4 * lane);
+      o.gL = reinterpret_cast<const float*>(sl + R::oG)[63];
+    };
+    auto step = [&](int t, Ops& cur, Ops& nxt) {
+      const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
       frag_t<E> hfr[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      f32x4 dv[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) dv[sb] = quad_to_f32<E>(cur.dv[sb]);
       // dV' = dVl + Kt H'
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) dv[sb] = mma(kn[sb][kb], hfr[kb], dv[sb]);
+        for (int sb = 0; sb < 4; ++sb) dv[sb] = mma(cur.kn[sb][kb], hfr[kb], dv[sb]);
+      // exp(gamma_L) H' + Z, off the product's critical path
+      const float GL = __expf(cur.gL);
+#pragma unroll
+      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL) + quad_to_f32<E>(cur.z[ib]);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      if (kPipe && t + 1 < nc) {
+        // this chunk's reads are complete: release its slot, fetch the next
+        wait_lds();
+        ring_barrier();
+        read_ops(nxt, t + 1);
+      }
       frag_t<E> dvf[2];
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
       // H' <- exp(gamma_L) H' + Z - W^T dV'
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL) + z[ib];
-#pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb)
 #pragma unroll
-        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(wt[ib][rkb], dvf[rkb], hs[ib]);
+        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(cur.wt[ib][rkb], dvf[rkb], hs[ib]);
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
-      wait_lds();
-    } else if (mine && t + S - 1 < nc) {
-      issue(t + S - 1);
+    };
+    if constexpr (kPipe) {
+      if (nc > 0) {
+        Ops A, B;
+        ring_barrier();
+        read_ops(A, 0);
+        for (int t = 0; t < nc; t += 2) {
+          step(t, A, B);
+          if (t + 1 < nc) step(t + 1, B, A);
+        }
+      }
+    } else {
+      Ops A;
+      for (int t = 0; t < nc; ++t) {
+        ring_barrier();
+        read_ops(A, t);
+        step(t, A, A);
+        wait_lds();
+      }
     }
-  }
-  if (w == 0 && p.dh0) {
+    if (p.dh0) {
 #pragma unroll
-    for (int ib = 0; ib < NJ; ++ib) {
-      float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-      dst[0] = hs[ib][0];
-      dst[D] = hs[ib][1];
-      dst[2 * D] = hs[ib][2];
-      dst[3 * D] = hs[ib][3];
+      for (int ib = 0; ib < NJ; ++ib) {
+        float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        dst[0] = hs[ib][0];
+        dst[D] = hs[ib][1];
+        dst[2 * D] = hs[ib][2];
+        dst[3 * D] = hs[ib][3];
+      }
+    }
+  } else {
+    // loader wave w: steps t with t % (S - 1) == w - 1, S - 1 ahead
+    for (int t = 0; t < nc; ++t) {
+      const bool mine = (t % (S - 1)) == w - 1;
+      if (mine) wait_vmem();
+      ring_barrier();
+      if (mine && t + S - 1 < nc) issue(t + S - 1);
     }
   }
 }

@@ -308,8 +308,8 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
   };
   if (w >= 1 && w - 1 < nc) issue(w - 1);
 
-  f32x4 hs[NJ];
   if (w == 0) {
+    f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
       if (p.h0) {
@@ -319,69 +319,107 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
         hs[ib] = zero4();
       }
     }
-  }
-
-  for (int ci = 0; ci < nc; ++ci) {
-    const bool mine = w >= 1 && (ci % (S - 1)) == w - 1;
-    if (mine) wait_vmem();
-    ring_barrier();
-    if (w == 0) {
-      const size_t ch = (size_t)(c0 + ci) * p.H + h;
-      const char* sl = ring + (ci % S) * R::SLOT;
-      // all of this step's LDS operands first, then the products
+    // One chunk's LDS operands.  Where registers allow (bf16, or d = 64),
+    // two sets alternate: the next chunk's set is read from its slot while
+    // this chunk's second product runs.
+    constexpr bool kPipe = sizeof(E) == 2 || D <= 64;
+    // Values are kept as read (U in the storage type, raw gamma_L) and
+    // converted where the step uses them, so nothing in the step waits for
+    // the reads of the next set.
+    struct Ops {
       frag_t<E> wf[4][KB], kf[NJ][2];
-      f32x4 vp[4];
+      quad_t<E> u[4];
+      float gL;
+    };
+    auto read_ops = [&](Ops& o, int ci) {
+      const char* sl = ring + (ci % S) * R::SLOT;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-          wf[rb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (rb * KB + kb) * REC, lane);
+          o.wf[rb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (rb * KB + kb) * REC, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        vp[rb] = load_acc<E>(reinterpret_cast<const E*>(sl + R::oU) + rb * AREC, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      // Kt^T reads stay in flight while the V' products run
+        o.u[rb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oU) + rb * AREC + 4 * lane);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib)
 #pragma unroll
         for (int skb = 0; skb < 2; ++skb)
-          kf[ib][skb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (ib * 2 + skb) * REC, lane);
-      const float GL = __expf(reinterpret_cast<const float*>(sl + R::oG)[63]);
-      __builtin_amdgcn_sched_barrier(0);
+          o.kf[ib][skb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (ib * 2 + skb) * REC, lane);
+      o.gL = reinterpret_cast<const float*>(sl + R::oG)[63];
+    };
+    auto step = [&](int ci, Ops& cur, Ops& nxt) {
+      const size_t ch = (size_t)(c0 + ci) * p.H + h;
       frag_t<E> hfr[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) hfr[kb] = to_frag<E>(hs[2 * kb], hs[2 * kb + 1]);
+      f32x4 vp[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) vp[rb] = quad_to_f32<E>(cur.u[rb]);
       // V' = U - W h: contraction outermost so consecutive MFMAs are independent
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) vp[rb] = mma(wf[rb][kb], hfr[kb], vp[rb]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
-      frag_t<E> vfr[2];
-#pragma unroll
-      for (int skb = 0; skb < 2; ++skb) vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
+        for (int rb = 0; rb < 4; ++rb) vp[rb] = mma(cur.wf[rb][kb], hfr[kb], vp[rb]);
+      // decay of the state, off the product's critical path
+      const float GL = __expf(cur.gL);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL);
 #pragma unroll
+      for (int kb = 0; kb < KB; ++kb) store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      if (kPipe && ci + 1 < nc) {
+        // this chunk's reads are complete: release its slot, fetch the next
+        wait_lds();
+        ring_barrier();
+        read_ops(nxt, ci + 1);
+      }
+      frag_t<E> vfr[2];
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
+      // h <- exp(gamma_L) h + Kt^T V'
+#pragma unroll
       for (int skb = 0; skb < 2; ++skb)
 #pragma unroll
-        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(kf[ib][skb], vfr[skb], hs[ib]);
+        for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(cur.kf[ib][skb], vfr[skb], hs[ib]);
 #pragma unroll
       for (int skb = 0; skb < 2; ++skb) store_rec<E>(Vf + ((ch * NJ + jb) * 2 + skb) * REC, lane, vfr[skb]);
-      wait_lds();
-    } else if (mine && ci + S - 1 < nc) {
-      issue(ci + S - 1);
+    };
+    if constexpr (kPipe) {
+      if (nc > 0) {
+        Ops A, B;
+        ring_barrier();
+        read_ops(A, 0);
+        for (int ci = 0; ci < nc; ci += 2) {
+          step(ci, A, B);
+          if (ci + 1 < nc) step(ci + 1, B, A);
+        }
+      }
+    } else {
+      Ops A;
+      for (int ci = 0; ci < nc; ++ci) {
+        ring_barrier();
+        read_ops(A, ci);
+        step(ci, A, A);
+        wait_lds();
+      }
     }
-  }
-  if (w == 0 && write_ht && p.ht) {
+    if (write_ht && p.ht) {
 #pragma unroll
-    for (int ib = 0; ib < NJ; ++ib) {
-      float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-      dst[0] = hs[ib][0];
-      dst[D] = hs[ib][1];
-      dst[2 * D] = hs[ib][2];
-      dst[3 * D] = hs[ib][3];
+      for (int ib = 0; ib < NJ; ++ib) {
+        float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        dst[0] = hs[ib][0];
+        dst[D] = hs[ib][1];
+        dst[2 * D] = hs[ib][2];
+        dst[3 * D] = hs[ib][3];
+      }
+    }
+  } else {
+    // loader wave w: chunks ci with ci % (S - 1) == w - 1, S - 1 ahead
+    for (int ci = 0; ci < nc; ++ci) {
+      const bool mine = (ci % (S - 1)) == w - 1;
+      if (mine) wait_vmem();
+      ring_barrier();
+      if (mine && ci + S - 1 < nc) issue(ci + S - 1);
     }
   }
 }
