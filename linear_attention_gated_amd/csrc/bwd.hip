@@ -353,27 +353,30 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
 }
 
 // --------------------------------------------------------------------------
-// K6: per (chunk, head) gradients dq, dk, dv, dbeta, dg.  D/32 waves; wave w
-// owns feature columns [32w, 32w+32) of dq/dk (i) and dv (j).  Quantities
-// that need every column (dP, dW for dT, T, dT, dA, E) are shared through
-// LDS; sums over waves use per-wave slots so the result is deterministic.
+// K6: per (chunk, head) gradients dq, dk, dv, dbeta, dg.  D/16 waves; wave
+// w owns the 16 feature columns [16w, 16w+16) of dq/dk (i) and dv (j);
+// column block w is half hw = w % 2 of the 32-wide contraction block
+// kw = w / 2.  Quantities that need every column (dP, dW for dT, T, dT, dA,
+// E) are shared through LDS, their 16 x 16 tiles dealt round-robin over the
+// waves; sums over waves use per-wave slots so the result is deterministic.
 template <typename E, int D>
 struct BwdGradSmem {
   static constexpr int KB = D / 32;
-  static constexpr int NW = D / 32;
+  static constexpr int NW = D / 16;
   static constexpr int LDF = 68;                        // fp32 64x64 matrices, padded rows
   static constexpr int MAT = 64 * LDF * 4;
   static constexpr int LDE = sizeof(E) == 2 ? 72 : 68;  // operand-type 64x64 matrix
   static constexpr int PMAT = 64 * LDE * (int)sizeof(E);
   static constexpr int RECB = REC * (int)sizeof(E);
   static constexpr int SET = 4 * KB * RECB;             // records of a 64 x D fragment set
-  static constexpr int UNI = (2 * SET > MAT) ? 2 * SET : MAT;  // dV'^T + dW, later M1
+  static constexpr int UNI = (2 * SET > MAT + 6 * RECB) ? 2 * SET : MAT + 6 * RECB;  // dV'^T + dW, later M1 + (dP*D)^T
   static constexpr int TILE = NatTile<E, D>::BYTES;
-  static constexpr int oEE = 0;                         // E + E^T
-  static constexpr int oT = oEE + MAT;                  // T, from the forward context
+  static constexpr int oEE = 0;                         // E + E^T, operand type
+  static constexpr int oT = oEE + PMAT;                 // T, from the forward context
   static constexpr int odP = oT + MAT;                  // dP * D
   static constexpr int oVt = odP + PMAT;
-  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1
+  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1 | sPDt
+  static constexpr int oPDt = oU + MAT;
   static constexpr int odTt = oU + UNI;
   static constexpr int oQ = odTt + MAT;                 // staged natural tiles
   static constexpr int oK = oQ + TILE;
@@ -386,11 +389,11 @@ struct BwdGradSmem {
 };
 
 template <typename E, int D>
-__global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
+__global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   using S = BwdGradSmem<E, D>;
-  constexpr int KB = D / 32, NJ = D / 16, NW = D / 32, LDF = S::LDF, LDE = S::LDE;
+  constexpr int KB = D / 32, NJ = D / 16, NW = D / 16, LDF = S::LDF, LDE = S::LDE;
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
-  float* sEE = reinterpret_cast<float*>(smem + S::oEE);
+  E* sEE = reinterpret_cast<E*>(smem + S::oEE);
   float* sT = reinterpret_cast<float*>(smem + S::oT);
   E* sdP = reinterpret_cast<E*>(smem + S::odP);
   E* sVt = reinterpret_cast<E*>(smem + S::oVt);
@@ -398,6 +401,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   E* sdW = reinterpret_cast<E*>(smem + S::oU + S::SET);
   float* sM1 = reinterpret_cast<float*>(smem + S::oU);
   float* sdTt = reinterpret_cast<float*>(smem + S::odTt);
+  E* sTt = reinterpret_cast<E*>(smem + S::odTt);       // after M1: F(T; s, r) records
+  E* sPDt = reinterpret_cast<E*>(smem + S::oPDt);      // after M1: F(dP*D; s, r) records
   char* tQ = smem + S::oQ;
   char* tK = smem + S::oK;
   char* tO = smem + S::odO;
@@ -413,6 +418,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   const int4 ct = chunk_info(p, c);
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
+  const int kw = w >> 1, hw = w & 1;
   const int tid = threadIdx.x;
   constexpr int NT = 64 * NW;
   const E* Q = reinterpret_cast<const E*>(p.q);
@@ -441,7 +447,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     const float* row = M + (16 * ab + li) * LDF + 32 * kb;
     return to_frag<float>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
   };
-  auto mfrag = [&](const float* M, int ab, int kb) { return f32_to_frag<E>(frag_to_f32<float>(mfrag32(M, ab, kb))); };
   // the same read transposed: index = columns 16cb.., contraction = rows 32kb..
   auto mfragT32 = [&](const float* M, int cb, int kb) {
     f32x8 t;
@@ -450,11 +455,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     return t;
   };
   auto mfragT = [&](const float* M, int cb, int kb) { return f32_to_frag<E>(mfragT32(M, cb, kb)); };
-  // operand-type dP*D matrix
-  auto pfrag = [&](int ab, int kb) {
-    const E* row = sdP + (16 * ab + li) * LDE + 32 * kb;
-    return load_frag_row<E>(row, lg);
-  };
+  // operand-type 64 x 64 matrices (dP*D, E + E^T)
+  auto efrag = [&](const E* M, int ab, int kb) { return load_frag_row<E>(M + (16 * ab + li) * LDE + 32 * kb, lg); };
   auto pfragT = [&](int cb, int kb) {
     frag_t<E> t;
 #pragma unroll
@@ -462,6 +464,25 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     return t;
   };
   auto lrec = [&](const E* b, int a, int kb) { return load_rec<E>(b + (a * KB + kb) * REC, lane); };
+  // records of lower-triangular 64 x 64 matrices read transposed, F(X; s, r)
+  // for the six (s-block sb, r-block rkb) with a nonzero entry
+  auto tri_idx = [](int sb, int rkb) { return sb < 2 ? 2 * sb + rkb : sb + 2; };
+  auto trec = [&](const E* b, int sb, int rkb) { return load_rec<E>(b + tri_idx(sb, rkb) * REC, lane); };
+  // half hw of a record: the four elements a 16-column block contributes
+  auto store_half = [&](E* rec, f32x4 x) {
+    *reinterpret_cast<quad_t<E>*>(rec + 8 * lane + 4 * hw) = to_quad<E>(x);
+  };
+  // a record read for an identity transpose that keeps half hw of the
+  // contraction: the other half is never multiplied by a nonzero
+  auto load_half = [&](const E* rec) {
+    const quad_t<E> x = *reinterpret_cast<const quad_t<E>*>(rec + 8 * lane + 4 * hw);
+    const quad_t<E> z = to_quad<E>(zero4());
+    return hw ? join<E>(z, x) : join<E>(x, z);
+  };
+  // the four elements of a natural fragment that fall in this wave's columns
+  auto my4 = [&](f32x8 x) {
+    return hw ? f32x4{x[4], x[5], x[6], x[7]} : f32x4{x[0], x[1], x[2], x[3]};
+  };
   constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
   constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
@@ -494,42 +515,36 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       *reinterpret_cast<f32x4*>(&sT[r * LDF + 4 * c4]) = tv[k];
     }
   }
-  frag_t<E> vrec[2][2], drec[2][2];   // V', dV' records of this wave's column blocks
+  frag_t<E> vrec[2], drec[2];   // F(V'; j, s), F(dV'; j, r) of column block w
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-    for (int skb = 0; skb < 2; ++skb) {
-      vrec[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
-      drec[hs][skb] = load_rec<E>(dVf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
-    }
+  for (int skb = 0; skb < 2; ++skb) {
+    vrec[skb] = load_rec<E>(Vf + (((size_t)ch * NJ + w) * 2 + skb) * REC, lane);
+    drec[skb] = load_rec<E>(dVf + (((size_t)ch * NJ + w) * 2 + skb) * REC, lane);
+  }
   __syncthreads();
   const float gL = s_gam[63];
   const float GL = __expf(gL);
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
+  const frag_t<E> idw = hw ? id1 : id0;
 
-
-  // ---- transposes of this wave's column slice of V' and dV' into LDS:
-  //      sVt rec (sb, w) = F(V'; s, j), sdVt rec (rb, w) = F(dV'; r, j)
+  // ---- transposes of this wave's column block of V' and dV' into LDS:
+  //      half hw of sVt rec (sb, kw) = F(V'; s, j), of sdVt rec (rb, kw) = F(dV'; r, j)
 #pragma unroll
   for (int sbp = 0; sbp < 4; ++sbp) {
     const frag_t<E> idh = (sbp & 1) ? id1 : id0;
     const int skb = sbp >> 1;
-    const f32x4 a0 = mma(vrec[0][skb], idh, zero4());
-    const f32x4 a1 = mma(vrec[1][skb], idh, zero4());
-    store_rec<E>(sVt + (sbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
-    const f32x4 b0 = mma(drec[0][skb], idh, zero4());
-    const f32x4 b1 = mma(drec[1][skb], idh, zero4());
-    store_rec<E>(sdVt + (sbp * KB + w) * REC, lane, to_frag<E>(b0, b1));
+    store_half(sVt + (sbp * KB + kw) * REC, mma(vrec[skb], idh, zero4()));
+    store_half(sdVt + (sbp * KB + kw) * REC, mma(drec[skb], idh, zero4()));
   }
   // zero the blocks no tile writes: dT^T below the block diagonal, dP*D above
   zero_off_blocks<float, false>(sdTt, LDF, tid, NT);
   zero_off_blocks<E, true>(sdP, LDE, tid, NT);
-  // records of h and H' for this wave's i-slice (used after the next barrier)
+  // halves of the h and H' records this wave's i-block needs (used after the next barrier)
   frag_t<E> hrec[NJ], hprec[NJ];
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
-    hrec[jb] = load_rec<E>(Hf + (((size_t)ch * NJ + jb) * KB + w) * REC, lane);
-    hprec[jb] = load_rec<E>(HPf + (((size_t)ch * NJ + jb) * KB + w) * REC, lane);
+    hrec[jb] = load_half(Hf + (((size_t)ch * NJ + jb) * KB + kw) * REC);
+    hprec[jb] = load_half(HPf + (((size_t)ch * NJ + jb) * KB + kw) * REC);
   }
   __syncthreads();
 
@@ -578,82 +593,76 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     add_col(dgc, sb, -cs);
   }
 
-  // ---- transposes of h and H' for this wave's i-slice; dW = -dV' h^T
-  frag_t<E> hT[2][KB], hpT[2][KB];   // F(h; i, j), F(H'; i, j) for i-block 2w + hs
+  // ---- transposes of h and H' for this wave's i-block; dW = -dV' h^T
+  frag_t<E> hT[KB], hpT[KB];   // F(h; i, j), F(H'; i, j) for i-block w
   {
     float hh = 0.f;
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const frag_t<E> idh = hs ? id1 : id0;
+    for (int jkb = 0; jkb < KB; ++jkb) {
+      const f32x4 a0 = mma(hrec[2 * jkb], idw, zero4());
+      const f32x4 a1 = mma(hrec[2 * jkb + 1], idw, zero4());
+      hT[jkb] = to_frag<E>(a0, a1);
+      const f32x4 b0 = mma(hprec[2 * jkb], idw, zero4());
+      const f32x4 b1 = mma(hprec[2 * jkb + 1], idw, zero4());
+      hpT[jkb] = to_frag<E>(b0, b1);
 #pragma unroll
-      for (int jkb = 0; jkb < KB; ++jkb) {
-        const f32x4 a0 = mma(hrec[2 * jkb], idh, zero4());
-        const f32x4 a1 = mma(hrec[2 * jkb + 1], idh, zero4());
-        hT[hs][jkb] = to_frag<E>(a0, a1);
-        const f32x4 b0 = mma(hprec[2 * jkb], idh, zero4());
-        const f32x4 b1 = mma(hprec[2 * jkb + 1], idh, zero4());
-        hpT[hs][jkb] = to_frag<E>(b0, b1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hh += a0[q] * b0[q] + a1[q] * b1[q];
-      }
+      for (int q = 0; q < 4; ++q) hh += a0[q] * b0[q] + a1[q] * b1[q];
     }
     hh = sum_in_group(sum_groups(hh));
     if (lane == 0) s_misc[2 * w + 1] = hh;
   }
-  frag_t<E> dWir[2][2];  // F(dW; i, r) for i-block 2w + hs, rkb
+  frag_t<E> dWir[2];  // F(dW; i, r) for i-block w, rkb
   {
-    f32x4 dw[4][2];
+    f32x4 dw[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb) {
+      f32x4 acc = zero4();
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int jkb = 0; jkb < KB; ++jkb) acc = mma(lrec(sdVt, rb, jkb), hT[hs][jkb], acc);
-        dw[rb][hs] = -acc;   // lane holds dW[r = 16rb + 4lg + q][i = 32w + 16hs + li]
-      }
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) dWir[hs][rkb] = to_frag<E>(dw[2 * rkb][hs], dw[2 * rkb + 1][hs]);
-    // F(dW; r, i) records (rb, w) for the dT product
-#pragma unroll
-    for (int rbp = 0; rbp < 4; ++rbp) {
-      const frag_t<E> idh = (rbp & 1) ? id1 : id0;
-      const f32x4 a0 = mma(dWir[0][rbp >> 1], idh, zero4());
-      const f32x4 a1 = mma(dWir[1][rbp >> 1], idh, zero4());
-      store_rec<E>(sdW + (rbp * KB + w) * REC, lane, to_frag<E>(a0, a1));
+      for (int jkb = 0; jkb < KB; ++jkb) acc = mma(lrec(sdVt, rb, jkb), hT[jkb], acc);
+      dw[rb] = -acc;   // lane holds dW[r = 16rb + 4lg + q][i = 16w + li]
     }
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb) dWir[rkb] = to_frag<E>(dw[2 * rkb], dw[2 * rkb + 1]);
+    // half hw of the F(dW; r, i) records (rb, kw) for the dT product
+#pragma unroll
+    for (int rbp = 0; rbp < 4; ++rbp)
+      store_half(sdW + (rbp * KB + kw) * REC, mma(dWir[rbp >> 1], (rbp & 1) ? id1 : id0, zero4()));
   }
-  // value rows for the dT product (all row blocks, all column blocks)
-  frag_t<E> vn[4][KB];
+  // value rows of this wave's dT tiles
+  constexpr int NTT = (10 + NW - 1) / NW;   // dT tiles per wave, at most
+  frag_t<E> vn[NTT][KB];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb)
+  for (int k = 0; k < NTT; ++k) {
+    const int t = w + NW * k;
+    const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+    const int sbt = t - rbt * (rbt + 1) / 2;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) vn[sb][kb] = gnat(V, 16 * sb + li, kb);
+    for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, 16 * sbt + li, kb) : zero_frag<E>();
+  }
   __syncthreads();
 
-  // ---- dT = dW Xw^T + dV' Xu^T (lower tiles, round-robin) -> sdTt[s][r], strict lower only
+  // ---- dT = dW Xw^T + dV' Xu^T (lower tiles, round-robin) -> sdTt[s][r], strict lower only.
+  //      Xw = diag(beta Gam) K and Xu = diag(beta) V scale the columns s of the
+  //      tile, so the products run on the unscaled rows.
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (t % NW != w) continue;
-    const int rb = TR[t], sb = TS[t];
-    // Xw = diag(beta Gam) K and Xu = diag(beta) V scale the columns s of the
-    // tile, so the products run on the unscaled rows
+  for (int k = 0; k < NTT; ++k) {
+    const int t = w + NW * k;
+    if (t >= 10) continue;
+    const int rb = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+    const int sb = t - rb * (rb + 1) / 2;
     const int s_ = 16 * sb + li;
     const float bs = s_beta[s_], bgs = bs * __expf(s_gam[s_]);
     f32x4 aw = zero4(), au = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       aw = mma(lrec(sdW, rb, kb), kf(sb, kb), aw);
-      au = mma(lrec(sdVt, rb, kb), vn[sb][kb], au);
+      au = mma(lrec(sdVt, rb, kb), vn[k][kb], au);
     }
     // lane holds dT[r = 16rb + 4lg + q][s]
-    float4 out;
-    float* po = reinterpret_cast<float*>(&out);
+    f32x4 out;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) po[q] = (16 * rb + 4 * lg + q) > s_ ? bgs * aw[q] + bs * au[q] : 0.f;
-    *reinterpret_cast<float4*>(&sdTt[s_ * LDF + 16 * rb + 4 * lg]) = out;
+    for (int q = 0; q < 4; ++q) out[q] = (16 * rb + 4 * lg + q) > s_ ? bgs * aw[q] + bs * au[q] : 0.f;
+    *reinterpret_cast<f32x4*>(&sdTt[s_ * LDF + 16 * rb + 4 * lg]) = out;
   }
   __syncthreads();
 
@@ -674,7 +683,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   }
   __syncthreads();
 
-  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE (over A')
+  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
     if (t % NW != w) continue;
@@ -706,12 +715,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
       rs_g[q] = ma;
       cs += ma;
       // E + E^T: E strictly lower, so the diagonal is zero
-      const float ev = da * ba * Dm;
+      const E ev = (E)(da * ba * Dm);
       if (a > b) {
-        sEE[a * LDF + b] = ev;
-        sEE[b * LDF + a] = ev;
+        sEE[a * LDE + b] = ev;
+        sEE[b * LDE + a] = ev;
       } else if (a == b) {
-        sEE[a * LDF + a] = 0.f;
+        sEE[a * LDE + a] = (E)0.f;
       }
     }
 #pragma unroll
@@ -724,68 +733,79 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
     add_row(dgr, ab, rs_g);
     add_col(dgc, bb, -cs);
   }
+  // transposed records of T and dP*D for the output phase, once per workgroup
+  // (sdTt is free after M1; the dP*D records sit above sM1)
+  for (int k = NW - 1 - w; k < 12; k += NW) {
+    const int kk = k < 6 ? k : k - 6;
+    const int sb = kk < 4 ? kk >> 1 : kk - 2, rkb = kk < 4 ? kk & 1 : 1;
+    frag_t<E> x;
+    if (k < 6) {
+      x = mfragT(sT, sb, rkb);
+      store_rec<E>(sTt + kk * REC, lane, x);
+    } else {
+      x = pfragT(sb, rkb);
+      store_rec<E>(sPDt + kk * REC, lane, x);
+    }
+  }
   // operands of the output phase that come from global memory
-  frag_t<E> dvr[2][2], vw[4];
+  frag_t<E> vw[4];
 #pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-    for (int rkb = 0; rkb < 2; ++rkb) dvr[hs][rkb] = drec[hs][rkb];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, 16 * sb + li, w);
+  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, 16 * sb + li, kw);
   __syncthreads();
 
   // ---- per-wave outputs
-  // K and Q transposes for this wave's i-slice: F(K; i, s), F(Q; i, r)
-  frag_t<E> kT[2][2], qT[2][2];
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const frag_t<E> idh = hs ? id1 : id0;
+  // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
+  frag_t<E> kT[2], qT[2];
+  {
     f32x4 tk[4], tq[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      tk[sb] = mma(kf(sb, w), idh, zero4());
-      tq[sb] = mma(qf(sb, w), idh, zero4());
+      tk[sb] = mma(kf(sb, kw), idw, zero4());
+      tq[sb] = mma(qf(sb, kw), idw, zero4());
     }
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      kT[hs][kb2] = to_frag<E>(tk[2 * kb2], tk[2 * kb2 + 1]);
-      qT[hs][kb2] = to_frag<E>(tq[2 * kb2], tq[2 * kb2 + 1]);
+      kT[kb2] = to_frag<E>(tk[2 * kb2], tk[2 * kb2 + 1]);
+      qT[kb2] = to_frag<E>(tq[2 * kb2], tq[2 * kb2 + 1]);
     }
   }
 
-  // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s])
+  // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s]);
+  // the four row blocks run side by side so consecutive MFMAs are independent
   {
     E* dQ = reinterpret_cast<E*>(p.dq);
+    f32x4 t1[4], aq[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      t1[rb] = zero4();
+      aq[rb] = zero4();
+    }
+#pragma unroll
+    for (int jkb = 0; jkb < KB; ++jkb)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) t1[rb] = mma(hT[jkb], of(rb, jkb), t1[rb]);
+#pragma unroll
+    for (int skb = 0; skb < 2; ++skb)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        if (32 * skb > 16 * rb + 15) continue;
+        aq[rb] = mma(kT[skb], efrag(sdP, rb, skb), aq[rb]);
+      }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = 16 * rb + li;
-      f32x4 t1[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int jkb = 0; jkb < KB; ++jkb) {
-        const frag_t<E> dof = of(rb, jkb);
-        t1[0] = mma(hT[0][jkb], dof, t1[0]);
-        t1[1] = mma(hT[1][jkb], dof, t1[1]);
-      }
       // dgamma(r) += Gam_r sum_i (scale Q[r][i]) t1[i][r]
-      const f32x8 qn = frag_to_f32<E>(qf(rb, w));
+      const f32x4 qn = my4(frag_to_f32<E>(qf(rb, kw)));
       float dot = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dot += qn[q] * t1[0][q] + qn[4 + q] * t1[1][q];
+      for (int q = 0; q < 4; ++q) dot += qn[q] * t1[rb][q];
       dot = sum_groups(dot);
       const float Gr = __expf(s_gam[r]);
       add_col(dgc, rb, sc * Gr * dot);
+      f32x4 acc;
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        f32x4 acc = scale4(t1[hs], Gr);
-#pragma unroll
-        for (int skb = 0; skb < 2; ++skb) {
-          if (32 * skb > 16 * rb + 15) continue;
-          acc = mma(kT[hs][skb], pfrag(rb, skb), acc);
-        }
-        acc = scale4(acc, sc);
-        if (r < L)
-          *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
-      }
+      for (int q = 0; q < 4; ++q) acc[q] = sc * (Gr * t1[rb][q] + aq[rb][q]);
+      if (r < L) *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
     }
   }
 
@@ -793,63 +813,49 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   //            + beta_s Gam_s sum_r dW[r][i] T[r][s] + sum_r K[r][i] (E + E^T)[s][r]
   {
     E* dK = reinterpret_cast<E*>(p.dk);
+    f32x4 ta[4], tb[4], tc[4], td[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      ta[sb] = zero4();
+      tb[sb] = zero4();
+      tc[sb] = zero4();
+      td[sb] = zero4();
+    }
+#pragma unroll
+    for (int jkb = 0; jkb < KB; ++jkb)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) tb[sb] = mma(hpT[jkb], lrec(sVt, sb, jkb), tb[sb]);
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        td[sb] = mma(kT[rkb], efrag(sEE, sb, rkb), td[sb]);
+        if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s], T[r][s] vanish for r < s
+        ta[sb] = mma(qT[rkb], trec(sPDt, sb, rkb), ta[sb]);
+        tc[sb] = mma(dWir[rkb], trec(sTt, sb, rkb), tc[sb]);
+      }
     float csum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const int s_ = 16 * sb + li;
       const float gs = s_gam[s_], Gs = __expf(gs), bs = s_beta[s_], ks = __expf(gL - gs);
-      f32x4 ta[2], tb[2], tc[2], td[2];
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        ta[hs] = zero4();
-        tb[hs] = zero4();
-        tc[hs] = zero4();
-        td[hs] = zero4();
-      }
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s], T[r][s] vanish for r < s
-        const frag_t<E> dpT = pfragT(sb, rkb);
-        const frag_t<E> tT = mfragT(sT, sb, rkb);
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          ta[hs] = mma(qT[hs][rkb], dpT, ta[hs]);
-          tc[hs] = mma(dWir[hs][rkb], tT, tc[hs]);
-        }
-      }
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        const frag_t<E> ee = mfrag(sEE, sb, rkb);
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) td[hs] = mma(kT[hs][rkb], ee, td[hs]);
-      }
-#pragma unroll
-      for (int jkb = 0; jkb < KB; ++jkb) {
-        const frag_t<E> vt = lrec(sVt, sb, jkb);
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) tb[hs] = mma(hpT[hs][jkb], vt, tb[hs]);
-      }
-      // per-s dots with k_s over this wave's i-slice: c_s and k_s . dXw_s
-      const f32x8 kn = frag_to_f32<E>(kf(sb, w));
+      // per-s dots with k_s over this wave's i-block: c_s and k_s . dXw_s
+      const f32x4 kn = my4(frag_to_f32<E>(kf(sb, kw)));
       float dc = 0.f, dx = 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        dc += kn[q] * tb[0][q] + kn[4 + q] * tb[1][q];
-        dx += kn[q] * tc[0][q] + kn[4 + q] * tc[1][q];
+        dc += kn[q] * tb[sb][q];
+        dx += kn[q] * tc[sb][q];
       }
       dc = sum_groups(dc) * ks;   // c_s (partial)
       dx = sum_groups(dx);
       add_col(dgc, sb, -dc + bs * Gs * dx);
       add_col(dbc, sb, Gs * dx);
       csum += (lg == 0) ? dc : 0.f;
+      f32x4 acc;
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        f32x4 acc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = sc * ta[hs][q] + ks * tb[hs][q] + bs * Gs * tc[hs][q] + td[hs][q];
-        if (s_ < L)
-          *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 32 * w + 16 * hs + 4 * lg) = to_quad<E>(acc);
-      }
+      for (int q = 0; q < 4; ++q) acc[q] = sc * ta[sb][q] + ks * tb[sb][q] + bs * Gs * tc[sb][q] + td[sb][q];
+      if (s_ < L) *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
     }
     csum = sum_in_group(csum);
     if (lane == 0) s_misc[2 * w] = csum;
@@ -858,29 +864,28 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_grad(Params p) {
   // dV^T[j][s] = beta_s sum_r dV'[r][j] T[r][s]; dbeta_s += v_s . (T^T dV')_s
   {
     E* dV = reinterpret_cast<E*>(p.dv);
+    f32x4 acc[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        if (32 * rkb + 31 < 16 * sb) continue;
+        acc[sb] = mma(drec[rkb], trec(sTt, sb, rkb), acc[sb]);
+      }
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const int s_ = 16 * sb + li;
       const float bs = s_beta[s_];
-      f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) {
-        if (32 * rkb + 31 < 16 * sb) continue;
-        const frag_t<E> tT = mfragT(sT, sb, rkb);
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) acc[hs] = mma(dvr[hs][rkb], tT, acc[hs]);
-      }
-      const f32x8 vv = frag_to_f32<E>(vw[sb]);
+      const f32x4 vv = my4(frag_to_f32<E>(vw[sb]));
       float dot = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dot += vv[q] * acc[0][q] + vv[4 + q] * acc[1][q];
+      for (int q = 0; q < 4; ++q) dot += vv[q] * acc[sb][q];
       dot = sum_groups(dot);
       add_col(dbc, sb, dot);
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-        if (s_ < L)
-          *reinterpret_cast<quad_t<E>*>(dV + base + (size_t)s_ * rowstride + 32 * w + 16 * hs + 4 * lg) =
-              to_quad<E>(scale4(acc[hs], bs));
+      if (s_ < L)
+        *reinterpret_cast<quad_t<E>*>(dV + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(scale4(acc[sb], bs));
     }
   }
   {
@@ -943,7 +948,7 @@ static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_bwd_grad<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel((const void*)k_bwd_grad<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 16)), args, 0, s);
 }
 
 // fp32 with D = 128 needs more LDS than a workgroup has for the gradient
