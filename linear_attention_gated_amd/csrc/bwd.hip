@@ -770,41 +770,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     }
   }
 
-  // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s]);
-  // the four row blocks run side by side so consecutive MFMAs are independent
+  // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s])
   {
     E* dQ = reinterpret_cast<E*>(p.dq);
-    f32x4 t1[4], aq[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      t1[rb] = zero4();
-      aq[rb] = zero4();
-    }
-#pragma unroll
-    for (int jkb = 0; jkb < KB; ++jkb)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) t1[rb] = mma(hT[jkb], of(rb, jkb), t1[rb]);
-#pragma unroll
-    for (int skb = 0; skb < 2; ++skb)
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        if (32 * skb > 16 * rb + 15) continue;
-        aq[rb] = mma(kT[skb], efrag(sdP, rb, skb), aq[rb]);
-      }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = 16 * rb + li;
+      f32x4 t1 = zero4(), aq = zero4();
+#pragma unroll
+      for (int jkb = 0; jkb < KB; ++jkb) t1 = mma(hT[jkb], of(rb, jkb), t1);
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) {
+        if (32 * skb > 16 * rb + 15) continue;
+        aq = mma(kT[skb], efrag(sdP, rb, skb), aq);
+      }
       // dgamma(r) += Gam_r sum_i (scale Q[r][i]) t1[i][r]
       const f32x4 qn = my4(frag_to_f32<E>(qf(rb, kw)));
       float dot = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dot += qn[q] * t1[rb][q];
+      for (int q = 0; q < 4; ++q) dot += qn[q] * t1[q];
       dot = sum_groups(dot);
       const float Gr = __expf(s_gam[r]);
       add_col(dgc, rb, sc * Gr * dot);
       f32x4 acc;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = sc * (Gr * t1[rb][q] + aq[rb][q]);
+      for (int q = 0; q < 4; ++q) acc[q] = sc * (Gr * t1[q] + aq[q]);
       if (r < L) *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
     }
   }
