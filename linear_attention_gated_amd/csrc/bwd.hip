@@ -289,21 +289,29 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) dv[sb] = mma(cur.kn[sb][kb], hfr[kb], dv[sb]);
-      // exp(gamma_L) H' + Z, off the product's critical path
+      // exp(gamma_L) H' + Z and dV' in the operand type, before the barrier:
+      // the empty asm keeps the compiler from sinking them past it onto the
+      // second product's critical path
       const float GL = __expf(cur.gL);
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL) + quad_to_f32<E>(cur.z[ib]);
+      for (int ib = 0; ib < NJ; ++ib) {
+        hs[ib] = scale4(hs[ib], GL) + quad_to_f32<E>(cur.z[ib]);
+        asm volatile("" : "+v"(hs[ib]));
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      frag_t<E> dvf[2];
+#pragma unroll
+      for (int rkb = 0; rkb < 2; ++rkb) {
+        dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
+        asm volatile("" : "+v"(dvf[rkb]));
+      }
       if (kPipe && t + 1 < nc) {
         // this chunk's reads are complete: release its slot, fetch the next
         wait_lds();
         ring_barrier();
         read_ops(nxt, t + 1);
       }
-      frag_t<E> dvf[2];
-#pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) dvf[rkb] = to_frag<E>(dv[2 * rkb], dv[2 * rkb + 1]);
       // H' <- exp(gamma_L) H' + Z - W^T dV'
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb)
@@ -485,6 +493,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   };
   constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
   constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+  // Owners of the M1 and dA tiles and of the transposed records at 8 waves,
+  // balanced by cost: M1 tiles of a-block <= 1 and dA tiles of b-block >= 2
+  // take two 32-deep fp32 steps, the others one; a record costs about a
+  // third of a one-step tile.  Other wave counts deal round-robin.
+  constexpr int M1_OWN[10] = {0, 1, 2, 3, 4, 5, 6, 7, 3, 4};
+  constexpr int DA_OWN[10] = {3, 3, 4, 4, 5, 2, 5, 6, 0, 1};
+  constexpr int TREC_OWN[12] = {2, 3, 4, 5, 6, 7, 2, 3, 4, 5, 6, 7};
+  auto m1_own = [&](int t) { return NW == 8 ? M1_OWN[t] : t % NW; };
+  auto da_own = [&](int t) { return NW == 8 ? DA_OWN[t] : t % NW; };
+  auto trec_own = [&](int k) { return NW == 8 ? TREC_OWN[k] : NW - 1 - k % NW; };
 
   // ---- setup: decays, staged tiles, and the records the transposes need
   {
@@ -575,11 +593,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
     const int s_ = 16 * sb + li;
     const float gs = s_gam[s_];
+    const f32x4 gr4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * rb + 4 * lg);
     float rs[4], cs = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * rb + 4 * lg + q;
-      const float Dm = s_ <= r ? __expf(s_gam[r] - gs) : 0.f;
+      const float Dm = s_ <= r ? __expf(gr4[q] - gs) : 0.f;
       const float dpd = dp[q] * Dm;
       sdP[r * LDE + s_] = (E)dpd;
       const float mo = dpd * sc * qk[q];
@@ -670,7 +689,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   zero_off_blocks<float, true>(sM1, LDF, tid, NT);   // blocks no tile writes are read as zero later
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
-    if (t % NW != w) continue;
+    if (m1_own(t) != w) continue;
     const int ab = TR[t], sb = TS[t];
     f32x4 acc = zero4();
 #pragma unroll
@@ -686,7 +705,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
-    if (t % NW != w) continue;
+    if (da_own(t) != w) continue;
     const int ab = TR[t], bb = TS[t];
     f32x4 acc = zero4(), kk = zero4();
 #pragma unroll
@@ -699,28 +718,42 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li] and (K K^T)[a][b]
     const int b = 16 * bb + li;
     const float gb = s_gam[b];
+    const f32x4 ga4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * ab + 4 * lg);
+    const f32x4 be4 = *reinterpret_cast<const f32x4*>(s_beta + 16 * ab + 4 * lg);
     float rs_b[4], rs_g[4], cs = 0.f;
+    f32x4 ev;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int a = 16 * ab + 4 * lg + q;
       float da = 0.f, ap = 0.f, Dm = 0.f;
-      if (a > b) {
+      if (ab > bb || a > b) {
         da = -acc[q];
-        Dm = __expf(s_gam[a] - gb);
+        Dm = __expf(ga4[q] - gb);
         ap = kk[q] * Dm;   // A'[a][b]
       }
-      const float ba = s_beta[a];
       rs_b[q] = da * ap;
-      const float ma = da * ba * ap;
+      const float ma = da * be4[q] * ap;
       rs_g[q] = ma;
       cs += ma;
-      // E + E^T: E strictly lower, so the diagonal is zero
-      const E ev = (E)(da * ba * Dm);
-      if (a > b) {
-        sEE[a * LDE + b] = ev;
-        sEE[b * LDE + a] = ev;
-      } else if (a == b) {
-        sEE[a * LDE + a] = (E)0.f;
+      ev[q] = da * be4[q] * Dm;   // E[a][b]; zero on and above the diagonal
+    }
+    // E + E^T into sEE: E[a][b] at (a, b) and at (b, a).  Off the block
+    // diagonal the mirrored values of a lane are four consecutive entries of
+    // row b; in a diagonal block every entry of the block is written once,
+    // by the lane holding it or its mirror.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int a = 16 * ab + 4 * lg + q;
+      if (ab > bb || a > b) sEE[a * LDE + b] = (E)ev[q];
+      else if (a == b) sEE[a * LDE + a] = (E)0.f;
+    }
+    if (ab > bb) {
+      *reinterpret_cast<quad_t<E>*>(sEE + b * LDE + 16 * ab + 4 * lg) = to_quad<E>(ev);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int a = 16 * ab + 4 * lg + q;
+        if (a > b) sEE[b * LDE + a] = (E)ev[q];
       }
     }
 #pragma unroll
@@ -735,7 +768,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
   // transposed records of T and dP*D for the output phase, once per workgroup
   // (sdTt is free after M1; the dP*D records sit above sM1)
-  for (int k = NW - 1 - w; k < 12; k += NW) {
+#pragma unroll
+  for (int k = 0; k < 12; ++k) {
+    if (trec_own(k) != w) continue;
     const int kk = k < 6 ? k : k - 6;
     const int sb = kk < 4 ? kk >> 1 : kk - 2, rkb = kk < 4 ? kk & 1 : 1;
     frag_t<E> x;

@@ -361,21 +361,29 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) vp[rb] = mma(cur.wf[rb][kb], hfr[kb], vp[rb]);
-      // decay of the state, off the product's critical path
+      // decay of the state and V' in the operand type, before the barrier:
+      // the empty asm keeps the compiler from sinking them past it onto the
+      // second product's critical path
       const float GL = __expf(cur.gL);
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) hs[ib] = scale4(hs[ib], GL);
+      for (int ib = 0; ib < NJ; ++ib) {
+        hs[ib] = scale4(hs[ib], GL);
+        asm volatile("" : "+v"(hs[ib]));
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) store_rec<E>(Hf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      frag_t<E> vfr[2];
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) {
+        vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
+        asm volatile("" : "+v"(vfr[skb]));
+      }
       if (kPipe && ci + 1 < nc) {
         // this chunk's reads are complete: release its slot, fetch the next
         wait_lds();
         ring_barrier();
         read_ops(nxt, ci + 1);
       }
-      frag_t<E> vfr[2];
-#pragma unroll
-      for (int skb = 0; skb < 2; ++skb) vfr[skb] = to_frag<E>(vp[2 * skb], vp[2 * skb + 1]);
       // h <- exp(gamma_L) h + Kt^T V'
 #pragma unroll
       for (int skb = 0; skb < 2; ++skb)
