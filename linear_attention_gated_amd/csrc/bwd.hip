@@ -307,16 +307,25 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         asm volatile("" : "+v"(dvf[rkb]));
       }
       if (kPipe && t + 1 < nc) {
-        // this chunk's reads are complete: release its slot, fetch the next
+        // this chunk's reads are complete: release its slot
         wait_lds();
         ring_barrier();
-        read_ops(nxt, t + 1);
       }
+      // fetch the next chunk's operands (the last step reads its own slot
+      // again, unused), interleaved with the second product below
+      if (kPipe) read_ops(nxt, t + 1 < nc ? t + 1 : t);
       // H' <- exp(gamma_L) H' + Z - W^T dV'
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb)
 #pragma unroll
         for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(cur.wt[ib][rkb], dvf[rkb], hs[ib]);
+      if (kPipe) {
+#pragma unroll
+        for (int i = 0; i < 2 * NJ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+      }
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
     };

@@ -379,16 +379,25 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
         asm volatile("" : "+v"(vfr[skb]));
       }
       if (kPipe && ci + 1 < nc) {
-        // this chunk's reads are complete: release its slot, fetch the next
+        // this chunk's reads are complete: release its slot
         wait_lds();
         ring_barrier();
-        read_ops(nxt, ci + 1);
       }
+      // fetch the next chunk's operands (the last step reads its own slot
+      // again, unused), interleaved with the second product below
+      if (kPipe) read_ops(nxt, ci + 1 < nc ? ci + 1 : ci);
       // h <- exp(gamma_L) h + Kt^T V'
 #pragma unroll
       for (int skb = 0; skb < 2; ++skb)
 #pragma unroll
         for (int ib = 0; ib < NJ; ++ib) hs[ib] = mma(cur.kf[ib][skb], vfr[skb], hs[ib]);
+      if (kPipe) {
+#pragma unroll
+        for (int i = 0; i < 2 * NJ; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+      }
 #pragma unroll
       for (int skb = 0; skb < 2; ++skb) store_rec<E>(Vf + ((ch * NJ + jb) * 2 + skb) * REC, lane, vfr[skb]);
     };
