@@ -58,7 +58,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   E* s_dof = reinterpret_cast<E*>(smem + S::oDof);
   E* sPT = reinterpret_cast<E*>(smem + S::oPT);
   float* s_gam = reinterpret_cast<float*>(smem + S::oG);
-  const int ch = blockIdx.x;
+  // units in reverse chunk order: the reverse pass reads the last chunk
+  // first, and it is then the least recently written (the caches keep the
+  // order of use)
+  const int ch = p.NC * p.H - 1 - (int)blockIdx.x;
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
   const int4 ct = chunk_info(p, c);
