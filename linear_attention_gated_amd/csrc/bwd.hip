@@ -27,6 +27,32 @@
 
 namespace gdn {
 
+// Per-wave work lists packed into an integer: item k of wave w is nibble
+// (w * MAXT + k) (15 = none), built from an owner table at compile time, so
+// a wave walks only its own items and the code holds MAXT copies of a body
+// rather than one per item.
+template <int NI, int NWV, int MAXT>
+constexpr unsigned long long pack_owned(const int (&own)[NI]) {
+  unsigned long long r = ~0ull;
+  for (int w = 0; w < NWV; ++w) {
+    int k = 0;
+    for (int t = 0; t < NI; ++t)
+      if (own[t] == w && k < MAXT) {
+        const int sh = 4 * (w * MAXT + k);
+        r = (r & ~(15ull << sh)) | ((unsigned long long)t << sh);
+        ++k;
+      }
+  }
+  return r;
+}
+__device__ __forceinline__ int owned_item(unsigned long long packed, int w, int maxt, int k) {
+  return (int)((packed >> (4 * (w * maxt + k))) & 15ull);
+}
+// Row and column block of the t-th lower 16 x 16 tile of a 64 x 64 matrix
+// (row-major order over the lower triangle including the diagonal).
+__device__ __forceinline__ int tri_row(int t) { return t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0)); }
+__device__ __forceinline__ int tri_col(int t) { const int r = tri_row(t); return t - r * (r + 1) / 2; }
+
 // --------------------------------------------------------------------------
 // K4: per (chunk, head), D/32 waves; wave w owns feature columns [32w, 32w+32).
 // Writes the operands of the reverse pass:
@@ -503,18 +529,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   auto my4 = [&](f32x8 x) {
     return hw ? f32x4{x[4], x[5], x[6], x[7]} : f32x4{x[0], x[1], x[2], x[3]};
   };
-  constexpr int TR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-  constexpr int TS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
   // Owners of the M1 and dA tiles and of the transposed records at 8 waves,
   // balanced by cost: M1 tiles of a-block <= 1 and dA tiles of b-block >= 2
   // take two 32-deep fp32 steps, the others one; a record costs about a
   // third of a one-step tile.  Other wave counts deal round-robin.
-  constexpr int M1_OWN[10] = {0, 1, 2, 3, 4, 5, 6, 7, 3, 4};
-  constexpr int DA_OWN[10] = {3, 3, 4, 4, 5, 2, 5, 6, 0, 1};
-  constexpr int TREC_OWN[12] = {2, 3, 4, 5, 6, 7, 2, 3, 4, 5, 6, 7};
-  auto m1_own = [&](int t) { return NW == 8 ? M1_OWN[t] : t % NW; };
-  auto da_own = [&](int t) { return NW == 8 ? DA_OWN[t] : t % NW; };
-  auto trec_own = [&](int k) { return NW == 8 ? TREC_OWN[k] : NW - 1 - k % NW; };
+  constexpr int M1_OWN8[10] = {0, 1, 2, 3, 4, 5, 6, 7, 3, 4};
+  constexpr int DA_OWN8[10] = {3, 3, 4, 4, 5, 2, 5, 6, 0, 1};
+  constexpr int TREC_OWN8[12] = {2, 3, 4, 5, 6, 7, 2, 3, 4, 5, 6, 7};
+  constexpr int RR4[10] = {0, 1, 2, 3, 0, 1, 2, 3, 0, 1};
+  constexpr int RREC4[12] = {3, 2, 1, 0, 3, 2, 1, 0, 3, 2, 1, 0};
+  constexpr int MAXT = NW == 8 ? 2 : 3;
+  constexpr unsigned long long M1_LIST = NW == 8 ? pack_owned<10, 8, 2>(M1_OWN8) : pack_owned<10, 4, 3>(RR4);
+  constexpr unsigned long long DA_LIST = NW == 8 ? pack_owned<10, 8, 2>(DA_OWN8) : pack_owned<10, 4, 3>(RR4);
+  constexpr unsigned long long TREC_LIST = NW == 8 ? pack_owned<12, 8, 2>(TREC_OWN8) : pack_owned<12, 4, 3>(RREC4);
+  static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
   // ---- setup: decays, staged tiles, and the records the transposes need
   {
@@ -593,9 +621,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // ---- dP = dO V'^T and P (lower tiles, round-robin): sdP = dP * D,
   //      dgamma += rowsum(dP * P) - colsum(dP * P)
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (t % NW != w) continue;
-    const int rb = TR[t], sb = TS[t];
+  for (int k = 0; k < MAXT; ++k) {
+    const int t = w + NW * k;
+    if (t >= 10) break;
+    const int rb = tri_row(t), sb = tri_col(t);
     f32x4 dp = zero4(), qk = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -700,9 +729,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // ---- M1 = T^T dT (fp32): M1[a][s] = sum_r T[r][a] dT[r][s]; tiles s-block <= a-block -> sM1[a][s]
   zero_off_blocks<float, true>(sM1, LDF, tid, NT);   // blocks no tile writes are read as zero later
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (m1_own(t) != w) continue;
-    const int ab = TR[t], sb = TS[t];
+  for (int k = 0; k < MAXT; ++k) {
+    const int t = owned_item(M1_LIST, w, MAXT, k);
+    if (t == 15) break;
+    const int ab = tri_row(t), sb = tri_col(t);
     f32x4 acc = zero4();
 #pragma unroll
     for (int rkb = 0; rkb < 2; ++rkb) {
@@ -716,9 +746,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 
   // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (da_own(t) != w) continue;
-    const int ab = TR[t], bb = TS[t];
+  for (int k = 0; k < MAXT; ++k) {
+    const int t = owned_item(DA_LIST, w, MAXT, k);
+    if (t == 15) break;
+    const int ab = tri_row(t), bb = tri_col(t);
     f32x4 acc = zero4(), kk = zero4();
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb) {
@@ -781,8 +812,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // transposed records of T and dP*D for the output phase, once per workgroup
   // (sdTt is free after M1; the dP*D records sit above sM1)
 #pragma unroll
-  for (int k = 0; k < 12; ++k) {
-    if (trec_own(k) != w) continue;
+  for (int j = 0; j < MAXT; ++j) {
+    const int k = owned_item(TREC_LIST, w, MAXT, j);
+    if (k == 15) break;
     const int kk = k < 6 ? k : k - 6;
     const int sb = kk < 4 ? kk >> 1 : kk - 2, rkb = kk < 4 ? kk & 1 : 1;
     frag_t<E> x;
