@@ -117,3 +117,20 @@ def test_fp32_head_dim_128_backward_rejected():
 def test_full_fwd_bwd(name):
     x = gi.make_inputs(gi.CONFIGS[name], 0)
     compare(x, label=name)
+
+
+def test_full_packed_varlen_fwd_bwd():
+    # the packed workload (32768 tokens in log-uniform sequences, H=16, d=128) with do
+    import dataclasses
+    cfg = dataclasses.replace(gi.CONFIGS["c2"], name="c2_fwdbwd", with_grad=True)
+    x = gi.make_inputs(cfg, 0)
+    assert x["N"] > 1 and x["cu_seqlens"] is not None
+    compare(x, label="c2 packed fwd+bwd")
+
+
+def test_packed_varlen_with_states_and_scale():
+    # packed sequences with initial states, a final-state gradient and scale != 1
+    cfg = small_cfg("bf16", 128, H=3, h0_std=0.05, with_grad=True)
+    x = gi.make_inputs(cfg, 21, lengths=[300, 1, 64, 0, 777, 129, 5])
+    dht = np.random.default_rng(22).standard_normal((x["N"], 3, 128, 128)) * 0.05
+    compare(x, dht=dht, scale=0.3, label="packed h0 dht scale")
