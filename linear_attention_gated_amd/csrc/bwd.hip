@@ -733,12 +733,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const int t = owned_item(M1_LIST, w, MAXT, k);
     if (t == 15) break;
     const int ab = tri_row(t), sb = tri_col(t);
-    f32x4 acc = zero4();
+    // every operand read first, then the products
+    const bool two = ab <= 1;   // T[r][a] = 0 for r < a: the first 32-block only for a-block <= 1
+    f32x8 df[2], tf[2];
 #pragma unroll
     for (int rkb = 0; rkb < 2; ++rkb) {
-      if (32 * rkb + 31 < 16 * ab) continue;   // T[r][a] = 0 for r < a
-      acc = mma(mfrag32(sdTt, sb, rkb), mfragT32(sT, ab, rkb), acc);
+      df[rkb] = (rkb == 1 || two) ? mfrag32(sdTt, sb, rkb) : f32x8{};
+      tf[rkb] = (rkb == 1 || two) ? mfragT32(sT, ab, rkb) : f32x8{};
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = zero4();
+    if (two) acc = mma(df[0], tf[0], acc);
+    acc = mma(df[1], tf[1], acc);
     // lane holds M1[a = 16ab + li][s = 16sb + 4lg + q]
     *reinterpret_cast<f32x4*>(&sM1[(16 * ab + li) * LDF + 16 * sb + 4 * lg]) = acc;
   }
@@ -750,14 +756,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const int t = owned_item(DA_LIST, w, MAXT, k);
     if (t == 15) break;
     const int ab = tri_row(t), bb = tri_col(t);
-    f32x4 acc = zero4(), kk = zero4();
+    // every operand read first, then the products (one LDS latency per tile)
+    f32x8 mf[2], tf[2];
+    frag_t<E> ka[KB], kb_[KB];
+    const bool two = bb >= 2;   // T[b][s] = 0 for s > b: the second 32-block only for b-block >= 2
 #pragma unroll
     for (int skb = 0; skb < 2; ++skb) {
-      if (32 * skb > 16 * bb + 15) continue;   // T[b][s] = 0 for s > b
-      acc = mma(mfrag32(sM1, ab, skb), mfrag32(sT, bb, skb), acc);
+      mf[skb] = (skb == 0 || two) ? mfrag32(sM1, ab, skb) : f32x8{};
+      tf[skb] = (skb == 0 || two) ? mfrag32(sT, bb, skb) : f32x8{};
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kk = mma(kf(ab, kb), kf(bb, kb), kk);
+    for (int kb = 0; kb < KB; ++kb) {
+      ka[kb] = kf(ab, kb);
+      kb_[kb] = kf(bb, kb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = zero4(), kk = zero4();
+    acc = mma(mf[0], tf[0], acc);
+    if (two) acc = mma(mf[1], tf[1], acc);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kk = mma(ka[kb], kb_[kb], kk);
     // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li] and (K K^T)[a][b]
     const int b = 16 * bb + li;
     const float gb = s_gam[b];

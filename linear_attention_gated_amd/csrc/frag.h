@@ -58,10 +58,16 @@ __device__ __forceinline__ constexpr int kslot(int lg, int e) {
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp32: two independent accumulation chains (even and odd k-steps), summed
+// at the end, so consecutive MFMAs do not wait on each other's results
 __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
+  f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
-  return c;
+  for (int e = 0; e < 8; e += 2) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e + 1], b[e + 1], d, 0, 0, 0);
+  }
+  return c + d;
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
