@@ -45,6 +45,7 @@ class Config:
     len_hi: int = 16384
     with_grad: bool = False
     chunk: int = 64
+    qk_normalized: bool = True   # False: raw q, k rows (norms spread over [0.5, 4]) for in-operator normalisation
 
 
 # The five workloads, plus the training-step shape the throughput metric uses.
@@ -129,6 +130,9 @@ def make_inputs(cfg: Config, seed: int = 0, *, T: int | None = None, B: int | No
     dt = cfg.dtype
     q = _l2norm(rng.standard_normal((B, T, H, cfg.dk)))
     k = _l2norm(rng.standard_normal((B, T, H, cfg.dk)))
+    if not cfg.qk_normalized:
+        q = q * rng.uniform(0.5, 4.0, (B, T, H, 1))
+        k = k * rng.uniform(0.5, 4.0, (B, T, H, 1))
     v = rng.standard_normal((B, T, H, cfg.dv))
     g = -_softplus(rng.standard_normal((B, T, H))) * cfg.g_scale
     beta = _sigmoid(rng.standard_normal((B, T, H)))

@@ -81,17 +81,46 @@ def _flat(q, k, v, g, beta, cu_seqlens):
             _f64(beta).reshape(B * T, H))
 
 
+# In-operator L2 normalisation of q and k (optional): each (token, head) row
+# x becomes x / max(||x||_2, L2_EPS).  Where ||x|| > L2_EPS the gradient is
+# dx = (dy - y (y . dy)) / ||x||, the derivative of x / ||x||; below it the
+# map is x / L2_EPS and dx = dy / L2_EPS.
+L2_EPS = 1e-12
+
+
+def l2norm_rows(x):
+    """Rows of x over the last axis divided by max(||row||_2, L2_EPS), in fp64.
+    Returns (y, divisor)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    d = np.maximum(n, L2_EPS)
+    return x / d, d
+
+
+def l2norm_rows_bwd(y, d, dy):
+    """Gradient with respect to x of y = x / max(||x||, L2_EPS), given dy."""
+    dy = np.asarray(dy, dtype=np.float64)
+    proj = np.sum(y * dy, axis=-1, keepdims=True)
+    above = d > L2_EPS
+    return np.where(above, (dy - y * proj) / d, dy / L2_EPS)
+
+
 def threads_used(nseq: int, heads: int, nthreads: int = 0) -> int:
     return int(_load().gdn_oracle_threads(nseq, heads, nthreads))
 
 
-def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, nthreads=0):
+def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, nthreads=0,
+        qk_l2norm=False):
     """Token-by-token forward in fp64.
 
     q, k: [B,T,H,dk]; v: [B,T,H,dv]; g, beta: [B,T,H]; initial_state: [N,H,dk,dv]
-    holding S^T (N = B dense, or len(cu_seqlens)-1).  Returns (o [B,T,H,dv],
-    final_state [N,H,dk,dv]).
+    holding S^T (N = B dense, or len(cu_seqlens)-1).  With ``qk_l2norm`` the
+    recurrence runs on the L2-normalised rows of q and k.  Returns (o
+    [B,T,H,dv], final_state [N,H,dk,dv]).
     """
+    if qk_l2norm:
+        q, _ = l2norm_rows(q)
+        k, _ = l2norm_rows(k)
     lib = _load()
     B, T = q.shape[:2]
     NT, H, dk, dv, cu, q_, k_, v_, g_, b_ = _flat(q, k, v, g, beta, cu_seqlens)
@@ -109,12 +138,19 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0, nthrea
 
 
 def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, scale=1.0,
-        nthreads=0):
+        nthreads=0, qk_l2norm=False):
     """Reverse-mode gradient of L = sum <do, o> + <dht, ht> through the token loop.
 
-    Returns (dq, dk, dv, dg, dbeta, dh0) with the shapes of q, k, v, g, beta and
-    the state.
+    With ``qk_l2norm`` the loop runs on the normalised rows and dq, dk are
+    taken back through the normalisation.  Returns (dq, dk, dv, dg, dbeta,
+    dh0) with the shapes of q, k, v, g, beta and the state.
     """
+    if qk_l2norm:
+        qh, qd = l2norm_rows(q)
+        kh, kd = l2norm_rows(k)
+        dqh, dkh, dv_, dg, db, dh0 = bwd(qh, kh, v, g, beta, do, initial_state, dht, cu_seqlens,
+                                         scale, nthreads)
+        return (l2norm_rows_bwd(qh, qd, dqh), l2norm_rows_bwd(kh, kd, dkh), dv_, dg, db, dh0)
     lib = _load()
     B, T = q.shape[:2]
     NT, H, dk, dv, cu, q_, k_, v_, g_, b_ = _flat(q, k, v, g, beta, cu_seqlens)

@@ -337,3 +337,79 @@ def test_thread_count_does_not_change_results():
     b = oracle.bwd(q, k, v, g, beta, do, s0, nthreads=5)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ------------------------------------------ in-operator L2 normalisation of q, k
+
+def _raw_qk_case(rng, T=21, H=2, dk=5, dv=4):
+    q, k, v, g, beta, s0 = rand_case(rng, T=T, H=H, dk=dk, dv=dv)
+    k = k * rng.uniform(0.3, 3.0, k.shape[:-1] + (1,))   # rand_case's keys are unit rows
+    return q, k, v, g, beta, s0
+
+
+def test_l2norm_forward_is_scale_invariant():
+    """Normalised rows do not depend on a positive rescaling of q or k rows."""
+    rng = np.random.default_rng(61)
+    q, k, v, g, beta, s0 = _raw_qk_case(rng)
+    cq = rng.uniform(0.1, 10.0, q.shape[:-1] + (1,))
+    ck = rng.uniform(0.1, 10.0, k.shape[:-1] + (1,))
+    o1, h1 = oracle.fwd(q, k, v, g, beta, s0, scale=0.8, qk_l2norm=True)
+    o2, h2 = oracle.fwd(q * cq, k * ck, v, g, beta, s0, scale=0.8, qk_l2norm=True)
+    assert rel(o2, o1) < 1e-12 and rel(h2, h1) < 1e-12
+    # and equals the plain recurrence on rows divided by their norms
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o3, h3 = oracle.fwd(qn, kn, v, g, beta, s0, scale=0.8)
+    assert rel(o3, o1) < 1e-12 and rel(h3, h1) < 1e-12
+
+
+def test_l2norm_gradients_orthogonal_and_scaled():
+    """d/dx of f(x/||x||) is orthogonal to x, and scales as 1/c under x -> c x."""
+    rng = np.random.default_rng(62)
+    q, k, v, g, beta, s0 = _raw_qk_case(rng, T=17)
+    do = rng.standard_normal(v.shape)
+    dht = rng.standard_normal(s0.shape)
+    dq, dk, dv, dg, db, dh0 = oracle.bwd(q, k, v, g, beta, do, s0, dht, scale=1.1, qk_l2norm=True)
+    for x, dx in ((q, dq), (k, dk)):
+        dots = np.sum(x * dx, axis=-1)
+        assert np.max(np.abs(dots)) < 1e-10 * np.max(np.linalg.norm(x, axis=-1) * np.linalg.norm(dx, axis=-1))
+    c = 3.5
+    dq2, dk2, dv2, dg2, db2, dh02 = oracle.bwd(q * c, k, v, g, beta, do, s0, dht, scale=1.1, qk_l2norm=True)
+    assert rel(dq2 * c, dq) < 1e-10 and rel(dk2, dk) < 1e-10 and rel(dv2, dv) < 1e-10
+    # the other gradients do not see the normalisation
+    dqh = oracle.bwd(q / np.linalg.norm(q, axis=-1, keepdims=True), k / np.linalg.norm(k, axis=-1, keepdims=True),
+                     v, g, beta, do, s0, dht, scale=1.1)
+    for a, b in zip((dv, dg, db, dh0), dqh[2:]):
+        assert rel(a, b) < 1e-12
+
+
+def test_l2norm_backward_finite_differences():
+    """Central differences of L = <do, o> + <dht, ht> in raw q and k entries."""
+    rng = np.random.default_rng(63)
+    q, k, v, g, beta, s0 = _raw_qk_case(rng, T=9, H=1, dk=4, dv=3)
+    do = rng.standard_normal(v.shape)
+    dht = rng.standard_normal(s0.shape)
+
+    def loss(qq, kk):
+        o, ht = oracle.fwd(qq, kk, v, g, beta, s0, scale=0.6, qk_l2norm=True)
+        return float(np.sum(o * do) + np.sum(ht * dht))
+
+    dq, dk = oracle.bwd(q, k, v, g, beta, do, s0, dht, scale=0.6, qk_l2norm=True)[:2]
+    eps = 1e-6
+    for (which, x, dx) in (("q", q, dq), ("k", k, dk)):
+        for idx in [(0, 0, 0, 0), (0, 3, 0, 2), (0, 8, 0, 3), (0, 5, 0, 1)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num = (loss(xp, k) - loss(xm, k)) / (2 * eps) if which == "q" else (loss(q, xp) - loss(q, xm)) / (2 * eps)
+            assert abs(num - dx[idx]) < 1e-6 * max(1.0, abs(num)), (which, idx, num, dx[idx])
+
+
+def test_l2norm_rows_below_eps():
+    """Rows shorter than the floor are divided by the floor (and differentiated so)."""
+    x = np.zeros((1, 1, 1, 4))
+    x[..., 0] = 1e-13
+    y, d = oracle.l2norm_rows(x)
+    assert d[..., 0] == oracle.L2_EPS and y[..., 0] == 1e-13 / oracle.L2_EPS
+    dy = np.arange(1.0, 5.0).reshape(x.shape)
+    assert np.array_equal(oracle.l2norm_rows_bwd(y, d, dy), dy / oracle.L2_EPS)
