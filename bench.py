@@ -36,6 +36,8 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
     (chunk, head) unit unless noted; state kernels add their per-(sequence,
     head) state I/O."""
     per_unit = {
+        # reads Q, K (2CD E); writes the reciprocal row norms (2C fp32)
+        "norms": 2 * C * D * E + 2 * C * 4,
         # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E), T (C^2 fp32)
         "fwd_prep": 5 * C * D * E + 3 * C * 4 + C * C * 4,
         # reads -W, Kt^T, U (3CD E), gamma_L; writes h (D^2 E), V' (CD E)
@@ -60,6 +62,7 @@ def kernel_flops(D, units):
     """Algorithmic flops per launch (2mnk per product, triangular operands at
     one half, no recompute, no transposes)."""
     per_unit = {
+        "norms": 4 * C * D,
         "fwd_prep": C * C * D + C ** 3 // 3 + 2 * C * C * D,
         "fwd_state": 4 * C * D * D,
         "fwd_out": 2 * C * D * D + 2 * C * C * D,
@@ -103,15 +106,15 @@ def traffic_for(kernel):
     return round(found)
 
 
-def cpu_baseline(x, budget_s=10.0, max_reps=20):
+def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False):
     import oracle
     nthreads = min(16, os.cpu_count() or 1)
     used = oracle.threads_used(x["N"], x["H"], nthreads)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads)
-        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], nthreads=nthreads)
+        oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
+        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], nthreads=nthreads, qk_l2norm=l2)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
@@ -170,6 +173,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--qk-l2norm", action="store_true",
+                    help="raw q/k rows, normalised inside the operator (not the headline workload)")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
@@ -187,6 +192,10 @@ def main():
 
     dev = torch.device("cuda:0")
     cfg = gi.CONFIGS["metric"]
+    l2 = bool(args.qk_l2norm)
+    if l2:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, qk_normalized=False)
     x = gi.make_inputs(cfg, 0)
     B, T, H, D = x["B"], x["T"], x["H"], x["dk"]
 
@@ -195,14 +204,14 @@ def main():
 
     q, k, v, do = (t(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
     g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
-    p = gdn.make_problem(q, v)
+    p = gdn.make_problem(q, v, qk_l2norm=l2)
     L = gdn.lib()
     wsf = torch.empty(L.gdn_fwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
     wsb = torch.empty(L.gdn_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
 
     def step():
-        o, ht, ctx = gdn.fwd(q, k, v, g, beta, return_context=True, workspace=wsf)
-        return gdn.bwd(q, k, v, g, beta, do, context=ctx, need_dh0=False, workspace=wsb)
+        o, ht, ctx = gdn.fwd(q, k, v, g, beta, return_context=True, workspace=wsf, qk_l2norm=l2)
+        return gdn.bwd(q, k, v, g, beta, do, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
 
     for _ in range(args.warmup):
         step()
@@ -220,7 +229,7 @@ def main():
     step_roof = None
     units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
     if not args.no_profile_pass:
-        launches_per_step = 8
+        launches_per_step = 9 if l2 else 8
         n = launches_per_step * args.steps
         evs = HipEvents(2 * n)
         L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)
@@ -268,13 +277,14 @@ def main():
     if args.copy_calib:
         copy_calibration(torch, dev)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(x)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x, l2=l2)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64", "B": B, "T": T, "H": H,
+        "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64" + ("_qkl2norm" if l2 else ""),
+                   "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,
         "sources_sha": sources_sha(),

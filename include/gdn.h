@@ -51,6 +51,12 @@
  * Supported set: d_k = d_v in {64, 128}, chunk = 64, dtype fp32 or bf16,
  * any T >= 0 (a problem with no tokens enqueues only state copies).
  * Anything else returns GDN_ERR_UNSUPPORTED.
+ *
+ * In-operator L2 normalisation (qk_l2norm = 1) is the usual prologue of the
+ * GDN layer (Qwen3.5 normalises q and k per head before the recurrence).
+ * The forward writes the reciprocal row norms into its workspace, next to
+ * the rest of the forward context; gdn_bwd reads them from there (or
+ * recomputes them).
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -62,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -87,6 +93,11 @@ typedef struct {
                                    /* both NULL: dense; both non-NULL: varlen      */
   float scale;     /* o = scale * S q                                             */
   gdn_dtype dtype; /* dtype of q, k, v, o, do, dq, dk, dv                         */
+  int32_t qk_l2norm;  /* 0: q and k are used as given.  1: every (token, head) row */
+                      /* of q and of k is divided by max(||row||_2, 1e-12) inside  */
+                      /* the operator (rounded to the problem dtype), and dq, dk   */
+                      /* are the gradients with respect to the raw rows.           */
+  int32_t reserved;   /* must be 0                                                 */
 } gdn_problem;
 
 /* GDN_ABI_VERSION of the loaded library. */

@@ -36,7 +36,7 @@ class GdnProblem(ctypes.Structure):
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int64),
                 ("num_seqs", ctypes.c_int64), ("cu_seqlens_host", ctypes.c_void_p),
                 ("cu_seqlens_dev", ctypes.c_void_p), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int)]
+                ("dtype", ctypes.c_int), ("qk_l2norm", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -119,7 +119,7 @@ def _cu_pair(cu_seqlens, device):
     return host, dev
 
 
-def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0) -> GdnProblem:
+def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0, qk_l2norm=False) -> GdnProblem:
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     p = GdnProblem()
@@ -129,6 +129,8 @@ def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0) -> GdnP
     p.cu_seqlens_dev = None if cu_dev is None else cu_dev.data_ptr()
     p.scale = float(scale)
     p.dtype = _dtype_code(q.dtype)
+    p.qk_l2norm = 1 if qk_l2norm else 0
+    p.reserved = 0
     return p
 
 
@@ -164,8 +166,9 @@ class Context:
 
 
 def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
-        output_final_state=True, return_context=False, workspace=None):
-    """Forward pass.  Returns (o, ht) or (o, ht, Context)."""
+        output_final_state=True, return_context=False, workspace=None, qk_l2norm=False):
+    """Forward pass.  Returns (o, ht) or (o, ht, Context).  With ``qk_l2norm``
+    the rows of q and k are L2-normalised inside the operator."""
     dev = q.device
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -174,7 +177,7 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
     _require(beta, "beta", torch.float32, dev)
     _require(initial_state, "initial_state", torch.float32, dev)
     cu_h, cu_d = _cu_pair(cu_seqlens, dev)
-    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
     L = lib()
     nbytes = L.gdn_fwd_workspace_bytes(ctypes.byref(p))
     if nbytes == 0:
@@ -191,13 +194,13 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
                      _ptr(initial_state), _ptr(o), _ptr(ht), _ptr(workspace), nbytes, _stream(dev)))
     if return_context:
         key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
-               float(scale))
+               float(scale), bool(qk_l2norm))
         return o, ht, Context(workspace, key)
     return o, ht
 
 
 def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, scale=1.0,
-        context: Context | None = None, need_dh0=True, workspace=None):
+        context: Context | None = None, need_dh0=True, workspace=None, qk_l2norm=False):
     """Backward pass of L = <do, o> + <dht, ht>.  Returns (dq, dk, dv, dg, dbeta, dh0);
     dh0 is None when need_dh0 is False.  With ``context`` from ``fwd(...,
     return_context=True)`` on the same inputs, the forward is not recomputed."""
@@ -210,10 +213,10 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
     _require(initial_state, "initial_state", torch.float32, dev)
     _require(dht, "dht", torch.float32, dev)
     cu_h, cu_d = _cu_pair(cu_seqlens, dev)
-    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
     if context is not None:
         key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
-               float(scale))
+               float(scale), bool(qk_l2norm))
         if key != context.problem_key:
             raise ValueError("context was computed for a different problem")
     L = lib()

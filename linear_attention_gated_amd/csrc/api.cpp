@@ -68,10 +68,11 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   int64_t B = 0, T = 0, H = 0, D = 0, N = 0, NC = 0, tokens = 0;
-  bool varlen = false, bf16 = false;
+  bool varlen = false, bf16 = false, l2norm = false;
   size_t esz = 0;
   // byte offsets into a workspace
   size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0, Tm = 0;
+  size_t qinv = 0, kinv = 0;
   size_t fwd_bytes = 0;
   size_t Z = 0, WnT = 0, Ktn = 0, HPf = 0, dVf = 0, dVl = 0;
   size_t bwd_bytes = 0;
@@ -88,6 +89,9 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   if (p->dk != 64 && p->dk != 128) return fail(GDN_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)p->dk);
   if (p->chunk != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk %lld != 64", (long long)p->chunk);
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "qk_l2norm = %d is not 0 or 1", (int)p->qk_l2norm);
+  if (p->reserved != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved field is %d, not 0", (int)p->reserved);
   if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
   const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
   if (has_h != has_d)
@@ -97,6 +101,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->D = p->dk;
   L->T = p->seqlen;
   L->bf16 = p->dtype == GDN_BF16;
+  L->l2norm = p->qk_l2norm == 1;
   L->esz = L->bf16 ? 2 : 4;
   const int64_t maxtok = (int64_t)1 << 31;
   if (L->varlen) {
@@ -140,6 +145,10 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->Hf = take(e * ch * D * D);
   L->Vf = take(e * ch * 64 * D);
   L->Tm = take(sizeof(float) * ch * 64 * 64);
+  if (L->l2norm) {
+    L->qinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
+    L->kinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
+  }
   L->fwd_bytes = off;
   L->Z = take(e * ch * D * D);
   L->WnT = take(e * ch * 64 * D);
@@ -203,6 +212,10 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Hf = ws + L.Hf;
   P.Vf = ws + L.Vf;
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
+  if (L.l2norm) {
+    P.qinv = reinterpret_cast<float*>(ws + L.qinv);
+    P.kinv = reinterpret_cast<float*>(ws + L.kinv);
+  }
   return P;
 }
 
@@ -297,6 +310,8 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     const int D = (int)L.D;
     hipError_t e;
     if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+    if (L.l2norm)
+      if ((e = timed("norms", s, [&] { return gdn::launch_norms(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "norms launch");
     if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
     if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
@@ -351,6 +366,8 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     hipError_t e;
     if (!fwd_workspace) {
       if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+      if (L.l2norm)
+        if ((e = timed("norms", s, [&] { return gdn::launch_norms(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "norms launch");
       if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
       if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, false, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     }

@@ -106,8 +106,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
   {
     TileStage<E, D, NT> sq, sk, so;
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid);
+    const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, p.qinv ? p.qinv + nb : nullptr, H);
+    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, p.kinv ? p.kinv + nb : nullptr, H);
     so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
     sq.store(tQ, tid);
     sk.store(tK, tid);
@@ -553,8 +554,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       s_beta[lane] = bv;
     }
     TileStage<E, D, NT> sq, sk, so;
-    sq.load(Q + base, rowstride, L, tid);
-    sk.load(K + base, rowstride, L, tid);
+    const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
+    sq.load(Q + base, rowstride, L, tid, p.qinv ? p.qinv + nb : nullptr, H);
+    sk.load(K + base, rowstride, L, tid, p.kinv ? p.kinv + nb : nullptr, H);
     if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
     // T = (I + diag(beta) A')^-1 as the forward solved it
     constexpr int TPER = 64 * 16 / NT;
@@ -850,7 +852,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, 16 * sb + li, kw);
   __syncthreads();
 
-  // ---- per-wave outputs
+  // ---- per-wave outputs.  With in-operator normalisation the gradients just
+  // computed are those of the normalised rows, y = x / ||x||; their per-row
+  // dots y . dy over all D columns are gathered in LDS (the M1 region is
+  // free now) and dx = (dy - y (y . dy)) / ||x|| is written after the next
+  // barrier.
+  const bool norm = p.qinv != nullptr;
+  float* s_qd = sM1;             // [NW][64] partial q . dq
+  float* s_kd = sM1 + NW * 64;   // [NW][64] partial k . dk
+  f32x4 dqh[4], dkh[4];
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
   frag_t<E> kT[2], qT[2];
   {
@@ -892,7 +902,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 acc;
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = sc * (Gr * t1[q] + aq[q]);
-      if (r < L) *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+      if (norm) {
+        float yd = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yd += qn[q] * acc[q];
+        yd = sum_groups(yd);
+        if (lg == 0) s_qd[w * 64 + r] = yd;
+        dqh[rb] = acc;
+      } else if (r < L) {
+        *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+      }
     }
   }
 
@@ -942,7 +961,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 acc;
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = sc * ta[sb][q] + ks * tb[sb][q] + bs * Gs * tc[sb][q] + td[sb][q];
-      if (s_ < L) *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+      if (norm) {
+        float yd = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yd += kn[q] * acc[q];
+        yd = sum_groups(yd);
+        if (lg == 0) s_kd[w * 64 + s_] = yd;
+        dkh[sb] = acc;
+      } else if (s_ < L) {
+        *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+      }
     }
     csum = sum_in_group(csum);
     if (lane == 0) s_misc[2 * w] = csum;
@@ -987,6 +1015,33 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     pb[lane] += dbc;
   }
   __syncthreads();
+
+  if (norm) {
+    // dx = (dy - y (y . dy)) / ||x|| (rows above the floor), dy / floor below it
+    E* dQ = reinterpret_cast<E*>(p.dq);
+    E* dK = reinterpret_cast<E*>(p.dk);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + li;
+      if (r >= L) continue;
+      float yq = 0.f, yk = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        yq += s_qd[ww * 64 + r];
+        yk += s_kd[ww * 64 + r];
+      }
+      const float iq = p.qinv[(size_t)(tok0 + r) * H + h], ik = p.kinv[(size_t)(tok0 + r) * H + h];
+      const f32x4 qn = my4(frag_to_f32<E>(qf(rb, kw))), kn = my4(frag_to_f32<E>(kf(rb, kw)));
+      f32x4 oq, ok;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        oq[q] = iq > 0.f ? (dqh[rb][q] - qn[q] * yq) * iq : -dqh[rb][q] * iq;
+        ok[q] = ik > 0.f ? (dkh[rb][q] - kn[q] * yk) * ik : -dkh[rb][q] * ik;
+      }
+      *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(oq);
+      *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(ok);
+    }
+  }
 
   // ---- dgamma -> dg (reverse chunk-local cumsum), dbeta
   if (w == 0) {

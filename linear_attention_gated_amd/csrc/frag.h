@@ -202,9 +202,36 @@ struct NatTile {
   }
 };
 
+// A 16-byte piece of a row (8 bf16 or 4 fp32 values) times s, rounded back
+// to the element type: the row normalisation every kernel applies alike.
+template <typename E> __device__ __forceinline__ i32x4 scale_piece(i32x4 v, float s);
+template <> __device__ __forceinline__ i32x4 scale_piece<bf16>(i32x4 v, float s) {
+  f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] *= s;
+  return __builtin_bit_cast(i32x4, __builtin_convertvector(f, bf16x8));
+}
+template <> __device__ __forceinline__ i32x4 scale_piece<float>(i32x4 v, float s) {
+  f32x4 f = __builtin_bit_cast(f32x4, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] *= s;
+  return __builtin_bit_cast(i32x4, f);
+}
+// The same for a fragment (8 values of one row).
+template <typename E> __device__ __forceinline__ frag_t<E> scale_frag(frag_t<E> x, float s) {
+  f32x8 f = frag_to_f32<E>(x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] *= s;
+  return f32_to_frag<E>(f);
+}
+// Reciprocal row norms carry the branch of the normalisation in their sign:
+// positive 1 / ||x|| where ||x|| exceeds the floor, -1 / floor below it.
+__device__ __forceinline__ float row_scale(const float* inv, size_t i) { return fabsf(inv[i]); }
+
 // One thread's share of a staged tile, NTHR threads per tile: load() issues
 // every global read of rows [0, L) of X (row r at src + r * rstride
 // elements; rows >= L read as zero), store() writes the swizzled LDS tile.
+// With `rs`, row r is scaled by |rs[r * rsstride]| as it is read.
 // Loading several tiles before storing any keeps all their reads in flight.
 template <typename E, int D, int NTHR>
 struct TileStage {
@@ -213,12 +240,20 @@ struct TileStage {
   static_assert(N % NTHR == 0, "tile pieces must divide over the threads");
   static constexpr int PER = N / NTHR;
   i32x4 v[PER];
-  __device__ __forceinline__ void load(const E* src, size_t rstride, int L, int tid) {
+  __device__ __forceinline__ void load(const E* src, size_t rstride, int L, int tid,
+                                       const float* rs = nullptr, size_t rsstride = 0) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
       v[k] = i32x4{0, 0, 0, 0};
       if (r < L) v[k] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * c);
+    }
+    if (rs) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int q = tid + k * NTHR, r = q / T::NCH;
+        if (r < L) v[k] = scale_piece<E>(v[k], row_scale(rs, (size_t)r * rsstride));
+      }
     }
   }
   __device__ __forceinline__ void store(char* tile, int tid) const {

@@ -80,6 +80,39 @@ __global__ __launch_bounds__(1024) void k_plan(Params p) {
 }
 
 // --------------------------------------------------------------------------
+// K0b: reciprocal L2 norms of the q and k rows (in-operator normalisation):
+// inv = 1 / ||x|| where ||x|| > 1e-12, else -1 / 1e-12 (the sign records the
+// branch for the backward).  One 16-byte piece of a row per thread; the
+// D*sizeof(E)/16 pieces of a row sit in consecutive lanes and are summed by
+// a butterfly, the same order on every run.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_norms(Params p, int rows) {
+  constexpr int LPR = D * (int)sizeof(E) / 16;   // lanes per row
+  constexpr int EPP = 16 / (int)sizeof(E);       // elements per piece
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int which = blockIdx.y;                  // 0: q, 1: k
+  const long long row = gid / LPR;
+  const int piece = (int)(gid - row * LPR);
+  const E* X = reinterpret_cast<const E*>(which ? p.k : p.q);
+  float ss = 0.f;
+  if (row < rows) {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(X + row * D + piece * EPP);
+    const E* e = reinterpret_cast<const E*>(&v);
+#pragma unroll
+    for (int j = 0; j < EPP; ++j) {
+      const float x = (float)e[j];
+      ss += x * x;
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (row < rows && piece == 0) {
+    const float n = sqrtf(ss);
+    (which ? p.kinv : p.qinv)[row] = n > 1e-12f ? 1.f / n : -1.f / 1e-12f;
+  }
+}
+
+// --------------------------------------------------------------------------
 // K1: per (chunk, head): gamma, A, T = (I + A)^-1 (also stored for the
 // backward), and the fragment-native operands of the state pass: -W, Kt^T,
 // U.  D/32 waves; wave w owns feature columns [32w, 32w + 32).
@@ -125,6 +158,11 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
     for (int kb = 0; kb < KB; ++kb)
       kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
                            : zero_frag<E>();
+    if (p.kinv && row < L) {
+      const float ks = row_scale(p.kinv, (size_t)(tok0 + row) * H + h);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[sb][kb] = scale_frag<E>(kf[sb][kb], ks);
+    }
     vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
                       : zero_frag<E>();
   }
@@ -484,8 +522,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
   {
     TileStage<E, D, NT> sq, sk;
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid);
+    const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, p.qinv ? p.qinv + nb : nullptr, H);
+    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, p.kinv ? p.kinv + nb : nullptr, H);
     sq.store(tQ, tid);
     sk.store(tK, tid);
   }
@@ -559,6 +598,16 @@ hipError_t launch_plan(const Params& p, hipStream_t s) {
 }
 
 template <typename E, int D>
+static hipError_t norms_t(const Params& p, hipStream_t s) {
+  const long long rows = (long long)p.total_tokens * p.H;
+  if (rows == 0) return hipSuccess;
+  constexpr int LPR = D * (int)sizeof(E) / 16;
+  Params a = p;
+  int r = (int)rows;
+  void* args[] = {&a, &r};
+  return hipLaunchKernel((const void*)k_norms<E, D>, dim3((unsigned)((rows * LPR + 255) / 256), 2), dim3(256), args, 0, s);
+}
+template <typename E, int D>
 static hipError_t fwd_prep_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
@@ -593,6 +642,7 @@ static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
     return hipErrorInvalidValue;                                     \
   } while (0)
 
+hipError_t launch_norms(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(norms_t, p, s); }
 hipError_t launch_fwd_prep(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(fwd_prep_t, p, s); }
 hipError_t launch_fwd_state(const Params& p, int D, bool is_bf16, bool write_ht, hipStream_t s) {
   GDN_DISPATCH(fwd_state_t, p, write_ht, s);

@@ -18,6 +18,8 @@ constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 //   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
 //   Vf  F(V'; j, s)      [D/16][2]        corrected values
 //   Tm  T[r][s] fp32     64 x 64 row-major  (I + A)^-1, upper blocks zero
+// and, with in-operator normalisation, per (token, head) fp32:
+//   qinv, kinv           1 / max(||row||_2, 1e-12) of the q and k rows
 //   Z   acc Z[i][j]      [D/16 jb][D/16 ib]  backward: (scale Gam Q)^T dO
 //   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
 //   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
@@ -47,6 +49,7 @@ struct Params {
   float* gamma;           // [NC][H][64] chunk-local cumulative log decay
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
   float* Tm;
+  float *qinv, *kinv;     // reciprocal row norms, or nullptr: q and k used as given
   void *WnT, *Ktn, *HPf, *dVf;
   void *Z, *dVl;
 };
@@ -69,6 +72,7 @@ __device__ __forceinline__ int4 seq_info(const Params& p, int n) {
 
 // Launchers (each returns the first launch error, hipSuccess otherwise).
 hipError_t launch_plan(const Params& p, hipStream_t s);
+hipError_t launch_norms(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_fwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_fwd_state(const Params& p, int D, bool bf16, bool write_ht, hipStream_t s);
 hipError_t launch_fwd_out(const Params& p, int D, bool bf16, hipStream_t s);

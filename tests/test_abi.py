@@ -29,14 +29,14 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 1
+    assert gdn.lib().gdn_abi_version() == 2
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
 
 def test_problem_struct_layout():
-    # int64 x7, two pointers, float, enum(int) -> 80 bytes on x86-64
-    assert ctypes.sizeof(gdn.GdnProblem) == 80
+    # int64 x7, two pointers, float, enum(int), two int32 -> 88 bytes on x86-64
+    assert ctypes.sizeof(gdn.GdnProblem) == 88
 
 
 FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation
@@ -90,6 +90,9 @@ def test_workspace_query_valid_and_invalid():
     assert f > 0 and b > f and f % 256 == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(base_problem(dk=96, dv=96))) == 0
     assert L.gdn_fwd_workspace_bytes(None) == 0
+    # in-operator normalisation keeps two reciprocal norms per (token, head) in the forward context
+    fn = L.gdn_fwd_workspace_bytes(ctypes.byref(base_problem(qk_l2norm=1)))
+    assert fn >= f + 2 * 256 * 2 * 4 and fn % 256 == 0
 
 
 CASES = [
@@ -109,6 +112,8 @@ CASES = [
      "256-byte"),
     ("o_aliases_q", {}, dict(o=FAKE), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
     ("ht_aliases_h0", {}, dict(ht="h0"), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("l2norm_2", dict(qk_l2norm=2), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "qk_l2norm"),
+    ("reserved_1", dict(reserved=1), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "reserved"),
 ]
 
 

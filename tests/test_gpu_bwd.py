@@ -14,29 +14,29 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
 
 
-def run_bwd(x, dht=None, scale=1.0, use_context=True):
+def run_bwd(x, dht=None, scale=1.0, use_context=True, l2=False):
     d = dev_inputs(x)
     dht_t = None if dht is None else torch.from_numpy(dht).float().cuda()
     ctx = None
     if use_context:
         _, _, ctx = gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
-                            cu_seqlens=d["cu"], scale=scale, return_context=True)
+                            cu_seqlens=d["cu"], scale=scale, return_context=True, qk_l2norm=l2)
     r = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], initial_state=d["h0"],
-                dht=dht_t, cu_seqlens=d["cu"], scale=scale, context=ctx)
+                dht=dht_t, cu_seqlens=d["cu"], scale=scale, context=ctx, qk_l2norm=l2)
     torch.cuda.synchronize()
     return [to_np(t) for t in r]
 
 
-def ref_bwd(x, dht=None, scale=1.0):
+def ref_bwd(x, dht=None, scale=1.0, l2=False):
     return oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["h0"], dht,
-                      cu_seqlens=x["cu_seqlens"], scale=scale)
+                      cu_seqlens=x["cu_seqlens"], scale=scale, qk_l2norm=l2)
 
 
-def compare(x, dht=None, scale=1.0, label="", use_context=True):
+def compare(x, dht=None, scale=1.0, label="", use_context=True, l2=False):
     say("case", label, "dtype", x["dtype"], "B", x["B"], "T", x["T"], "H", x["H"], "d", x["dk"],
-        "N", x["N"], "context", use_context)
-    got = run_bwd(x, dht, scale, use_context)
-    ref = ref_bwd(x, dht, scale)
+        "N", x["N"], "context", use_context, "qk_l2norm", l2)
+    got = run_bwd(x, dht, scale, use_context, l2)
+    ref = ref_bwd(x, dht, scale, l2)
     tol = TOL[x["dtype"]]
     bad = []
     for name, a, b in zip(NAMES, got, ref):
@@ -134,3 +134,35 @@ def test_packed_varlen_with_states_and_scale():
     x = gi.make_inputs(cfg, 21, lengths=[300, 1, 64, 0, 777, 129, 5])
     dht = np.random.default_rng(22).standard_normal((x["N"], 3, 128, 128)) * 0.05
     compare(x, dht=dht, scale=0.3, label="packed h0 dht scale")
+
+
+
+# in-operator L2 normalisation of q and k, on raw rows
+L2 = [
+    ("fp32", 64, 1, 150, 2, 0.2, True, 0.9),
+    ("bf16", 64, 2, 130, 2, 0.0, False, 1.0),
+    ("bf16", 128, 1, 200, 3, 0.1, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,T,H,h0,with_dht,scale", L2)
+def test_l2norm_small(dtype, d, B, T, H, h0, with_dht, scale):
+    cfg = small_cfg(dtype, d, B=B, T=T, H=H, h0_std=h0, with_grad=True, qk_normalized=False)
+    x = gi.make_inputs(cfg, 41)
+    dht = np.random.default_rng(5).standard_normal((x["N"], H, d, d)) * 0.1 if with_dht else None
+    compare(x, dht=dht, scale=scale, label="l2norm", l2=True)
+
+
+def test_l2norm_varlen_and_recompute():
+    cfg = small_cfg("bf16", 128, H=2, h0_std=0.1, with_grad=True, qk_normalized=False)
+    x = gi.make_inputs(cfg, 42, lengths=[70, 0, 1, 128, 33])
+    a = compare(x, label="l2norm varlen", l2=True)
+    b = run_bwd(x, use_context=False, l2=True)
+    for n, u, v in zip(NAMES, a, b):
+        assert np.array_equal(u, v), n
+
+
+def test_l2norm_metric_shape_fwd_bwd():
+    import dataclasses
+    cfg = dataclasses.replace(gi.CONFIGS["metric"], name="metric_l2", qk_normalized=False)
+    compare(gi.make_inputs(cfg, 0), label="metric shape, raw q/k, in-operator normalisation", l2=True)

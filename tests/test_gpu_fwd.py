@@ -12,24 +12,24 @@ from gpu_util import check, dev_inputs, say, small_cfg, to_np
 pytestmark = pytest.mark.gpu
 
 
-def run_fwd(x, scale=1.0):
+def run_fwd(x, scale=1.0, l2=False):
     d = dev_inputs(x)
     o, ht = gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"],
-                    cu_seqlens=d["cu"], scale=scale)
+                    cu_seqlens=d["cu"], scale=scale, qk_l2norm=l2)
     torch.cuda.synchronize()
     return to_np(o), to_np(ht)
 
 
-def ref_fwd(x, scale=1.0):
+def ref_fwd(x, scale=1.0, l2=False):
     return oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"],
-                      cu_seqlens=x["cu_seqlens"], scale=scale)
+                      cu_seqlens=x["cu_seqlens"], scale=scale, qk_l2norm=l2)
 
 
-def compare(x, scale=1.0, label=""):
+def compare(x, scale=1.0, label="", l2=False):
     say("case", label, "dtype", x["dtype"], "B", x["B"], "T", x["T"], "H", x["H"], "d", x["dk"],
-        "N", x["N"])
-    o, ht = run_fwd(x, scale)
-    ro, rht = ref_fwd(x, scale)
+        "N", x["N"], "qk_l2norm", l2)
+    o, ht = run_fwd(x, scale, l2)
+    ro, rht = ref_fwd(x, scale, l2)
     check("o", o, ro, x["dtype"], "maxrel")
     if x["dtype"] == "fp32":
         check("ht", ht, rht, "fp32", "maxrel")
@@ -99,3 +99,33 @@ def test_bitwise_deterministic():
 def test_full_config(name):
     x = gi.make_inputs(gi.CONFIGS[name], 0)
     compare(x, label=name)
+
+
+# in-operator L2 normalisation of q and k, on raw rows (norms spread over [0.5, 4])
+L2 = [
+    ("fp32", 64, 1, 200, 2, 0.2, 1.0),
+    ("fp32", 128, 1, 130, 2, 0.0, 0.5),
+    ("bf16", 64, 2, 150, 2, 0.0, 1.0),
+    ("bf16", 128, 1, 257, 3, 0.1, 0.8),
+]
+
+
+@pytest.mark.parametrize("dtype,d,B,T,H,h0,scale", L2)
+def test_l2norm_small(dtype, d, B, T, H, h0, scale):
+    cfg = small_cfg(dtype, d, B=B, T=T, H=H, h0_std=h0, qk_normalized=False)
+    compare(gi.make_inputs(cfg, 31), scale=scale, label="l2norm", l2=True)
+
+
+def test_l2norm_varlen():
+    cfg = small_cfg("bf16", 128, H=2, qk_normalized=False)
+    compare(gi.make_inputs(cfg, 32, lengths=[5, 0, 64, 129, 1, 70]), label="l2norm varlen", l2=True)
+
+
+def test_l2norm_is_a_no_op_on_unit_rows():
+    # rows that are already unit length give the plain operator's result up to the rounding
+    # of the rescaled rows
+    cfg = small_cfg("bf16", 128, T=200, H=2)
+    x = gi.make_inputs(cfg, 33)
+    a, _ = run_fwd(x)
+    b, _ = run_fwd(x, l2=True)
+    assert np.max(np.abs(a - b)) <= 2e-2 * np.max(np.abs(a))
