@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256) void k_norms(Params p, int rows) {
 // K1: per (chunk, head): gamma, A, T = (I + A)^-1 (also stored for the
 // backward), and the fragment-native operands of the state pass: -W, Kt^T,
 // U.  D/32 waves; wave w owns feature columns [32w, 32w + 32).
-template <typename E, int D>
+template <typename E, int D, bool NORM>
 __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 4 : 1))) void k_fwd_prep(Params p) {
   constexpr int NW = D / 32;
   constexpr int KB = D / 32;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
     for (int kb = 0; kb < KB; ++kb)
       kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
                            : zero_frag<E>();
-    if (p.kinv && row < L) {
+    if (NORM && row < L) {
       const float ks = row_scale(p.kinv, (size_t)(tok0 + row) * H + h);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) kf[sb][kb] = scale_frag<E>(kf[sb][kb], ks);
@@ -496,7 +496,7 @@ struct FwdOutSmem {
   static constexpr int BYTES = oG + 256;
 };
 
-template <typename E, int D>
+template <typename E, int D, bool NORM>
 __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   using S = FwdOutSmem<E, D>;
   constexpr int NJ = D / 16, KB = D / 32, NW = D / 32, LDE = S::LDE;
@@ -523,8 +523,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   {
     TileStage<E, D, NT> sq, sk;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, p.qinv ? p.qinv + nb : nullptr, H);
-    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, p.kinv ? p.kinv + nb : nullptr, H);
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NORM ? p.qinv + nb : nullptr, H);
+    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
     sq.store(tQ, tid);
     sk.store(tK, tid);
   }
@@ -612,7 +612,7 @@ static hipError_t fwd_prep_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_fwd_prep<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel(p.kinv ? (const void*)k_fwd_prep<E, D, true> : (const void*)k_fwd_prep<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
@@ -627,7 +627,7 @@ static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_fwd_out<E, D>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel(p.qinv ? (const void*)k_fwd_out<E, D, true> : (const void*)k_fwd_out<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 
 #define GDN_DISPATCH(fn, ...)                                        \
