@@ -36,8 +36,6 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
     (chunk, head) unit unless noted; state kernels add their per-(sequence,
     head) state I/O."""
     per_unit = {
-        # reads Q, K (2CD E); writes the reciprocal row norms (2C fp32)
-        "norms": 2 * C * D * E + 2 * C * 4,
         # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E), T (C^2 fp32)
         "fwd_prep": 5 * C * D * E + 3 * C * 4 + C * C * 4,
         # reads -W, Kt^T, U (3CD E), gamma_L; writes h (D^2 E), V' (CD E)
@@ -62,7 +60,6 @@ def kernel_flops(D, units):
     """Algorithmic flops per launch (2mnk per product, triangular operands at
     one half, no recompute, no transposes)."""
     per_unit = {
-        "norms": 4 * C * D,
         "fwd_prep": C * C * D + C ** 3 // 3 + 2 * C * C * D,
         "fwd_state": 4 * C * D * D,
         "fwd_out": 2 * C * D * D + 2 * C * C * D,
@@ -229,7 +226,7 @@ def main():
     step_roof = None
     units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
     if not args.no_profile_pass:
-        launches_per_step = 9 if l2 else 8
+        launches_per_step = 8
         n = launches_per_step * args.steps
         evs = HipEvents(2 * n)
         L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)

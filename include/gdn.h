@@ -54,9 +54,9 @@
  *
  * In-operator L2 normalisation (qk_l2norm = 1) is the usual prologue of the
  * GDN layer (Qwen3.5 normalises q and k per head before the recurrence).
- * The forward writes the reciprocal row norms into its workspace, next to
- * the rest of the forward context; gdn_bwd reads them from there (or
- * recomputes them).
+ * The norms are taken inside the kernels that read the rows; the forward
+ * keeps the reciprocal key norms in its workspace with the rest of the
+ * forward context, and gdn_bwd reads them from there (or recomputes them).
  */
 #ifndef GDN_H_
 #define GDN_H_

@@ -145,10 +145,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->Hf = take(e * ch * D * D);
   L->Vf = take(e * ch * 64 * D);
   L->Tm = take(sizeof(float) * ch * 64 * 64);
-  if (L->l2norm) {
-    L->qinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
-    L->kinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
-  }
+  if (L->l2norm) L->kinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
   L->fwd_bytes = off;
   L->Z = take(e * ch * D * D);
   L->WnT = take(e * ch * 64 * D);
@@ -156,6 +153,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->HPf = take(e * ch * D * D);
   L->dVf = take(e * ch * 64 * D);
   L->dVl = take(e * ch * 64 * D);
+  if (L->l2norm) L->qinv = take(sizeof(float) * (size_t)(L->tokens * L->H));
   L->bwd_bytes = off;
   return GDN_OK;
 }
@@ -212,10 +210,8 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Hf = ws + L.Hf;
   P.Vf = ws + L.Vf;
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
-  if (L.l2norm) {
-    P.qinv = reinterpret_cast<float*>(ws + L.qinv);
-    P.kinv = reinterpret_cast<float*>(ws + L.kinv);
-  }
+  P.qk_l2norm = L.l2norm ? 1 : 0;
+  if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
   return P;
 }
 
@@ -310,8 +306,6 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     const int D = (int)L.D;
     hipError_t e;
     if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
-    if (L.l2norm)
-      if ((e = timed("norms", s, [&] { return gdn::launch_norms(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "norms launch");
     if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
     if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
@@ -362,12 +356,11 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     P.dO = d_o; P.dht = dht; P.dq = dq; P.dk = dk; P.dv = dv; P.dg = dg; P.dbeta = dbeta; P.dh0 = dh0;
     P.Z = ws + L.Z; P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;
     P.HPf = ws + L.HPf; P.dVf = ws + L.dVf; P.dVl = ws + L.dVl;
+    if (L.l2norm) P.qinv = reinterpret_cast<float*>(ws + L.qinv);
     const int D = (int)L.D;
     hipError_t e;
     if (!fwd_workspace) {
       if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
-      if (L.l2norm)
-        if ((e = timed("norms", s, [&] { return gdn::launch_norms(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "norms launch");
       if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
       if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, false, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     }

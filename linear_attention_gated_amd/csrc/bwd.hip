@@ -107,9 +107,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   {
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NORM ? p.qinv + nb : nullptr, H);
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
     sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
     so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
+    // query norms for this pass and the gradient pass (same arithmetic as the forward's)
+    if constexpr (NORM) sq.norm_rows(L, tid, p.qinv + nb, H);
     sq.store(tQ, tid);
     sk.store(tK, tid);
     so.store(tO, tid);
@@ -545,16 +547,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   constexpr unsigned long long TREC_LIST = NW == 8 ? pack_owned<12, 8, 2>(TREC_OWN8) : pack_owned<12, 4, 3>(RREC4);
   static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
-  // reciprocal norms of rows 16 rb + li, read now and used by the epilogue
-  float iqv[4], ikv[4];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int r = 16 * rb + li;
-      iqv[rb] = r < L ? p.qinv[(size_t)(tok0 + r) * H + h] : 0.f;
-      ikv[rb] = r < L ? p.kinv[(size_t)(tok0 + r) * H + h] : 0.f;
-    }
-  }
+  __shared__ float s_inv[NORM ? 128 : 1];   // sign-encoded reciprocal norms of the q, k rows
   // ---- setup: decays, staged tiles, and the records the transposes need
   {
     const float gv = p.gamma[(size_t)ch * 64 + lane];
@@ -578,6 +571,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     }
     sq.store(tQ, tid);
     sk.store(tK, tid);
+    if constexpr (NORM) {
+      sq.store_scales(s_inv, tid);
+      sk.store_scales(s_inv + 64, tid);
+    }
     if constexpr (S::kStageDO) so.store(tO, tid);
 #pragma unroll
     for (int k = 0; k < TPER; ++k) {
@@ -865,12 +862,33 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
   // computed are those of the normalised rows, y = x / ||x||; their per-row
   // dots y . dy over all D columns are gathered in LDS (the M1 region is
-  // free now) and dx = (dy - y (y . dy)) / ||x|| is written after the next
-  // barrier.
+  // free now) and dx = (dy - y (y . dy)) / ||x|| is written after a barrier:
+  // dq's right after its products (its stores overlap the dk work), dk's at
+  // the end.
   constexpr bool norm = NORM;
-  float* s_qd = sM1;             // [NW][64] partial q . dq
-  float* s_kd = sM1 + NW * 64;   // [NW][64] partial k . dk
-  f32x4 dqh[4], dkh[4];
+  float* s_qd = sM1;             // [64][NW] partial q . dq
+  float* s_kd = sM1 + NW * 64;   // [64][NW] partial k . dk
+  f32x4 dqh[4], dkh[4], qn4[4], kn4[4];
+  // dx for rows 16 rb + li of this wave's columns (rows above the floor:
+  // (dy - y (y . dy)) / ||x||; below it: dy / floor)
+  auto norm_out = [&](const f32x4 (&dy)[4], const f32x4 (&yn)[4], const float* part, const float* iv, E* dst) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int r = 16 * rb + li;
+      float yd = 0.f;
+#pragma unroll
+      for (int w4 = 0; w4 < NW; w4 += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(part + r * NW + w4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) yd += a[q];
+      }
+      const float ir = iv[r];
+      f32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = ir > 0.f ? (dy[rb][q] - yn[rb][q] * yd) * ir : -dy[rb][q] * ir;
+      if (r < L) *reinterpret_cast<quad_t<E>*>(dst + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(o);
+    }
+  };
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
   frag_t<E> kT[2], qT[2];
   {
@@ -917,11 +935,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) yd += qn[q] * acc[q];
         yd = sum_groups(yd);
-        if (lg == 0) s_qd[w * 64 + r] = yd;
+        if (lg == 0) s_qd[r * NW + w] = yd;
         dqh[rb] = acc;
+        qn4[rb] = qn;
       } else if (r < L) {
         *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
       }
+    }
+    if constexpr (norm) {
+      __syncthreads();
+      norm_out(dqh, qn4, s_qd, s_inv, dQ);
     }
   }
 
@@ -976,8 +999,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) yd += kn[q] * acc[q];
         yd = sum_groups(yd);
-        if (lg == 0) s_kd[w * 64 + s_] = yd;
+        if (lg == 0) s_kd[s_ * NW + w] = yd;
         dkh[sb] = acc;
+        kn4[sb] = kn;
       } else if (s_ < L) {
         *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
       }
@@ -1026,32 +1050,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
   __syncthreads();
 
-  if constexpr (norm) {
-    // dx = (dy - y (y . dy)) / ||x|| (rows above the floor), dy / floor below it
-    E* dQ = reinterpret_cast<E*>(p.dq);
-    E* dK = reinterpret_cast<E*>(p.dk);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int r = 16 * rb + li;
-      if (r >= L) continue;
-      float yq = 0.f, yk = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        yq += s_qd[ww * 64 + r];
-        yk += s_kd[ww * 64 + r];
-      }
-      const float iq = iqv[rb], ik = ikv[rb];
-      const f32x4 qn = my4(frag_to_f32<E>(qf(rb, kw))), kn = my4(frag_to_f32<E>(kf(rb, kw)));
-      f32x4 oq, ok;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        oq[q] = iq > 0.f ? (dqh[rb][q] - qn[q] * yq) * iq : -dqh[rb][q] * iq;
-        ok[q] = ik > 0.f ? (dkh[rb][q] - kn[q] * yk) * ik : -dkh[rb][q] * ik;
-      }
-      *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(oq);
-      *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(ok);
-    }
-  }
+  if constexpr (norm) norm_out(dkh, kn4, s_kd, s_inv + 64, reinterpret_cast<E*>(p.dk));
 
   // ---- dgamma -> dg (reverse chunk-local cumsum), dbeta
   if (w == 0) {
@@ -1086,7 +1085,7 @@ static hipError_t bwd_prep_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel(p.qinv ? (const void*)k_bwd_prep<E, D, true> : (const void*)k_bwd_prep<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel(p.qk_l2norm ? (const void*)k_bwd_prep<E, D, true> : (const void*)k_bwd_prep<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
@@ -1100,7 +1099,7 @@ static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel(p.qinv ? (const void*)k_bwd_grad<E, D, true> : (const void*)k_bwd_grad<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 16)), args, 0, s);
+  return hipLaunchKernel(p.qk_l2norm ? (const void*)k_bwd_grad<E, D, true> : (const void*)k_bwd_grad<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 16)), args, 0, s);
 }
 
 // fp32 with D = 128 needs more LDS than a workgroup has for the gradient

@@ -217,6 +217,22 @@ template <> __device__ __forceinline__ i32x4 scale_piece<float>(i32x4 v, float s
   for (int e = 0; e < 4; ++e) f[e] *= s;
   return __builtin_bit_cast(i32x4, f);
 }
+// Sum of squares of the values of a 16-byte piece, in element order.
+template <typename E> __device__ __forceinline__ float sum_sq_piece(i32x4 v);
+template <> __device__ __forceinline__ float sum_sq_piece<bf16>(i32x4 v) {
+  const f32x8 f = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += f[e] * f[e];
+  return s;
+}
+template <> __device__ __forceinline__ float sum_sq_piece<float>(i32x4 v) {
+  const f32x4 f = __builtin_bit_cast(f32x4, v);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += f[e] * f[e];
+  return s;
+}
 // The same for a fragment (8 values of one row).
 template <typename E> __device__ __forceinline__ frag_t<E> scale_frag(frag_t<E> x, float s) {
   f32x8 f = frag_to_f32<E>(x);
@@ -225,14 +241,16 @@ template <typename E> __device__ __forceinline__ frag_t<E> scale_frag(frag_t<E> 
   return f32_to_frag<E>(f);
 }
 // Reciprocal row norms carry the branch of the normalisation in their sign:
-// positive 1 / ||x|| where ||x|| exceeds the floor, -1 / floor below it.
-__device__ __forceinline__ float row_scale(const float* inv, size_t i) { return fabsf(inv[i]); }
+// positive 1 / ||x|| where ||x|| exceeds the floor, -1 / floor below it;
+// the row scale is the absolute value.
 
 // One thread's share of a staged tile, NTHR threads per tile: load() issues
 // every global read of rows [0, L) of X (row r at src + r * rstride
 // elements; rows >= L read as zero), store() writes the swizzled LDS tile.
-// With `rs`, row r is scaled by |rs[r * rsstride]| as it is read.
-// Loading several tiles before storing any keeps all their reads in flight.
+// With `rs`, row r is scaled by |rs[r * rsstride]| on its way to LDS (the
+// scale reads are issued with the tile's, rows >= L read row 0's and scale
+// zeros).  Loading several tiles before storing any keeps all their reads
+// in flight; L >= 1.
 template <typename E, int D, int NTHR>
 struct TileStage {
   using T = NatTile<E, D>;
@@ -240,6 +258,8 @@ struct TileStage {
   static_assert(N % NTHR == 0, "tile pieces must divide over the threads");
   static constexpr int PER = N / NTHR;
   i32x4 v[PER];
+  float sc[PER];
+  bool scaled = false;
   __device__ __forceinline__ void load(const E* src, size_t rstride, int L, int tid,
                                        const float* rs = nullptr, size_t rsstride = 0) {
 #pragma unroll
@@ -248,19 +268,49 @@ struct TileStage {
       v[k] = i32x4{0, 0, 0, 0};
       if (r < L) v[k] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * c);
     }
+    scaled = rs != nullptr;
     if (rs) {
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int q = tid + k * NTHR, r = q / T::NCH;
-        if (r < L) v[k] = scale_piece<E>(v[k], row_scale(rs, (size_t)r * rsstride));
+        sc[k] = rs[(size_t)(r < L ? r : 0) * rsstride];   // sign-encoded, as stored
       }
     }
+  }
+  // With row scales: the first lane of each row writes its (sign-encoded)
+  // scale to dst[r], rows >= L included.  No barrier.
+  __device__ __forceinline__ void store_scales(float* dst, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
+      if (c == 0) dst[r] = sc[k];
+    }
+  }
+  // L2-normalise the loaded rows (waits for the reads): each row's pieces
+  // sit in NCH consecutive lanes, whose sums of squares are combined by a
+  // butterfly; the rows are scaled on their way to LDS.  With `inv`, the
+  // first lane of each row r < L writes its sign-encoded reciprocal norm to
+  // inv[r * stride].
+  __device__ __forceinline__ void norm_rows(int L, int tid, float* inv, size_t stride) {
+    static_assert(64 % T::NCH == 0 && NTHR % 64 == 0, "a row's pieces must sit in one wave");
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
+      float ss = sum_sq_piece<E>(v[k]);
+#pragma unroll
+      for (int off = T::NCH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      const float n = sqrtf(ss);
+      const float iv = n > 1e-12f ? 1.f / n : -1.f / 1e-12f;
+      sc[k] = iv;
+      if (inv && c == 0 && r < L) inv[(size_t)r * stride] = iv;
+    }
+    scaled = true;
   }
   __device__ __forceinline__ void store(char* tile, int tid) const {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
-      *reinterpret_cast<i32x4*>(tile + T::off(r, 16 * c)) = v[k];
+      *reinterpret_cast<i32x4*>(tile + T::off(r, 16 * c)) = scaled ? scale_piece<E>(v[k], fabsf(sc[k])) : v[k];
     }
   }
 };

@@ -80,38 +80,6 @@ __global__ __launch_bounds__(1024) void k_plan(Params p) {
 }
 
 // --------------------------------------------------------------------------
-// K0b: reciprocal L2 norms of the q and k rows (in-operator normalisation):
-// inv = 1 / ||x|| where ||x|| > 1e-12, else -1 / 1e-12 (the sign records the
-// branch for the backward).  One 16-byte piece of a row per thread; the
-// D*sizeof(E)/16 pieces of a row sit in consecutive lanes and are summed by
-// a butterfly, the same order on every run.
-template <typename E, int D>
-__global__ __launch_bounds__(256) void k_norms(Params p, int rows) {
-  constexpr int LPR = D * (int)sizeof(E) / 16;   // lanes per row
-  constexpr int EPP = 16 / (int)sizeof(E);       // elements per piece
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int which = blockIdx.y;                  // 0: q, 1: k
-  const long long row = gid / LPR;
-  const int piece = (int)(gid - row * LPR);
-  const E* X = reinterpret_cast<const E*>(which ? p.k : p.q);
-  float ss = 0.f;
-  if (row < rows) {
-    const i32x4 v = *reinterpret_cast<const i32x4*>(X + row * D + piece * EPP);
-    const E* e = reinterpret_cast<const E*>(&v);
-#pragma unroll
-    for (int j = 0; j < EPP; ++j) {
-      const float x = (float)e[j];
-      ss += x * x;
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if (row < rows && piece == 0) {
-    const float n = sqrtf(ss);
-    (which ? p.kinv : p.qinv)[row] = n > 1e-12f ? 1.f / n : -1.f / 1e-12f;
-  }
-}
-
 // --------------------------------------------------------------------------
 // K1: per (chunk, head): gamma, A, T = (I + A)^-1 (also stored for the
 // backward), and the fragment-native operands of the state pass: -W, Kt^T,
@@ -123,7 +91,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   constexpr int LDA = 68;
   __shared__ __attribute__((aligned(16))) float sA[64 * LDA];
   __shared__ __attribute__((aligned(16))) float sT[64 * LDA];
-  __shared__ float s_gam[64], s_beta[64];
+  __shared__ float s_gam[64], s_beta[64], s_ks[64];
 
   const int ch = blockIdx.x;
   const int H = p.H;
@@ -150,6 +118,8 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
 
   // natural key fragments F(K; s, i) for all row blocks, and this wave's
   // value columns (used after the solve; their reads overlap it)
+  // (raw keys: with normalisation the Gram tiles take both rows' reciprocal
+  // norms, and this wave's key columns are scaled once selected)
   frag_t<E> kf[4][KB], vfw[4];
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
@@ -158,13 +128,30 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
     for (int kb = 0; kb < KB; ++kb)
       kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
                            : zero_frag<E>();
-    if (NORM && row < L) {
-      const float ks = row_scale(p.kinv, (size_t)(tok0 + row) * H + h);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[sb][kb] = scale_frag<E>(kf[sb][kb], ks);
-    }
     vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
                       : zero_frag<E>();
+  }
+  if constexpr (NORM) {
+    // sign-encoded reciprocal key norms; every wave holds whole rows, wave 0
+    // publishes them (LDS, and the context for the later passes)
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      float ss = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const f32x8 f = frag_to_f32<E>(kf[sb][kb]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+      }
+      ss = sum_groups(ss);
+      const float n = sqrtf(ss);
+      const float iv = n > 1e-12f ? 1.f / n : -1.f / 1e-12f;
+      const int row = 16 * sb + li;
+      if (w == 0 && lg == 0) {
+        s_ks[row] = fabsf(iv);
+        if (row < L) p.kinv[(size_t)(tok0 + row) * H + h] = iv;
+      }
+    }
   }
   __syncthreads();
 
@@ -181,13 +168,14 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
       for (int kb = 0; kb < KB; ++kb) acc = mma(kf[sc][kb], kf[rr][kb], acc);
       // lane holds G[r = 16rr + li][s = 16sc + 4lg + q]
       const int r = 16 * rr + li;
-      const float gr = s_gam[r], br = s_beta[r];
+      const float gr = s_gam[r], br = NORM ? s_beta[r] * s_ks[r] : s_beta[r];
       float4 out;
       float* po = reinterpret_cast<float*>(&out);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int s = 16 * sc + 4 * lg + q;
-        po[q] = s < r ? br * acc[q] * __expf(gr - s_gam[s]) : 0.f;
+        const float a = br * acc[q] * __expf(gr - s_gam[s]);
+        po[q] = s < r ? (NORM ? a * s_ks[s] : a) : 0.f;
       }
       *reinterpret_cast<float4*>(&sA[r * LDA + 16 * sc + 4 * lg]) = out;
     }
@@ -200,6 +188,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb)
       if (kb == w) kw[sb] = kf[sb][kb];
+    if constexpr (NORM) kw[sb] = scale_frag<E>(kw[sb], s_ks[16 * sb + li]);
   }
   __syncthreads();
 
@@ -523,8 +512,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   {
     TileStage<E, D, NT> sq, sk;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid, NORM ? p.qinv + nb : nullptr, H);
+    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
     sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    if constexpr (NORM) sq.norm_rows(L, tid, nullptr, 0);
     sq.store(tQ, tid);
     sk.store(tK, tid);
   }
@@ -598,21 +588,11 @@ hipError_t launch_plan(const Params& p, hipStream_t s) {
 }
 
 template <typename E, int D>
-static hipError_t norms_t(const Params& p, hipStream_t s) {
-  const long long rows = (long long)p.total_tokens * p.H;
-  if (rows == 0) return hipSuccess;
-  constexpr int LPR = D * (int)sizeof(E) / 16;
-  Params a = p;
-  int r = (int)rows;
-  void* args[] = {&a, &r};
-  return hipLaunchKernel((const void*)k_norms<E, D>, dim3((unsigned)((rows * LPR + 255) / 256), 2), dim3(256), args, 0, s);
-}
-template <typename E, int D>
 static hipError_t fwd_prep_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel(p.kinv ? (const void*)k_fwd_prep<E, D, true> : (const void*)k_fwd_prep<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel(p.qk_l2norm ? (const void*)k_fwd_prep<E, D, true> : (const void*)k_fwd_prep<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
@@ -627,7 +607,7 @@ static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
   if (p.NC == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel(p.qinv ? (const void*)k_fwd_out<E, D, true> : (const void*)k_fwd_out<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
+  return hipLaunchKernel(p.qk_l2norm ? (const void*)k_fwd_out<E, D, true> : (const void*)k_fwd_out<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 32)), args, 0, s);
 }
 
 #define GDN_DISPATCH(fn, ...)                                        \
@@ -642,7 +622,6 @@ static hipError_t fwd_out_t(const Params& p, hipStream_t s) {
     return hipErrorInvalidValue;                                     \
   } while (0)
 
-hipError_t launch_norms(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(norms_t, p, s); }
 hipError_t launch_fwd_prep(const Params& p, int D, bool is_bf16, hipStream_t s) { GDN_DISPATCH(fwd_prep_t, p, s); }
 hipError_t launch_fwd_state(const Params& p, int D, bool is_bf16, bool write_ht, hipStream_t s) {
   GDN_DISPATCH(fwd_state_t, p, write_ht, s);

@@ -18,8 +18,12 @@ constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 //   Hf  F(h; j, i)       [D/16][D/32]     chunk-entry state
 //   Vf  F(V'; j, s)      [D/16][2]        corrected values
 //   Tm  T[r][s] fp32     64 x 64 row-major  (I + A)^-1, upper blocks zero
-// and, with in-operator normalisation, per (token, head) fp32:
-//   qinv, kinv           1 / max(||row||_2, 1e-12) of the q and k rows
+// and, with in-operator normalisation, per (token, head) fp32 (negative:
+// the row's norm is below the floor and the value is -1 / floor):
+//   kinv                 1 / max(||k||_2, 1e-12), written by the WY prep
+//   qinv                 1 / max(||q||_2, 1e-12), backward workspace, written
+//                        by the backward prep (the forward output pass
+//                        computes its own, with the same arithmetic)
 //   Z   acc Z[i][j]      [D/16 jb][D/16 ib]  backward: (scale Gam Q)^T dO
 //   WnT F(-W; i, r)      [D/16][2]        backward: WY factor, transposed
 //   Ktn F(Kt; s, i)      [4][D/32]        backward: decayed keys
@@ -49,7 +53,9 @@ struct Params {
   float* gamma;           // [NC][H][64] chunk-local cumulative log decay
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
   float* Tm;
-  float *qinv, *kinv;     // reciprocal row norms, or nullptr: q and k used as given
+  int qk_l2norm;          // 1: q and k rows L2-normalised inside the operator
+  float* kinv;            // reciprocal key norms [tokens][H] (forward context), sign-encoded
+  float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;
   void *Z, *dVl;
 };
@@ -72,7 +78,6 @@ __device__ __forceinline__ int4 seq_info(const Params& p, int n) {
 
 // Launchers (each returns the first launch error, hipSuccess otherwise).
 hipError_t launch_plan(const Params& p, hipStream_t s);
-hipError_t launch_norms(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_fwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_fwd_state(const Params& p, int D, bool bf16, bool write_ht, hipStream_t s);
 hipError_t launch_fwd_out(const Params& p, int D, bool bf16, hipStream_t s);

@@ -90,9 +90,12 @@ def test_workspace_query_valid_and_invalid():
     assert f > 0 and b > f and f % 256 == 0
     assert L.gdn_fwd_workspace_bytes(ctypes.byref(base_problem(dk=96, dv=96))) == 0
     assert L.gdn_fwd_workspace_bytes(None) == 0
-    # in-operator normalisation keeps two reciprocal norms per (token, head) in the forward context
+    # in-operator normalisation keeps the reciprocal key norms (one fp32 per token and head) in the
+    # forward context and the query norms in the backward's own region
     fn = L.gdn_fwd_workspace_bytes(ctypes.byref(base_problem(qk_l2norm=1)))
-    assert fn >= f + 2 * 256 * 2 * 4 and fn % 256 == 0
+    bn = L.gdn_bwd_workspace_bytes(ctypes.byref(base_problem(qk_l2norm=1)))
+    assert fn >= f + 256 * 2 * 4 and fn % 256 == 0
+    assert bn >= b + 2 * 256 * 2 * 4 and bn % 256 == 0
 
 
 CASES = [
