@@ -166,3 +166,42 @@ def test_l2norm_metric_shape_fwd_bwd():
     import dataclasses
     cfg = dataclasses.replace(gi.CONFIGS["metric"], name="metric_l2", qk_normalized=False)
     compare(gi.make_inputs(cfg, 0), label="metric shape, raw q/k, in-operator normalisation", l2=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128)])
+def test_l2norm_rows_below_the_floor(dtype, d):
+    # rows of q and k that are exactly zero lie below the norm floor: the normalised row is
+    # zero and its gradient is dy / floor.  Those rows' gradients are ~1e12 times the others',
+    # so they are checked on their own and the remaining rows separately.
+    cfg = small_cfg(dtype, d, T=150, H=2, with_grad=True, qk_normalized=False)
+    x = gi.make_inputs(cfg, 43)
+    x["q"] = x["q"].copy()
+    x["k"] = x["k"].copy()
+    zq, zk = [0, 5, 63, 64, 100], [1, 5, 70, 149]
+    x["q"][0, zq, 0] = 0
+    x["k"][0, zk, 1] = 0
+    say("case", "rows below the floor", dtype, "d", d, "zero q rows (head 0)", zq, "zero k rows (head 1)", zk)
+    d_ = dev_inputs(x)
+    o, _ = gdn.fwd(d_["q"], d_["k"], d_["v"], d_["g"], d_["beta"], qk_l2norm=True)
+    ro, _ = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], qk_l2norm=True)
+    o = to_np(o)
+    tol = TOL[dtype]
+    assert np.all(np.isfinite(o)) and maxrel(o, ro) <= tol["maxrel"], maxrel(o, ro)
+    got = run_bwd(x, l2=True)
+    ref = ref_bwd(x, l2=True)
+    masks = {"dq": (zq, 0), "dk": (zk, 1)}
+    for name, a, b in zip(NAMES, got, ref):
+        if b is None:
+            continue
+        assert np.all(np.isfinite(a)), name
+        parts = [(a, b)]
+        if name in masks:
+            rows, h = masks[name]
+            sel = np.zeros(a.shape, bool)
+            sel[0, rows, h] = True
+            assert np.max(np.abs(b[sel])) > 1e6 * np.max(np.abs(b[~sel]))   # the branch was taken
+            parts = [(a[sel], b[sel]), (a[~sel], b[~sel])]
+        for u, v in parts:
+            mr, fr = maxrel(u, v), frob(u, v)
+            say("  %-6s maxrel %.3e  frob %.3e" % (name, mr, fr))
+            assert mr <= tol["maxrel"] and fr <= tol["frob"], (name, mr, fr)
