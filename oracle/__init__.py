@@ -167,3 +167,7 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
         raise MemoryError("oracle backward failed (%d)" % rc)
     return (dq.reshape(B, T, H, dk), dk_.reshape(B, T, H, dk), dv_.reshape(B, T, H, dv),
             dg.reshape(B, T, H), db.reshape(B, T, H), dh0)
+
+
+# Gated RMSNorm on the operator's output (plain NumPy fp64; see gated_norm.py).
+from .gated_norm import gated_rmsnorm_bwd, gated_rmsnorm_fwd  # noqa: E402,F401
