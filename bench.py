@@ -49,6 +49,10 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         # reads Q, K, V, dO, V', dV' (6CD E), h, H' (2 D^2 E), T (C^2 fp32), gamma, beta;
         # writes dQ, dK, dV (3CD E), dg, dbeta
         "bwd_grad": 9 * C * D * E + 2 * D * D * E + C * C * 4 + 4 * C * 4,
+        # gated RMSNorm on the output, per C rows: reads x, z; writes y
+        "gnorm_fwd": 3 * C * D * E,
+        # reads x, z, dy; writes dx, dz (the dw partials are per workgroup, not counted)
+        "gnorm_bwd": 5 * C * D * E,
     }
     out = {k: v * units for k, v in per_unit.items()}
     if with_ht:
@@ -103,15 +107,19 @@ def traffic_for(kernel):
     return round(found)
 
 
-def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False):
+def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None):
     import oracle
     nthreads = min(16, os.cpu_count() or 1)
     used = oracle.threads_used(x["N"], x["H"], nthreads)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
-        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], nthreads=nthreads, qk_l2norm=l2)
+        o, _ = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
+        do = x["do"]
+        if gn is not None:
+            oracle.gated_rmsnorm_fwd(o, gn["z"].reshape(o.shape), gn["w"])
+            do = oracle.gated_rmsnorm_bwd(o, gn["z"].reshape(o.shape), gn["w"], gn["dy"].reshape(o.shape))[0]
+        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, nthreads=nthreads, qk_l2norm=l2)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
@@ -172,6 +180,9 @@ def main():
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--qk-l2norm", action="store_true",
                     help="raw q/k rows, normalised inside the operator (not the headline workload)")
+    ap.add_argument("--gated-norm", action="store_true",
+                    help="the output gate's RMSNorm in the step (forward after the operator, its "
+                         "backward feeding the operator's); not the headline workload")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
@@ -201,14 +212,29 @@ def main():
 
     q, k, v, do = (t(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
     g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
+    gn = None
+    if args.gated_norm:
+        gn = gi.make_gated_norm_inputs(B * T * H, D, "bf16", seed=1, x=np.zeros((B * T * H, D)))
+        zt = t(gn["z"].reshape(B, T, H, D), torch.bfloat16)
+        wt = t(gn["w"], torch.float32)
+        dyt = t(gn["dy"].reshape(B, T, H, D), torch.bfloat16)
+        pn = gdn.make_gated_norm_problem(zt)
     p = gdn.make_problem(q, v, qk_l2norm=l2)
     L = gdn.lib()
     wsf = torch.empty(L.gdn_fwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
     wsb = torch.empty(L.gdn_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
 
+    if gn is not None:
+        wsn = torch.empty(L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(pn)), dtype=torch.uint8,
+                          device=dev)
+
     def step():
         o, ht, ctx = gdn.fwd(q, k, v, g, beta, return_context=True, workspace=wsf, qk_l2norm=l2)
-        return gdn.bwd(q, k, v, g, beta, do, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
+        dO = do
+        if gn is not None:
+            gdn.gated_rmsnorm_fwd(o, zt, wt)
+            dO = gdn.gated_rmsnorm_bwd(o, zt, wt, dyt, workspace=wsn)[0]
+        return gdn.bwd(q, k, v, g, beta, dO, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
 
     for _ in range(args.warmup):
         step()
@@ -226,7 +252,7 @@ def main():
     step_roof = None
     units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
     if not args.no_profile_pass:
-        launches_per_step = 8
+        launches_per_step = 11 if gn is not None else 8
         n = launches_per_step * args.steps
         evs = HipEvents(2 * n)
         L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)
@@ -253,6 +279,7 @@ def main():
             kernels[name] = {"avg_us": round(avg_us, 2), "launches_per_step": num[name] / args.steps}
             if name in kbytes:
                 kernels[name]["achieved_GBps"] = round(kbytes[name] / (avg_us * 1e-6) / 1e9, 1)
+            if name in kflops:
                 kernels[name]["achieved_TFLOPs"] = round(kflops[name] / (avg_us * 1e-6) / 1e12, 2)
         dom = max((k_ for k_ in tot if k_ in kbytes), key=lambda k_: tot[k_])
         a_gbs = kbytes[dom] / (1e-3 * tot[dom] / num[dom]) / 1e9
@@ -274,13 +301,14 @@ def main():
     if args.copy_calib:
         copy_calibration(torch, dev)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(x, l2=l2)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x, l2=l2, gn=gn)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64" + ("_qkl2norm" if l2 else ""),
+        "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64" + ("_qkl2norm" if l2 else "")
+                   + ("_gatednorm" if gn is not None else ""),
                    "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,

@@ -20,6 +20,13 @@ values, so the oracle sees the bits the GPU sees.
 
 Varlen lengths: L = floor(exp(U(ln lo, ln hi))) drawn until the total reaches
 ``total``; the last length is cut to fit (it is never zero).
+
+Gated RMSNorm on the operator's output (``make_gated_norm_inputs``, its own
+stream, draws in the order x, row scales, z, w, dy):
+  x      ~ N(0, 1) rows times U(0.1, 3) per row, unless given (the operator's o)
+  z      ~ N(0, 1.5^2)                           (the gate)
+  w      = 1 + 0.1 N(0, 1), fp32                 (the norm weight, one per column)
+  dy     ~ N(0, 1)                               (upstream gradient)
 """
 from __future__ import annotations
 
@@ -143,3 +150,19 @@ def make_inputs(cfg: Config, seed: int = 0, *, T: int | None = None, B: int | No
                do=None if do is None else round_to(do, dt), cu_seqlens=cu, dtype=dt,
                B=B, T=T, H=H, dk=cfg.dk, dv=cfg.dv, N=N)
     return out
+
+
+def make_gated_norm_inputs(rows: int, dim: int, dtype: str, seed: int = 0, x=None) -> dict:
+    """Inputs of the gated RMSNorm: x, z, dy [rows, dim] in ``dtype``, w [dim] fp32 (recipe
+    in the module docstring).  ``x`` may be given (e.g. the operator's output, already
+    rounded); it is then used as is."""
+    rng = np.random.default_rng(seed)
+    if x is None:
+        x = rng.standard_normal((rows, dim)) * rng.uniform(0.1, 3.0, (rows, 1))
+        x = round_to(x, dtype)
+    else:
+        x = np.asarray(x, dtype=np.float64).reshape(rows, dim)
+    z = round_to(rng.standard_normal((rows, dim)) * 1.5, dtype)
+    w = round_fp32(1.0 + 0.1 * rng.standard_normal(dim))
+    dy = round_to(rng.standard_normal((rows, dim)), dtype)
+    return dict(x=x, z=z, w=w, dy=dy, dtype=dtype, rows=rows, dim=dim)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -142,9 +142,50 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                    float* dh0, const void* fwd_workspace, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* ---- Gated RMSNorm on the operator's output ------------------------------
+ * The output gate of the GDN layer, as the XTuner / Ascend 910C Qwen3.5
+ * training article takes it apart in §2.4 (Fig. 3C: squares, mean, eps,
+ * reciprocal square root, the products with the row and the weight, the
+ * gate's SiLU and its product) and fuses it in §3.1.2 (Fig. 6: one forward
+ * and one backward kernel).  For every row x of `dim` values (one token and
+ * head of the operator's output o), gate row z and weight w[dim]:
+ *     y = x * (mean(x^2) + eps)^(-1/2) * w * z * sigmoid(z)
+ * computed in fp32 and rounded once to the problem dtype.  The backward
+ * returns dx, dz (problem dtype) and dw = the sum over all rows (fp32).
+ *
+ * Layouts: x, z, y, dy, dx, dz are [rows][dim] row-major and contiguous (a
+ * [B][T][H][dv] tensor is rows = B*T*H rows of dim = dv); w and dw are fp32
+ * [dim].  Device pointers, 16-byte aligned; the workspace 256-byte aligned.
+ * Ownership, streams and errors as for gdn_fwd: every buffer is the caller's,
+ * nothing is allocated or synchronised, all work is enqueued on `stream`,
+ * every argument is checked before any HIP call.  Outputs are overwritten
+ * and must not overlap the inputs or each other.  With eps = 0 a zero row
+ * gives NaN (0 * inf), as the formula does.  Supported set: dim in {64, 128},
+ * dtype fp32 or bf16, rows >= 0 (rows = 0: the backward writes dw = 0).
+ * Results are bitwise reproducible for a given problem. */
+typedef struct {
+  int64_t rows;     /* number of rows (tokens x heads), >= 0                    */
+  int64_t dim;      /* values per row                                           */
+  float eps;        /* added to the mean square: finite, >= 0                   */
+  gdn_dtype dtype;  /* dtype of x, z, y, dy, dx, dz                             */
+} gdn_gated_norm_problem;
+
+/* Workspace of gdn_gated_rmsnorm_bwd in bytes (per-workgroup partial sums of
+ * dw, at most 512 KiB); 0 if the problem is invalid or unsupported. */
+size_t gdn_gated_rmsnorm_bwd_workspace_bytes(const gdn_gated_norm_problem* p);
+
+/* Forward: y from x, z and w. */
+gdn_status gdn_gated_rmsnorm_fwd(const gdn_gated_norm_problem* p, const void* x, const void* z,
+                                 const float* w, void* y, void* stream);
+
+/* Backward of L = sum(dy * y): dx, dz and dw (all three written). */
+gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x, const void* z,
+                                 const float* w, const void* dy, void* dx, void* dz, float* dw,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Timing diagnostics ------------------------------------------------
  * gdn_profile_events: bracket each kernel launched by the following
- * gdn_fwd / gdn_bwd calls made on this thread with caller-created HIP events
+ * gdn_fwd / gdn_bwd / gdn_gated_rmsnorm_* calls made on this thread with caller-created HIP events
  * (hipEvent_t passed as void*): events[2i] is recorded on the call's stream
  * just before launch i and events[2i+1] just after it, for the first n_pairs
  * launches; later launches run unbracketed.  Enabling restarts the launch

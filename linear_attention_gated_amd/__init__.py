@@ -7,6 +7,8 @@ no fallback: if the library is missing or fails, these functions raise.
 
     o, ht = fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
     dq, dk, dv, dg, dbeta, dh0 = bwd(q, k, v, g, beta, do, ...)
+    y = gated_rmsnorm_fwd(x, z, w, eps=1e-6)          # the output gate: RMSNorm(x) w silu(z)
+    dx, dz, dw = gated_rmsnorm_bwd(x, z, w, dy, eps=1e-6)
 
 Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g, beta [B,T,H] fp32; states
 [N,H,dk,dv] fp32 holding S^T.  Packed variable-length input: B = 1 and
@@ -28,7 +30,8 @@ GDN_F32, GDN_BF16 = 0, 1
 
 EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_fwd",
             "gdn_bwd", "gdn_status_string", "gdn_last_error_message", "gdn_profile_events",
-            "gdn_profile_count", "gdn_profile_name")
+            "gdn_profile_count", "gdn_profile_name", "gdn_gated_rmsnorm_bwd_workspace_bytes",
+            "gdn_gated_rmsnorm_fwd", "gdn_gated_rmsnorm_bwd")
 
 
 class GdnProblem(ctypes.Structure):
@@ -37,6 +40,11 @@ class GdnProblem(ctypes.Structure):
                 ("num_seqs", ctypes.c_int64), ("cu_seqlens_host", ctypes.c_void_p),
                 ("cu_seqlens_dev", ctypes.c_void_p), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int), ("qk_l2norm", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class GdnGatedNormProblem(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("dim", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -75,6 +83,13 @@ def lib() -> ctypes.CDLL:
         L.gdn_profile_count.restype = ctypes.c_int
         L.gdn_profile_name.argtypes = [ctypes.c_int]
         L.gdn_profile_name.restype = ctypes.c_char_p
+        gprob = ctypes.POINTER(GdnGatedNormProblem)
+        L.gdn_gated_rmsnorm_bwd_workspace_bytes.argtypes = [gprob]
+        L.gdn_gated_rmsnorm_bwd_workspace_bytes.restype = sz
+        L.gdn_gated_rmsnorm_fwd.argtypes = [gprob] + [p] * 4 + [p]
+        L.gdn_gated_rmsnorm_fwd.restype = ctypes.c_int
+        L.gdn_gated_rmsnorm_bwd.argtypes = [gprob] + [p] * 7 + [p, sz, p]
+        L.gdn_gated_rmsnorm_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -239,3 +254,57 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
                      _ptr(dg), _ptr(dbeta), _ptr(dh0), _ptr(fws), _ptr(workspace), nbytes,
                      _stream(dev)))
     return dq, dk_, dv, dg, dbeta, dh0
+
+
+# ---- gated RMSNorm on the operator's output --------------------------------
+
+GATED_NORM_EPS = 1e-6
+
+
+def make_gated_norm_problem(x, eps=GATED_NORM_EPS) -> GdnGatedNormProblem:
+    p = GdnGatedNormProblem()
+    d = x.shape[-1] if x.dim() > 0 else 0
+    p.rows = x.numel() // d if d else 0
+    p.dim = d
+    p.eps = float(eps)
+    p.dtype = _dtype_code(x.dtype)
+    return p
+
+
+def gated_rmsnorm_fwd(x, z, w, eps=GATED_NORM_EPS):
+    """y = x (mean(x^2) + eps)^(-1/2) w silu(z) over the last dim; x, z [..., d] in the
+    problem dtype, w [d] fp32.  Returns y shaped like x."""
+    dev, dt = x.device, x.dtype
+    _require(x, "x", dt, dev)
+    _require(z, "z", dt, dev)
+    _require(w, "w", torch.float32, dev)
+    if z.shape != x.shape or w.shape != (x.shape[-1],):
+        raise ValueError("shapes: x %r, z %r, w %r" % (tuple(x.shape), tuple(z.shape), tuple(w.shape)))
+    p = make_gated_norm_problem(x, eps)
+    y = torch.empty_like(x)
+    _check(lib().gdn_gated_rmsnorm_fwd(ctypes.byref(p), _ptr(x), _ptr(z), _ptr(w), _ptr(y), _stream(dev)))
+    return y
+
+
+def gated_rmsnorm_bwd(x, z, w, dy, eps=GATED_NORM_EPS, workspace=None):
+    """Gradients (dx, dz, dw) of sum(dy * gated_rmsnorm_fwd(x, z, w, eps)); dw is fp32 [d]."""
+    dev, dt = x.device, x.dtype
+    for name, t in (("x", x), ("z", z), ("dy", dy)):
+        _require(t, name, dt, dev)
+    _require(w, "w", torch.float32, dev)
+    if z.shape != x.shape or dy.shape != x.shape or w.shape != (x.shape[-1],):
+        raise ValueError("shapes: x %r, z %r, dy %r, w %r"
+                         % (tuple(x.shape), tuple(z.shape), tuple(dy.shape), tuple(w.shape)))
+    p = make_gated_norm_problem(x, eps)
+    L = lib()
+    nbytes = L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(p))
+    if nbytes == 0:
+        _check(L.gdn_gated_rmsnorm_bwd(ctypes.byref(p), *([None] * 8), 0, None))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dx = torch.empty_like(x)
+    dz = torch.empty_like(z)
+    dw = torch.empty_like(w)
+    _check(L.gdn_gated_rmsnorm_bwd(ctypes.byref(p), _ptr(x), _ptr(z), _ptr(w), _ptr(dy), _ptr(dx),
+                                   _ptr(dz), _ptr(dw), _ptr(workspace), nbytes, _stream(dev)))
+    return dx, dz, dw

@@ -219,6 +219,22 @@ gdn_status hip_fail(hipError_t e, const char* what) {
   return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+gdn_status check_gnorm(const gdn_gated_norm_problem* p) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (p->rows < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "rows < 0");
+  if (p->dim != 64 && p->dim != 128) return fail(GDN_ERR_UNSUPPORTED, "dim %lld not in {64, 128}", (long long)p->dim);
+  if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(GDN_ERR_INVALID_ARGUMENT, "eps is negative or not finite");
+  if (p->rows > ((int64_t)1 << 40) / p->dim) return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  return GDN_OK;
+}
+
+size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
+  const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, p->dtype == GDN_BF16, true);
+  return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)p->dim * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +253,74 @@ const char* gdn_status_string(gdn_status s) {
 }
 
 const char* gdn_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t gdn_gated_rmsnorm_bwd_workspace_bytes(const gdn_gated_norm_problem* p) {
+  try {
+    if (check_gnorm(p) != GDN_OK) return 0;
+    return gnorm_ws_bytes(p);
+  } catch (...) {
+    return 0;
+  }
+}
+
+gdn_status gdn_gated_rmsnorm_fwd(const gdn_gated_norm_problem* p, const void* x, const void* z,
+                                 const float* w, void* y, void* stream) {
+  try {
+    gdn_status st = check_gnorm(p);
+    if (st != GDN_OK) return st;
+    const size_t rb = (size_t)(p->rows * p->dim) * (p->dtype == GDN_BF16 ? 2 : 4);
+    const size_t wb = (size_t)p->dim * sizeof(float);
+    const Range req[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}, {y, rb, "y"}};
+    const Range outs[] = {{y, rb, "y"}};
+    const Range ins[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}};
+    st = check_ptrs(req, 4, nullptr, 0, outs, 1, ins, 3);
+    if (st != GDN_OK) return st;
+    gdn::GnormParams P;
+    std::memset(&P, 0, sizeof(P));
+    P.x = x; P.z = z; P.w = w; P.y = y; P.rows = p->rows; P.eps = p->eps;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed("gnorm_fwd", s, [&] { return gdn::launch_gnorm_fwd(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "gated rmsnorm forward launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_gated_rmsnorm_fwd");
+  }
+}
+
+gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x, const void* z,
+                                 const float* w, const void* dy, void* dx, void* dz, float* dw,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    gdn_status st = check_gnorm(p);
+    if (st != GDN_OK) return st;
+    const size_t rb = (size_t)(p->rows * p->dim) * (p->dtype == GDN_BF16 ? 2 : 4);
+    const size_t wb = (size_t)p->dim * sizeof(float);
+    const size_t need = gnorm_ws_bytes(p);
+    const Range req[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}, {dy, rb, "dy"}, {dx, rb, "dx"},
+                         {dz, rb, "dz"}, {dw, wb, "dw"}, {workspace, need, "workspace"}};
+    const Range outs[] = {{dx, rb, "dx"}, {dz, rb, "dz"}, {dw, wb, "dw"}, {workspace, need, "workspace"}};
+    const Range ins[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}, {dy, rb, "dy"}};
+    st = check_ptrs(req, 8, nullptr, 0, outs, 4, ins, 4);
+    if (st != GDN_OK) return st;
+    if (workspace && ((uintptr_t)workspace) % ALIGN)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    gdn::GnormParams P;
+    std::memset(&P, 0, sizeof(P));
+    P.x = x; P.z = z; P.w = w; P.dy = dy; P.dx = dx; P.dz = dz; P.dw = dw;
+    P.part = reinterpret_cast<float*>(workspace);
+    P.rows = p->rows; P.eps = p->eps;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed("gnorm_bwd", s, [&] { return gdn::launch_gnorm_bwd(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "gated rmsnorm backward launch");
+    e = timed("gnorm_dw", s, [&] { return gdn::launch_gnorm_dw(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    if (e != hipSuccess) return hip_fail(e, "gated rmsnorm weight-gradient launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_gated_rmsnorm_bwd");
+  }
+}
 
 int gdn_profile_events(void* const* events, int n_pairs) {
   if (events && n_pairs > 0) {

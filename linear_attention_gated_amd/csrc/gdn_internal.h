@@ -85,6 +85,27 @@ hipError_t launch_bwd_prep(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_bwd_state(const Params& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_bwd_grad(const Params& p, int D, bool bf16, hipStream_t s);
 
+// Gated RMSNorm on the operator's output (gnorm.hip): rows of D values,
+// row-major and contiguous.
+struct GnormParams {
+  const void *x, *z, *dy;   // [rows][D], problem dtype
+  const float* w;           // [D]
+  void *y, *dx, *dz;        // [rows][D], problem dtype
+  float* dw;                // [D]
+  float* part;              // [D][nblk] per-workgroup partials of dw (workspace)
+  long long rows;
+  float eps;
+  int nblk;                 // set by the launcher
+};
+constexpr int GNORM_MAX_BWD_BLOCKS = 1024;
+// Workgroups of the forward (bwd = false) or backward kernel for `rows` rows.
+int gnorm_blocks(long long rows, int D, bool bf16, bool bwd);
+hipError_t launch_gnorm_fwd(const GnormParams& p, int D, bool bf16, hipStream_t s);
+// backward kernel (dx, dz, per-workgroup dw partials), then the fixed-order
+// sum of the partials
+hipError_t launch_gnorm_bwd(const GnormParams& p, int D, bool bf16, hipStream_t s);
+hipError_t launch_gnorm_dw(const GnormParams& p, int D, bool bf16, hipStream_t s);
+
 // Grid of the sequential kernels: one wave per (sequence, head, 16-column
 // block), padded so that the column blocks of one (sequence, head) share an
 // XCD (workgroup ids are dealt round-robin over the 8 XCDs).

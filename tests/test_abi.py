@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 2
+    assert gdn.lib().gdn_abi_version() == 3
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
@@ -37,6 +37,8 @@ def test_abi_version_and_status_strings():
 def test_problem_struct_layout():
     # int64 x7, two pointers, float, enum(int), two int32 -> 88 bytes on x86-64
     assert ctypes.sizeof(gdn.GdnProblem) == 88
+    # int64 x2, float, enum(int) -> 24 bytes
+    assert ctypes.sizeof(gdn.GdnGatedNormProblem) == 24
 
 
 FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation
@@ -175,3 +177,72 @@ def test_bwd_rejects_missing_outputs():
     st = gdn.lib().gdn_bwd(ctypes.byref(p), *args, P(FAKE + (1 << 36)),
                            gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(p)), None)
     assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "dg is NULL" in gdn.last_error_message()
+
+
+# ---- gated RMSNorm entry points ---------------------------------------------
+
+def gnorm_problem(**kw):
+    p = gdn.GdnGatedNormProblem()
+    p.rows, p.dim, p.eps, p.dtype = 300, 128, 1e-6, gdn.GDN_BF16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def call_gnorm_bwd(p, **over):
+    L = gdn.lib()
+    ptrs = dict(x=FAKE, z=FAKE + (1 << 30), w=FAKE + (2 << 30), dy=FAKE + (3 << 30), dx=FAKE + (4 << 30),
+                dz=FAKE + (5 << 30), dw=FAKE + (6 << 30), ws=FAKE + (7 << 30))
+    ptrs.update(over)
+    need = L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(p))
+    nb = over.get("ws_bytes", need)
+    P = ctypes.c_void_p
+    st = L.gdn_gated_rmsnorm_bwd(ctypes.byref(p), *(P(ptrs[n]) if ptrs[n] else None for n in
+                                                    ("x", "z", "w", "dy", "dx", "dz", "dw", "ws")),
+                                 nb, None)
+    return st, gdn.last_error_message()
+
+
+GNORM_CASES = [
+    ("dim_96", dict(dim=96), {}, gdn.GDN_ERR_UNSUPPORTED, "dim"),
+    ("dtype_5", dict(dtype=5), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "dtype"),
+    ("rows_neg", dict(rows=-1), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "rows"),
+    ("eps_neg", dict(eps=-1e-6), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "eps"),
+    ("eps_inf", dict(eps=float("inf")), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "eps"),
+    ("null_w", {}, dict(w=0), gdn.GDN_ERR_INVALID_ARGUMENT, "w is NULL"),
+    ("null_dw", {}, dict(dw=0), gdn.GDN_ERR_INVALID_ARGUMENT, "dw is NULL"),
+    ("misaligned_dy", {}, dict(dy=FAKE + (3 << 30) + 4), gdn.GDN_ERR_INVALID_ARGUMENT, "aligned"),
+    ("dx_aliases_x", {}, dict(dx=FAKE + 256), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("dz_aliases_dx", {}, dict(dz=FAKE + (4 << 30) + 512), gdn.GDN_ERR_INVALID_ARGUMENT, "overlap"),
+    ("ws_misaligned", {}, dict(ws=FAKE + (7 << 30) + 16), gdn.GDN_ERR_INVALID_ARGUMENT, "256-byte"),
+    ("ws_small", {}, dict(ws_bytes=256), gdn.GDN_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+]
+
+
+@pytest.mark.parametrize("name,pkw,pover,status,msg", GNORM_CASES, ids=[c[0] for c in GNORM_CASES])
+def test_gated_norm_invalid_arguments(name, pkw, pover, status, msg):
+    st, m = call_gnorm_bwd(gnorm_problem(**pkw), **pover)
+    assert st == status, (st, m)
+    assert msg in m, m
+
+
+def test_gated_norm_forward_validation():
+    L = gdn.lib()
+    P = ctypes.c_void_p
+    p = gnorm_problem()
+    st = L.gdn_gated_rmsnorm_fwd(ctypes.byref(p), P(FAKE), P(FAKE + (1 << 30)), None, P(FAKE + (2 << 30)), None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "w is NULL" in gdn.last_error_message()
+    st = L.gdn_gated_rmsnorm_fwd(ctypes.byref(p), P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (3 << 30)),
+                                 P(FAKE + 64), None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps" in gdn.last_error_message()
+    st = L.gdn_gated_rmsnorm_fwd(None, None, None, None, None, None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT
+
+
+def test_gated_norm_workspace_size():
+    L = gdn.lib()
+    # one fp32 partial row of dw per backward workgroup, at most 1024 of them
+    big = L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(gnorm_problem(rows=1 << 20)))
+    assert big == 1024 * 128 * 4
+    assert L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(gnorm_problem(rows=0))) == 512
+    assert L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(gnorm_problem(dim=96))) == 0
