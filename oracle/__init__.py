@@ -171,3 +171,5 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
 
 # Gated RMSNorm on the operator's output (plain NumPy fp64; see gated_norm.py).
 from .gated_norm import gated_rmsnorm_bwd, gated_rmsnorm_fwd  # noqa: E402,F401
+# Causal depthwise conv1d over packed sequences (plain NumPy fp64; see conv1d.py).
+from .conv1d import causal_conv1d_bwd, causal_conv1d_fwd  # noqa: E402,F401
