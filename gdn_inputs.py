@@ -27,6 +27,13 @@ stream, draws in the order x, row scales, z, w, dy):
   z      ~ N(0, 1.5^2)                           (the gate)
   w      = 1 + 0.1 N(0, 1), fp32                 (the norm weight, one per column)
   dy     ~ N(0, 1)                               (upstream gradient)
+
+Causal conv1d (``make_conv_inputs``, its own stream, draws in the order
+lengths, x, w, bias, dy), x channels last [B, T, C]:
+  x      ~ N(0, 1)                               (the q/k/v projections)
+  w      ~ U(-1/sqrt(K), 1/sqrt(K)), fp32 [C, K]  (a depthwise conv's default init range)
+  bias   ~ U(-1/sqrt(K), 1/sqrt(K)), fp32 [C]
+  dy     ~ N(0, 1)
 """
 from __future__ import annotations
 
@@ -166,3 +173,23 @@ def make_gated_norm_inputs(rows: int, dim: int, dtype: str, seed: int = 0, x=Non
     w = round_fp32(1.0 + 0.1 * rng.standard_normal(dim))
     dy = round_to(rng.standard_normal((rows, dim)), dtype)
     return dict(x=x, z=z, w=w, dy=dy, dtype=dtype, rows=rows, dim=dim)
+
+
+def make_conv_inputs(B: int, T: int, C: int, K: int, dtype: str, seed: int = 0, *,
+                     varlen_total: int | None = None, lengths=None, len_lo: int = 128,
+                     len_hi: int = 16384) -> dict:
+    """Inputs of the causal conv1d (recipe in the module docstring).  Packed input: give
+    ``lengths`` or ``varlen_total`` (log-uniform lengths); B is then 1."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if lengths is not None or varlen_total is not None:
+        if lengths is None:
+            lengths = varlen_lengths(rng, varlen_total, len_lo, len_hi)
+        B, T = 1, int(sum(lengths))
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = round_to(rng.standard_normal((B, T, C)), dtype)
+    bound = 1.0 / math.sqrt(K)
+    w = round_fp32(rng.uniform(-bound, bound, (C, K)))
+    bias = round_fp32(rng.uniform(-bound, bound, C))
+    dy = round_to(rng.standard_normal((B, T, C)), dtype)
+    return dict(x=x, w=w, bias=bias, dy=dy, cu_seqlens=cu, dtype=dtype, B=B, T=T, C=C, K=K)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
   GDN_OK = 0,
@@ -183,9 +183,54 @@ gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x,
                                  const float* w, const void* dy, void* dx, void* dz, float* dw,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Causal depthwise conv1d over packed sequences -----------------------
+ * The GDN layer's short causal convolution, which the XTuner / Ascend 910C
+ * Qwen3.5 training article (§3.1.2, Fig. 8) moves from a loop of slices and
+ * pads per sequence into one native forward and one backward kernel.  For
+ * channel c, kernel size K and token t of a sequence whose first token is t0:
+ *     pre = bias[c] + sum_{j<K} w[c][j] * x[t - (K-1) + j][c]  (x = 0 before t0)
+ *     y   = pre * sigmoid(pre) with the activation, pre without it
+ * in fp32, rounded once.  Nothing crosses a sequence start.  The backward
+ * returns dx (same sequence only), dw = sum_t dpre[t] x[t - (K-1) + j] and,
+ * if dbias != NULL, dbias = sum_t dpre[t] (fp32, over all tokens).
+ *
+ * Layouts: x, y, dy, dx are [B*T][channels] row-major (channels last; for
+ * packed input B = 1 and cu_seqlens as in gdn_problem); w is fp32
+ * [channels][K] (a depthwise conv1d weight [C][1][K]); bias and dbias are fp32
+ * [channels] or NULL.  Device pointers 16-byte aligned, the workspace 256-byte
+ * aligned.  Ownership, streams, errors and non-overlap of outputs as for
+ * gdn_fwd.  Supported set: K in [1, 4], channels a positive multiple of 4,
+ * dtype fp32 or bf16, any T >= 0.  Results are bitwise reproducible. */
+typedef struct {
+  int64_t batch;       /* B; must be 1 when cu_seqlens are given                     */
+  int64_t seqlen;      /* T: tokens per batch row, or total packed tokens            */
+  int64_t channels;    /* C                                                          */
+  int64_t kernel_size; /* K                                                          */
+  int64_t num_seqs;                /* N when packed; ignored when dense              */
+  const int32_t* cu_seqlens_host;  /* [N+1] host copy (validation), or NULL          */
+  const int32_t* cu_seqlens_dev;   /* [N+1] device copy read by the kernels, or NULL */
+  int32_t activation;  /* 0: none, 1: SiLU                                           */
+  gdn_dtype dtype;     /* dtype of x, y, dy, dx                                      */
+} gdn_conv_problem;
+
+/* Workspace of gdn_causal_conv1d_bwd in bytes (per-grid-row partial sums of
+ * dw and dbias: at most 64 * channels * (K+1) fp32); 0 if the problem is
+ * invalid or unsupported. */
+size_t gdn_causal_conv1d_bwd_workspace_bytes(const gdn_conv_problem* p);
+
+/* Forward: y from x, w and bias (NULL: no bias). */
+gdn_status gdn_causal_conv1d_fwd(const gdn_conv_problem* p, const void* x, const float* w,
+                                 const float* bias, void* y, void* stream);
+
+/* Backward of L = sum(dy * y): dx, dw and (if dbias != NULL) dbias. */
+gdn_status gdn_causal_conv1d_bwd(const gdn_conv_problem* p, const void* x, const float* w,
+                                 const float* bias, const void* dy, void* dx, float* dw,
+                                 float* dbias, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ---- Timing diagnostics ------------------------------------------------
  * gdn_profile_events: bracket each kernel launched by the following
- * gdn_fwd / gdn_bwd / gdn_gated_rmsnorm_* calls made on this thread with caller-created HIP events
+ * gdn_fwd / gdn_bwd / gdn_gated_rmsnorm_* / gdn_causal_conv1d_* calls made on this thread with caller-created HIP events
  * (hipEvent_t passed as void*): events[2i] is recorded on the call's stream
  * just before launch i and events[2i+1] just after it, for the first n_pairs
  * launches; later launches run unbracketed.  Enabling restarts the launch

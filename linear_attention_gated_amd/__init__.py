@@ -9,6 +9,8 @@ no fallback: if the library is missing or fails, these functions raise.
     dq, dk, dv, dg, dbeta, dh0 = bwd(q, k, v, g, beta, do, ...)
     y = gated_rmsnorm_fwd(x, z, w, eps=1e-6)          # the output gate: RMSNorm(x) w silu(z)
     dx, dz, dw = gated_rmsnorm_bwd(x, z, w, dy, eps=1e-6)
+    y = causal_conv1d_fwd(x, w, bias=None, cu_seqlens=None, activation=True)   # x [B,T,C], w [C,K]
+    dx, dw, dbias = causal_conv1d_bwd(x, w, dy, bias=None, cu_seqlens=None, activation=True)
 
 Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; g, beta [B,T,H] fp32; states
 [N,H,dk,dv] fp32 holding S^T.  Packed variable-length input: B = 1 and
@@ -31,7 +33,8 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_fwd",
             "gdn_bwd", "gdn_status_string", "gdn_last_error_message", "gdn_profile_events",
             "gdn_profile_count", "gdn_profile_name", "gdn_gated_rmsnorm_bwd_workspace_bytes",
-            "gdn_gated_rmsnorm_fwd", "gdn_gated_rmsnorm_bwd")
+            "gdn_gated_rmsnorm_fwd", "gdn_gated_rmsnorm_bwd", "gdn_causal_conv1d_bwd_workspace_bytes",
+            "gdn_causal_conv1d_fwd", "gdn_causal_conv1d_bwd")
 
 
 class GdnProblem(ctypes.Structure):
@@ -45,6 +48,13 @@ class GdnProblem(ctypes.Structure):
 class GdnGatedNormProblem(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("dim", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("dtype", ctypes.c_int)]
+
+
+class GdnConvProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("kernel_size", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
+                ("cu_seqlens_host", ctypes.c_void_p), ("cu_seqlens_dev", ctypes.c_void_p),
+                ("activation", ctypes.c_int32), ("dtype", ctypes.c_int)]
 
 
 class GdnError(RuntimeError):
@@ -90,6 +100,13 @@ def lib() -> ctypes.CDLL:
         L.gdn_gated_rmsnorm_fwd.restype = ctypes.c_int
         L.gdn_gated_rmsnorm_bwd.argtypes = [gprob] + [p] * 7 + [p, sz, p]
         L.gdn_gated_rmsnorm_bwd.restype = ctypes.c_int
+        cprob = ctypes.POINTER(GdnConvProblem)
+        L.gdn_causal_conv1d_bwd_workspace_bytes.argtypes = [cprob]
+        L.gdn_causal_conv1d_bwd_workspace_bytes.restype = sz
+        L.gdn_causal_conv1d_fwd.argtypes = [cprob] + [p] * 4 + [p]
+        L.gdn_causal_conv1d_fwd.restype = ctypes.c_int
+        L.gdn_causal_conv1d_bwd.argtypes = [cprob] + [p] * 7 + [p, sz, p]
+        L.gdn_causal_conv1d_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -308,3 +325,63 @@ def gated_rmsnorm_bwd(x, z, w, dy, eps=GATED_NORM_EPS, workspace=None):
     _check(L.gdn_gated_rmsnorm_bwd(ctypes.byref(p), _ptr(x), _ptr(z), _ptr(w), _ptr(dy), _ptr(dx),
                                    _ptr(dz), _ptr(dw), _ptr(workspace), nbytes, _stream(dev)))
     return dx, dz, dw
+
+
+# ---- causal depthwise conv1d over packed sequences -------------------------
+
+def make_conv_problem(x, K, cu_host=None, cu_dev=None, activation=True) -> GdnConvProblem:
+    B, T, C = x.shape
+    p = GdnConvProblem()
+    p.batch, p.seqlen, p.channels, p.kernel_size = B, T, C, K
+    p.num_seqs = 0 if cu_host is None else cu_host.numel() - 1
+    p.cu_seqlens_host = None if cu_host is None else cu_host.data_ptr()
+    p.cu_seqlens_dev = None if cu_dev is None else cu_dev.data_ptr()
+    p.activation = 1 if activation else 0
+    p.dtype = _dtype_code(x.dtype)
+    return p
+
+
+def _conv_args(x, w, bias, cu_seqlens):
+    dev, dt = x.device, x.dtype
+    _require(x, "x", dt, dev)
+    _require(w, "w", torch.float32, dev)
+    _require(bias, "bias", torch.float32, dev)
+    if x.dim() != 3 or w.dim() != 2 or w.shape[0] != x.shape[2] or (
+            bias is not None and bias.shape != (x.shape[2],)):
+        raise ValueError("shapes: x %r (need [B,T,C]), w %r (need [C,K]), bias %r"
+                         % (tuple(x.shape), tuple(w.shape), None if bias is None else tuple(bias.shape)))
+    return _cu_pair(cu_seqlens, dev)
+
+
+def causal_conv1d_fwd(x, w, bias=None, cu_seqlens=None, activation=True):
+    """y[t, c] = act(bias[c] + sum_j w[c, j] x[t - (K-1) + j, c]) within each sequence;
+    x [B, T, C] channels last (B = 1 with cu_seqlens), w [C, K] and bias [C] fp32."""
+    cu_h, cu_d = _conv_args(x, w, bias, cu_seqlens)
+    p = make_conv_problem(x, w.shape[1], cu_h, cu_d, activation)
+    y = torch.empty_like(x)
+    _check(lib().gdn_causal_conv1d_fwd(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
+                                       _stream(x.device)))
+    return y
+
+
+def causal_conv1d_bwd(x, w, dy, bias=None, cu_seqlens=None, activation=True, need_dbias=True,
+                      workspace=None):
+    """Gradients (dx, dw, dbias) of sum(dy * causal_conv1d_fwd(...)); dbias is None when
+    need_dbias is False."""
+    cu_h, cu_d = _conv_args(x, w, bias, cu_seqlens)
+    _require(dy, "dy", x.dtype, x.device)
+    if dy.shape != x.shape:
+        raise ValueError("dy %r != x %r" % (tuple(dy.shape), tuple(x.shape)))
+    p = make_conv_problem(x, w.shape[1], cu_h, cu_d, activation)
+    L = lib()
+    nbytes = L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(p))
+    if nbytes == 0:
+        _check(L.gdn_causal_conv1d_bwd(ctypes.byref(p), *([None] * 8), 0, None))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    db = torch.empty(x.shape[2], dtype=torch.float32, device=x.device) if need_dbias else None
+    _check(L.gdn_causal_conv1d_bwd(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(bias), _ptr(dy), _ptr(dx),
+                                   _ptr(dw), _ptr(db), _ptr(workspace), nbytes, _stream(x.device)))
+    return dx, dw, db

@@ -230,6 +230,69 @@ gdn_status check_gnorm(const gdn_gated_norm_problem* p) {
   return GDN_OK;
 }
 
+struct ConvPlan {
+  int64_t tokens = 0, N = 0, T = 0;
+  bool varlen = false, bf16 = false;
+};
+
+gdn_status check_conv(const gdn_conv_problem* p, ConvPlan* P) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (p->kernel_size < 1 || p->kernel_size > 4)
+    return fail(GDN_ERR_UNSUPPORTED, "kernel_size %lld not in [1, 4]", (long long)p->kernel_size);
+  if (p->channels < 1 || p->channels % 4)
+    return fail(GDN_ERR_UNSUPPORTED, "channels %lld is not a positive multiple of 4", (long long)p->channels);
+  if (p->activation != 0 && p->activation != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "activation = %d is not 0 or 1", (int)p->activation);
+  if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
+  const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
+  if (has_h != has_d)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
+  P->varlen = has_h;
+  P->bf16 = p->dtype == GDN_BF16;
+  P->T = p->seqlen;
+  if (P->varlen) {
+    if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
+    if (p->num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs = %lld < 1", (long long)p->num_seqs);
+    if (((uintptr_t)p->cu_seqlens_dev) % 4) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_dev misaligned");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d != 0", cu[0]);
+    for (int64_t n = 0; n < p->num_seqs; ++n)
+      if (cu[n + 1] < cu[n])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %lld (%d -> %d)", (long long)n, cu[n], cu[n + 1]);
+    if (cu[p->num_seqs] != p->seqlen)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d != seqlen %lld", cu[p->num_seqs], (long long)p->seqlen);
+    P->N = p->num_seqs;
+  } else {
+    if (p->batch < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "batch = %lld < 1", (long long)p->batch);
+    P->N = p->batch;
+  }
+  P->tokens = (P->varlen ? 1 : p->batch) * p->seqlen;
+  if (P->tokens >= ((int64_t)1 << 31) || P->N >= ((int64_t)1 << 31) ||
+      P->tokens * p->channels >= ((int64_t)1 << 40))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  return GDN_OK;
+}
+
+size_t conv_ws_bytes(const gdn_conv_problem* p, const ConvPlan& P) {
+  const int rows = gdn::conv_bwd_rows(P.tokens);
+  return align_up((size_t)(rows > 0 ? rows : 1) * (size_t)p->channels * (size_t)(p->kernel_size + 1) * sizeof(float));
+}
+
+gdn::ConvParams conv_params(const gdn_conv_problem* p, const ConvPlan& P) {
+  gdn::ConvParams c;
+  std::memset(&c, 0, sizeof(c));
+  c.cu = P.varlen ? p->cu_seqlens_dev : nullptr;
+  c.N = (int)P.N;
+  c.dense_T = P.varlen ? 0 : (int)P.T;
+  c.tokens = P.tokens;
+  c.C = (int)p->channels;
+  c.K = (int)p->kernel_size;
+  c.act = p->activation;
+  return c;
+}
+
 size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
   const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, p->dtype == GDN_BF16, true);
   return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)p->dim * sizeof(float));
@@ -319,6 +382,79 @@ gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x,
     return GDN_OK;
   } catch (...) {
     return fail(GDN_ERR_HIP, "unexpected exception in gdn_gated_rmsnorm_bwd");
+  }
+}
+
+size_t gdn_causal_conv1d_bwd_workspace_bytes(const gdn_conv_problem* p) {
+  try {
+    ConvPlan P;
+    if (check_conv(p, &P) != GDN_OK) return 0;
+    return conv_ws_bytes(p, P);
+  } catch (...) {
+    return 0;
+  }
+}
+
+gdn_status gdn_causal_conv1d_fwd(const gdn_conv_problem* p, const void* x, const float* w,
+                                 const float* bias, void* y, void* stream) {
+  try {
+    ConvPlan P;
+    gdn_status st = check_conv(p, &P);
+    if (st != GDN_OK) return st;
+    const size_t xb = (size_t)(P.tokens * p->channels) * (P.bf16 ? 2 : 4);
+    const size_t wb = (size_t)(p->channels * p->kernel_size) * sizeof(float);
+    const size_t bb = (size_t)p->channels * sizeof(float);
+    const Range req[] = {{x, xb, "x"}, {w, wb, "w"}, {y, xb, "y"}};
+    const Range opt[] = {{bias, bb, "bias"}};
+    const Range outs[] = {{y, xb, "y"}};
+    const Range ins[] = {{x, xb, "x"}, {w, wb, "w"}, {bias, bb, "bias"}};
+    st = check_ptrs(req, 3, opt, 1, outs, 1, ins, 3);
+    if (st != GDN_OK) return st;
+    gdn::ConvParams c = conv_params(p, P);
+    c.x = x; c.w = w; c.bias = bias; c.y = y;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed("conv_fwd", s, [&] { return gdn::launch_conv_fwd(c, P.bf16, s); });
+    if (e != hipSuccess) return hip_fail(e, "causal conv1d forward launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_causal_conv1d_fwd");
+  }
+}
+
+gdn_status gdn_causal_conv1d_bwd(const gdn_conv_problem* p, const void* x, const float* w,
+                                 const float* bias, const void* dy, void* dx, float* dw,
+                                 float* dbias, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  try {
+    ConvPlan P;
+    gdn_status st = check_conv(p, &P);
+    if (st != GDN_OK) return st;
+    const size_t xb = (size_t)(P.tokens * p->channels) * (P.bf16 ? 2 : 4);
+    const size_t wb = (size_t)(p->channels * p->kernel_size) * sizeof(float);
+    const size_t bb = (size_t)p->channels * sizeof(float);
+    const size_t need = conv_ws_bytes(p, P);
+    const Range req[] = {{x, xb, "x"}, {w, wb, "w"}, {dy, xb, "dy"}, {dx, xb, "dx"}, {dw, wb, "dw"},
+                         {workspace, need, "workspace"}};
+    const Range opt[] = {{bias, bb, "bias"}, {dbias, bb, "dbias"}};
+    const Range outs[] = {{dx, xb, "dx"}, {dw, wb, "dw"}, {dbias, bb, "dbias"}, {workspace, need, "workspace"}};
+    const Range ins[] = {{x, xb, "x"}, {w, wb, "w"}, {bias, bb, "bias"}, {dy, xb, "dy"}};
+    st = check_ptrs(req, 6, opt, 2, outs, 4, ins, 4);
+    if (st != GDN_OK) return st;
+    if (workspace && ((uintptr_t)workspace) % ALIGN)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+    gdn::ConvParams c = conv_params(p, P);
+    c.x = x; c.w = w; c.bias = bias; c.dy = dy; c.dx = dx; c.dw = dw; c.dbias = dbias;
+    c.part = reinterpret_cast<float*>(workspace);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = timed("conv_bwd", s, [&] { return gdn::launch_conv_bwd(c, P.bf16, s); });
+    if (e != hipSuccess) return hip_fail(e, "causal conv1d backward launch");
+    e = timed("conv_dw", s, [&] { return gdn::launch_conv_dw(c, s); });
+    if (e != hipSuccess) return hip_fail(e, "causal conv1d weight-gradient launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_causal_conv1d_bwd");
   }
 }
 

@@ -1,0 +1,355 @@
+// conv.hip -- causal depthwise conv1d (optional SiLU) over packed sequences,
+// forward and backward.
+//
+// XTuner / Ascend 910C Qwen3.5 training article, §3.1.2: the GDN stack's
+// causal conv1d, first a loop of slices and pads per sequence, then one
+// native forward and one backward kernel (Fig. 8).  Per channel c, kernel
+// size K <= 4, token t of a sequence whose first token is t0:
+//     pre[t] = bias + sum_j w[j] x[t - (K-1) + j]   (x = 0 before t0)
+//     y[t]   = silu(pre[t])  (or pre[t])
+// and, for an upstream dy, dpre = dy silu'(pre) (or dy),
+//     dx[t'] = sum_j w[j] dpre[t' + (K-1) - j]      (same sequence only)
+//     dw[j]  = sum_t dpre[t] x[t - (K-1) + j],  dbias = sum_t dpre[t].
+// All arithmetic fp32; each output rounded once.
+//
+// Layout: x, y, dy, dx are [tokens][C] (channels last); w is [C][K], bias
+// [C], fp32.  A lane owns CPT = 4 consecutive channels (an 8-byte bf16 or
+// 16-byte fp32 piece of a row, so a wave reads a contiguous run); a wave streams
+// TW consecutive tokens through a register window of the last K inputs (and,
+// backward, the last K values of dpre), so every row is read once plus a
+// K-1 row halo.  Sequence boundaries enter only through each token's
+// position in its sequence (pos) and the tokens left after it (rem): tap s
+// of y[t] reads x[t - s] iff s <= pos(t), and dx[t'] takes dpre[t' + d] iff
+// d <= rem(t').  dw and dbias: per-lane sums over the lane's tokens, then a
+// fixed-order sum over the waves of a workgroup (one partial per workgroup
+// row of the grid) and, in k_conv_dw, over the partials.
+#include <hip/hip_runtime.h>
+
+#include "frag.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int NW = 4;    // waves per workgroup (token sub-tiles)
+constexpr int TW = 16;   // tokens per wave
+constexpr int WIN = TW + 6;   // tokens whose (pos, rem) a wave needs: t_a - 3 .. t_a + TW + 2
+
+constexpr int CPT = 4;   // channels per lane
+
+template <typename E> struct CPiece;
+template <> struct CPiece<bf16> {
+  using R = bf16x4;   // raw piece as stored
+  static __device__ __forceinline__ f32x4 to_f(R v) { return __builtin_convertvector(v, f32x4); }
+  static __device__ __forceinline__ R from_f(f32x4 f) { return __builtin_convertvector(f, bf16x4); }
+};
+template <> struct CPiece<float> {
+  using R = f32x4;
+  static __device__ __forceinline__ f32x4 to_f(R v) { return v; }
+  static __device__ __forceinline__ R from_f(f32x4 f) { return f; }
+};
+
+__device__ __forceinline__ float csigmoid(float u) { return __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
+
+// Position of token t in its sequence and the tokens after it (rem); tokens
+// past the end get pos = rem = -1 (never read, never contribute).
+__device__ __forceinline__ void seq_pos(const ConvParams& p, long long t, int& pos, int& rem) {
+  if (t < 0 || t >= p.tokens) {
+    pos = rem = -1;
+    return;
+  }
+  if (!p.cu) {
+    const long long q = t / p.dense_T;
+    pos = (int)(t - q * p.dense_T);
+    rem = p.dense_T - 1 - pos;
+    return;
+  }
+  // the last sequence n with cu[n] <= t (empty sequences are skipped by it)
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  pos = (int)(t - p.cu[lo]);
+  rem = (int)(p.cu[lo + 1] - 1 - t);
+}
+
+template <typename E>
+__device__ __forceinline__ typename CPiece<E>::R load_row(const ConvParams& p, const void* base, long long t, int cp, bool live) {
+  using R = typename CPiece<E>::R;
+  if (!live || t < 0 || t >= p.tokens) return R{0, 0, 0, 0};
+  return reinterpret_cast<const R*>(base)[t * (p.C / CPT) + cp];
+}
+
+template <typename E, int K>
+__global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
+  using P = CPiece<E>;
+  const int lane = lane_id(), w = wave_id();
+  const int cp = blockIdx.x * 64 + lane;        // channel piece of this lane
+  const bool live = cp * CPT < p.C;
+  float wt[K][CPT], bs[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    const int c = live ? cp * CPT + e : 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) wt[j][e] = p.w[(size_t)c * K + j];
+    bs[e] = p.bias ? p.bias[c] : 0.f;
+  }
+  typename P::R* Y = reinterpret_cast<typename P::R*>(p.y);
+  for (long long tile = blockIdx.y; tile * (NW * TW) < p.tokens; tile += gridDim.y) {
+    const long long ta = tile * (NW * TW) + (long long)w * TW;
+    if (ta >= p.tokens) break;
+    // (pos, rem) of tokens ta - 3 + l in lane l
+    int pv = -1, rv = -1;
+    if (lane < WIN) seq_pos(p, ta - 3 + lane, pv, rv);
+    f32x4 hist[4];   // x[t], x[t-1], x[t-2], x[t-3] once the step's shift is done
+    hist[3] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 1; s < 4; ++s) hist[s - 1] = P::to_f(load_row<E>(p, p.x, ta - s, cp, live && s < K));
+#pragma unroll
+    for (int i0 = 0; i0 < TW; i0 += 8) {
+      typename P::R xs[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xs[i] = load_row<E>(p, p.x, ta + i0 + i, cp, live);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const long long t = ta + i0 + i;
+        hist[3] = hist[2];
+        hist[2] = hist[1];
+        hist[1] = hist[0];
+        hist[0] = P::to_f(xs[i]);
+        const int pos = __builtin_amdgcn_readlane(pv, i0 + i + 3);
+        if (t >= p.tokens) continue;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          float acc = bs[e];
+#pragma unroll
+          for (int s = 0; s < K; ++s)
+            if (s <= pos) acc += wt[K - 1 - s][e] * hist[s][e];
+          o[e] = p.act ? acc * csigmoid(acc) : acc;
+        }
+        if (live) Y[t * (p.C / CPT) + cp] = P::from_f(o);
+      }
+    }
+  }
+}
+
+template <typename E, int K>
+__global__ __launch_bounds__(64 * NW) void k_conv_bwd(ConvParams p) {
+  using P = CPiece<E>;
+  constexpr int NP = CPT * (K + 1);   // per-lane partial sums: dw taps, then dbias
+  __shared__ float red[NW][64][NP];
+  const int lane = lane_id(), w = wave_id();
+  const int cp = blockIdx.x * 64 + lane;
+  const bool live = cp * CPT < p.C;
+  float wt[K][CPT], bs[CPT], acc_w[K][CPT], acc_b[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    const int c = live ? cp * CPT + e : 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      wt[j][e] = p.w[(size_t)c * K + j];
+      acc_w[j][e] = 0.f;
+    }
+    bs[e] = p.bias ? p.bias[c] : 0.f;
+    acc_b[e] = 0.f;
+  }
+  typename P::R* DX = reinterpret_cast<typename P::R*>(p.dx);
+  for (long long tile = blockIdx.y; tile * (NW * TW) < p.tokens; tile += gridDim.y) {
+    const long long ta = tile * (NW * TW) + (long long)w * TW;
+    if (ta >= p.tokens) continue;   // no barrier inside the loop: waves may leave early
+    int pv = -1, rv = -1;
+    if (lane < WIN) seq_pos(p, ta - 3 + lane, pv, rv);
+    f32x4 xh[4];    // x[t], x[t-1], x[t-2], x[t-3] once the step's shift is done
+    f32x4 dh[4];    // dpre[t], dpre[t-1], dpre[t-2], dpre[t-3] likewise (dpre before ta is never used)
+    xh[3] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dh[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 1; s < 4; ++s) xh[s - 1] = P::to_f(load_row<E>(p, p.x, ta - s, cp, live && s < K));
+    // steps t = ta .. ta + TW + K - 2: dpre[t]; dx[t - (K-1)] once its window is complete
+#pragma unroll
+    for (int i0 = 0; i0 < TW + 8; i0 += 8) {
+      typename P::R xs[8], gs[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool need = i0 + i < TW + K - 1;
+        xs[i] = load_row<E>(p, p.x, ta + i0 + i, cp, live && need);
+        gs[i] = load_row<E>(p, p.dy, ta + i0 + i, cp, live && need);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ii = i0 + i;
+        if (ii >= TW + K - 1) continue;
+        const long long t = ta + ii;
+        xh[3] = xh[2];
+        xh[2] = xh[1];
+        xh[1] = xh[0];
+        xh[0] = P::to_f(xs[i]);
+        dh[3] = dh[2];
+        dh[2] = dh[1];
+        dh[1] = dh[0];
+        const int pos = __builtin_amdgcn_readlane(pv, ii + 3);
+        // dpre[t] (zero past the end of the tokens: pos = -1 there, and dy reads as zero)
+        const f32x4 gf = P::to_f(gs[i]);
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          float pre = bs[e];
+#pragma unroll
+          for (int s = 0; s < K; ++s)
+            if (s <= pos) pre += wt[K - 1 - s][e] * xh[s][e];
+          float g = gf[e];
+          if (p.act) {
+            const float sg = csigmoid(pre);
+            g = g * sg * (1.f + pre * (1.f - sg));
+          }
+          dh[0][e] = pos >= 0 ? g : 0.f;
+        }
+        // this wave's own tokens feed dw and dbias
+        if (ii < TW && pos >= 0) {
+#pragma unroll
+          for (int e = 0; e < CPT; ++e) {
+            acc_b[e] += dh[0][e];
+#pragma unroll
+            for (int s = 0; s < K; ++s)
+              if (s <= pos) acc_w[K - 1 - s][e] += dh[0][e] * xh[s][e];
+          }
+        }
+        // dx[t'] with t' = t - (K-1), over dpre[t' .. t]
+        const int jj = ii - (K - 1);
+        if (jj >= 0 && jj < TW) {
+          const long long tp = t - (K - 1);
+          const int rem = __builtin_amdgcn_readlane(rv, jj + 3);
+          if (tp < p.tokens) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < CPT; ++e) {
+              float a = 0.f;
+#pragma unroll
+              for (int d = 0; d < K; ++d)   // dpre[t' + d] sits in dh[K-1-d]
+                if (d <= rem) a += wt[K - 1 - d][e] * dh[K - 1 - d][e];
+              o[e] = a;
+            }
+            if (live) DX[tp * (p.C / CPT) + cp] = P::from_f(o);
+          }
+        }
+      }
+    }
+  }
+  // partials of this workgroup: the waves' sums added in wave order
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) red[w][lane][j * CPT + e] = acc_w[j][e];
+    red[w][lane][K * CPT + e] = acc_b[e];
+  }
+  __syncthreads();
+  if (w == 0 && live) {
+    float* dst = p.part + (size_t)blockIdx.y * p.C * (K + 1);
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int c = cp * CPT + e;
+#pragma unroll
+      for (int j = 0; j <= K; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s += red[ww][lane][j * CPT + e];
+        dst[(size_t)c * (K + 1) + j] = s;   // [row of the grid][channel][tap | bias]
+      }
+    }
+  }
+}
+
+// dw[c][j] (j < K) and dbias[c] (j = K): the sum over the grid rows' partials in
+// row order, one thread per (channel, tap).
+__global__ __launch_bounds__(256) void k_conv_dw(ConvParams p) {
+  const int K1 = p.K + 1;
+  const long long n = (long long)p.C * K1;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int r0 = 0; r0 < p.ntiles; r0 += 16) {   // 16 reads in flight, added in row order
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = r0 + i < p.ntiles ? p.part[(size_t)(r0 + i) * n + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += v[i];
+  }
+  const int c = (int)(e / K1), j = (int)(e - (long long)c * K1);
+  if (j < p.K) p.dw[(size_t)c * p.K + j] = s;
+  else if (p.dbias) p.dbias[c] = s;
+}
+
+template <typename E, int K>
+hipError_t conv_fwd_t(const ConvParams& p, hipStream_t s) {
+  if (p.tokens == 0 || p.C == 0) return hipSuccess;
+  ConvParams a = p;
+  void* args[] = {&a};
+  const int gx = (p.C / CPT + 63) / 64;
+  const long long tiles = (p.tokens + NW * TW - 1) / (NW * TW);
+  const int gy = (int)(tiles < 65535 ? tiles : 65535);
+  return hipLaunchKernel((const void*)k_conv_fwd<E, K>, dim3(gx, gy), dim3(64 * NW), args, 0, s);
+}
+
+template <typename E, int K>
+hipError_t conv_bwd_t(const ConvParams& p, hipStream_t s) {
+  ConvParams a = p;
+  a.ntiles = conv_bwd_rows(p.tokens);
+  void* args[] = {&a};
+  if (p.tokens > 0 && p.C > 0) {
+    const int gx = (p.C / CPT + 63) / 64;
+    hipError_t e = hipLaunchKernel((const void*)k_conv_bwd<E, K>, dim3(gx, a.ntiles), dim3(64 * NW), args, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename E>
+hipError_t conv_fwd_e(const ConvParams& p, hipStream_t s) {
+  switch (p.K) {
+    case 1: return conv_fwd_t<E, 1>(p, s);
+    case 2: return conv_fwd_t<E, 2>(p, s);
+    case 3: return conv_fwd_t<E, 3>(p, s);
+    case 4: return conv_fwd_t<E, 4>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+template <typename E>
+hipError_t conv_bwd_e(const ConvParams& p, hipStream_t s) {
+  switch (p.K) {
+    case 1: return conv_bwd_t<E, 1>(p, s);
+    case 2: return conv_bwd_t<E, 2>(p, s);
+    case 3: return conv_bwd_t<E, 3>(p, s);
+    case 4: return conv_bwd_t<E, 4>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int conv_bwd_rows(long long tokens) {
+  const long long tiles = (tokens + NW * TW - 1) / (NW * TW);
+  if (tiles <= 0) return 0;
+  return (int)(tiles < CONV_MAX_BWD_ROWS ? tiles : CONV_MAX_BWD_ROWS);
+}
+
+hipError_t launch_conv_fwd(const ConvParams& p, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? conv_fwd_e<bf16>(p, s) : conv_fwd_e<float>(p, s);
+}
+
+hipError_t launch_conv_bwd(const ConvParams& p, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? conv_bwd_e<bf16>(p, s) : conv_bwd_e<float>(p, s);
+}
+
+hipError_t launch_conv_dw(const ConvParams& p, hipStream_t s) {
+  ConvParams a = p;
+  a.ntiles = conv_bwd_rows(p.tokens);
+  void* args[] = {&a};
+  const long long n = (long long)p.C * (p.K + 1);
+  if (n == 0) return hipSuccess;
+  return hipLaunchKernel((const void*)k_conv_dw, dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, s);
+}
+
+}  // namespace gdn

@@ -106,6 +106,27 @@ hipError_t launch_gnorm_fwd(const GnormParams& p, int D, bool bf16, hipStream_t 
 hipError_t launch_gnorm_bwd(const GnormParams& p, int D, bool bf16, hipStream_t s);
 hipError_t launch_gnorm_dw(const GnormParams& p, int D, bool bf16, hipStream_t s);
 
+// Causal depthwise conv1d over packed sequences (conv.hip): x, y, dy, dx are
+// [tokens][C], w [C][K], bias [C], fp32 parameters.
+struct ConvParams {
+  const void *x, *dy;
+  const float *w, *bias;    // bias may be nullptr
+  void *y, *dx;
+  float *dw, *dbias;        // dbias may be nullptr
+  float* part;              // [ntiles][C][K+1] per-workgroup-row partials (workspace)
+  const int32_t* cu;        // device cu_seqlens, or nullptr (dense)
+  int N;                    // sequences
+  int dense_T;              // tokens per sequence when dense
+  long long tokens;
+  int C, K, act, ntiles;    // ntiles: set by the launchers
+};
+constexpr int CONV_MAX_BWD_ROWS = 64;
+// rows of the backward grid (and of its partials) for `tokens` tokens
+int conv_bwd_rows(long long tokens);
+hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t s);
+hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t s);
+hipError_t launch_conv_dw(const ConvParams& p, hipStream_t s);
+
 // Grid of the sequential kernels: one wave per (sequence, head, 16-column
 // block), padded so that the column blocks of one (sequence, head) share an
 // XCD (workgroup ids are dealt round-robin over the 8 XCDs).

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 3
+    assert gdn.lib().gdn_abi_version() == 4
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
@@ -39,6 +39,8 @@ def test_problem_struct_layout():
     assert ctypes.sizeof(gdn.GdnProblem) == 88
     # int64 x2, float, enum(int) -> 24 bytes
     assert ctypes.sizeof(gdn.GdnGatedNormProblem) == 24
+    # int64 x5, two pointers, int32, enum(int) -> 64 bytes
+    assert ctypes.sizeof(gdn.GdnConvProblem) == 64
 
 
 FAKE = 0x7f0000000000  # never dereferenced: every call below fails validation
@@ -246,3 +248,69 @@ def test_gated_norm_workspace_size():
     assert big == 1024 * 128 * 4
     assert L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(gnorm_problem(rows=0))) == 512
     assert L.gdn_gated_rmsnorm_bwd_workspace_bytes(ctypes.byref(gnorm_problem(dim=96))) == 0
+
+
+# ---- causal conv1d entry points ---------------------------------------------
+
+def conv_problem(**kw):
+    p = gdn.GdnConvProblem()
+    p.batch, p.seqlen, p.channels, p.kernel_size, p.num_seqs = 2, 100, 64, 4, 0
+    p.cu_seqlens_host = p.cu_seqlens_dev = None
+    p.activation, p.dtype = 1, gdn.GDN_BF16
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def call_conv_bwd(p, **over):
+    L = gdn.lib()
+    ptrs = dict(x=FAKE, w=FAKE + (1 << 30), b=FAKE + (2 << 30), dy=FAKE + (3 << 30), dx=FAKE + (4 << 30),
+                dw=FAKE + (5 << 30), db=FAKE + (6 << 30), ws=FAKE + (7 << 30))
+    ptrs.update(over)
+    need = L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(p))
+    P = ctypes.c_void_p
+    st = L.gdn_causal_conv1d_bwd(ctypes.byref(p), *(P(ptrs[n]) if ptrs[n] else None for n in
+                                                    ("x", "w", "b", "dy", "dx", "dw", "db", "ws")),
+                                 over.get("ws_bytes", need), None)
+    return st, gdn.last_error_message()
+
+
+CONV_CASES = [
+    ("k5", dict(kernel_size=5), {}, gdn.GDN_ERR_UNSUPPORTED, "kernel_size"),
+    ("k0", dict(kernel_size=0), {}, gdn.GDN_ERR_UNSUPPORTED, "kernel_size"),
+    ("c6", dict(channels=6), {}, gdn.GDN_ERR_UNSUPPORTED, "channels"),
+    ("act2", dict(activation=2), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "activation"),
+    ("dtype9", dict(dtype=9), {}, gdn.GDN_ERR_UNSUPPORTED, "dtype"),
+    ("seqlen_neg", dict(seqlen=-3), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "seqlen"),
+    ("batch0", dict(batch=0), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "batch"),
+    ("null_w", {}, dict(w=0), gdn.GDN_ERR_INVALID_ARGUMENT, "w is NULL"),
+    ("null_dx", {}, dict(dx=0), gdn.GDN_ERR_INVALID_ARGUMENT, "dx is NULL"),
+    ("misaligned_x", {}, dict(x=FAKE + 8), gdn.GDN_ERR_INVALID_ARGUMENT, "aligned"),
+    ("dx_aliases_dy", {}, dict(dx=FAKE + (3 << 30) + 128), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("db_aliases_dw", {}, dict(db=FAKE + (5 << 30) + 16), gdn.GDN_ERR_INVALID_ARGUMENT, "overlap"),
+    ("ws_small", {}, dict(ws_bytes=256), gdn.GDN_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+    ("ws_misaligned", {}, dict(ws=FAKE + (7 << 30) + 64), gdn.GDN_ERR_INVALID_ARGUMENT, "256-byte"),
+]
+
+
+@pytest.mark.parametrize("name,pkw,pover,status,msg", CONV_CASES, ids=[c[0] for c in CONV_CASES])
+def test_conv_invalid_arguments(name, pkw, pover, status, msg):
+    st, m = call_conv_bwd(conv_problem(**pkw), **pover)
+    assert st == status, (st, m)
+    assert msg in m, m
+
+
+def test_conv_varlen_validation_and_workspace():
+    arr = (ctypes.c_int32 * 4)(0, 30, 20, 100)
+    p = conv_problem(batch=1, num_seqs=3, cu_seqlens_host=ctypes.addressof(arr), cu_seqlens_dev=FAKE + (1 << 40))
+    st, m = call_conv_bwd(p)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "decreases" in m
+    arr2 = (ctypes.c_int32 * 3)(0, 30, 100)
+    p = conv_problem(batch=2, num_seqs=2, cu_seqlens_host=ctypes.addressof(arr2), cu_seqlens_dev=FAKE + (1 << 40))
+    st, m = call_conv_bwd(p)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "batch" in m
+    L = gdn.lib()
+    # one fp32 partial per (grid row, channel, tap or bias), at most 64 grid rows
+    big = L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(conv_problem(batch=1, seqlen=1 << 20, channels=6144)))
+    assert big == 64 * 6144 * 5 * 4
+    assert L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(conv_problem(kernel_size=7))) == 0
