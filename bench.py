@@ -53,6 +53,10 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         "gnorm_fwd": 3 * C * D * E,
         # reads x, z, dy; writes dx, dz (the dw partials are per workgroup, not counted)
         "gnorm_bwd": 5 * C * D * E,
+        # causal conv1d on one of q, k, v (one head's D channels per unit): reads x, writes y
+        "conv_fwd": 2 * C * D * E,
+        # reads x, dy; writes dx (the dw/dbias partials are per workgroup, not counted)
+        "conv_bwd": 3 * C * D * E,
     }
     out = {k: v * units for k, v in per_unit.items()}
     if with_ht:
@@ -107,19 +111,25 @@ def traffic_for(kernel):
     return round(found)
 
 
-def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None):
+def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
     import oracle
     nthreads = min(16, os.cpu_count() or 1)
     used = oracle.threads_used(x["N"], x["H"], nthreads)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        o, _ = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
+        qkv = [x["q"], x["k"], x["v"]]
+        if cv is not None:
+            qkv = [oracle.causal_conv1d_fwd(c["x"], c["w"]).reshape(x["q"].shape) for c in cv]
+        o, _ = oracle.fwd(*qkv, x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
         do = x["do"]
         if gn is not None:
             oracle.gated_rmsnorm_fwd(o, gn["z"].reshape(o.shape), gn["w"])
             do = oracle.gated_rmsnorm_bwd(o, gn["z"].reshape(o.shape), gn["w"], gn["dy"].reshape(o.shape))[0]
-        oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], do, nthreads=nthreads, qk_l2norm=l2)
+        grads = oracle.bwd(*qkv, x["g"], x["beta"], do, nthreads=nthreads, qk_l2norm=l2)
+        if cv is not None:
+            for c, gq in zip(cv, grads[:3]):
+                oracle.causal_conv1d_bwd(c["x"], c["w"], gq.reshape(c["x"].shape))
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
@@ -183,6 +193,9 @@ def main():
     ap.add_argument("--gated-norm", action="store_true",
                     help="the output gate's RMSNorm in the step (forward after the operator, its "
                          "backward feeding the operator's); not the headline workload")
+    ap.add_argument("--conv", action="store_true",
+                    help="the layer's causal conv1d (K=4, SiLU) on raw q, k, v projections before the "
+                         "operator, its backward after; implies --qk-l2norm; not the headline workload")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
@@ -200,7 +213,7 @@ def main():
 
     dev = torch.device("cuda:0")
     cfg = gi.CONFIGS["metric"]
-    l2 = bool(args.qk_l2norm)
+    l2 = bool(args.qk_l2norm or args.conv)
     if l2:
         import dataclasses
         cfg = dataclasses.replace(cfg, qk_normalized=False)
@@ -212,6 +225,15 @@ def main():
 
     q, k, v, do = (t(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
     g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
+    cv = None
+    if args.conv:
+        # raw projections of q, k, v, each [B, T, H*D] channels last, and their conv weights
+        cv = [gi.make_conv_inputs(B, T, H * D, 4, "bf16", seed=20 + i) for i in range(3)]
+        cvx = [t(c["x"], torch.bfloat16) for c in cv]
+        cvw = [t(c["w"], torch.float32) for c in cv]
+        pc = gdn.make_conv_problem(cvx[0], 4)
+        wsc = torch.empty(gdn.lib().gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(pc)), dtype=torch.uint8,
+                          device=dev)
     gn = None
     if args.gated_norm:
         gn = gi.make_gated_norm_inputs(B * T * H, D, "bf16", seed=1, x=np.zeros((B * T * H, D)))
@@ -229,12 +251,19 @@ def main():
                           device=dev)
 
     def step():
-        o, ht, ctx = gdn.fwd(q, k, v, g, beta, return_context=True, workspace=wsf, qk_l2norm=l2)
+        qq, kk, vv = q, k, v
+        if cv is not None:
+            qq, kk, vv = (gdn.causal_conv1d_fwd(xx, ww).view(B, T, H, D) for xx, ww in zip(cvx, cvw))
+        o, ht, ctx = gdn.fwd(qq, kk, vv, g, beta, return_context=True, workspace=wsf, qk_l2norm=l2)
         dO = do
         if gn is not None:
             gdn.gated_rmsnorm_fwd(o, zt, wt)
             dO = gdn.gated_rmsnorm_bwd(o, zt, wt, dyt, workspace=wsn)[0]
-        return gdn.bwd(q, k, v, g, beta, dO, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
+        grads = gdn.bwd(qq, kk, vv, g, beta, dO, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
+        if cv is not None:
+            for xx, ww, gg in zip(cvx, cvw, grads[:3]):
+                gdn.causal_conv1d_bwd(xx, ww, gg.view(B, T, H * D), workspace=wsc)
+        return grads
 
     for _ in range(args.warmup):
         step()
@@ -252,7 +281,7 @@ def main():
     step_roof = None
     units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
     if not args.no_profile_pass:
-        launches_per_step = 11 if gn is not None else 8
+        launches_per_step = 8 + (3 if gn is not None else 0) + (9 if cv is not None else 0)
         n = launches_per_step * args.steps
         evs = HipEvents(2 * n)
         L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)
@@ -301,14 +330,14 @@ def main():
     if args.copy_calib:
         copy_calibration(torch, dev)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(x, l2=l2, gn=gn)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(x, l2=l2, gn=gn, cv=cv)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "gdn_fwdbwd_B1_T4096_H16_d128_bf16_chunk64" + ("_qkl2norm" if l2 else "")
-                   + ("_gatednorm" if gn is not None else ""),
+                   + ("_conv1d" if cv is not None else "") + ("_gatednorm" if gn is not None else ""),
                    "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,

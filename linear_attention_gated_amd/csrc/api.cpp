@@ -276,7 +276,7 @@ gdn_status check_conv(const gdn_conv_problem* p, ConvPlan* P) {
 }
 
 size_t conv_ws_bytes(const gdn_conv_problem* p, const ConvPlan& P) {
-  const int rows = gdn::conv_bwd_rows(P.tokens);
+  const int rows = gdn::conv_bwd_rows(P.tokens, (int)p->channels);
   return align_up((size_t)(rows > 0 ? rows : 1) * (size_t)p->channels * (size_t)(p->kernel_size + 1) * sizeof(float));
 }
 

@@ -102,23 +102,25 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   const size_t base = ((size_t)tok0 * H + h) * D;
   const float sc = p.scale;
 
-  // ---- stage Q, K, dO; the -W records of this wave's i-slice
-  if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
+  // ---- stage Q, K, dO; the -W records of this wave's i-slice.  Every global
+  // read is issued before the first use of any of them.
+  const float gv = p.gamma[(size_t)ch * 64 + lane];
+  frag_t<E> wrec[4];
   {
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
     sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
     sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
     so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
+    if (w == 0) s_gam[lane] = gv;
     // query norms for this pass and the gradient pass (same arithmetic as the forward's)
     if constexpr (NORM) sq.norm_rows(L, tid, p.qinv + nb, H);
     sq.store(tQ, tid);
     sk.store(tK, tid);
     so.store(tO, tid);
   }
-  frag_t<E> wrec[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
   __syncthreads();
   const float gL = s_gam[63];
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
@@ -552,10 +554,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   {
     const float gv = p.gamma[(size_t)ch * 64 + lane];
     const float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
-    if (w == 0) {
-      s_gam[lane] = gv;
-      s_beta[lane] = bv;
-    }
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
     sq.load(Q + base, rowstride, L, tid, NORM ? p.qinv + nb : nullptr, H);
@@ -568,6 +566,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     for (int k = 0; k < TPER; ++k) {
       const int e = tid + k * NT, r = e >> 4, c4 = e & 15;
       tv[k] = *reinterpret_cast<const f32x4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4);
+    }
+    // (the decays are written once every read above is in flight)
+    if (w == 0) {
+      s_gam[lane] = gv;
+      s_beta[lane] = bv;
     }
     sq.store(tQ, tid);
     sk.store(tK, tid);

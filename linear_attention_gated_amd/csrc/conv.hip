@@ -14,8 +14,8 @@
 //
 // Layout: x, y, dy, dx are [tokens][C] (channels last); w is [C][K], bias
 // [C], fp32.  A lane owns CPT = 4 consecutive channels (an 8-byte bf16 or
-// 16-byte fp32 piece of a row, so a wave reads a contiguous run); a wave streams
-// TW consecutive tokens through a register window of the last K inputs (and,
+// 16-byte fp32 piece of a row), so a wave reads a contiguous run; a wave
+// streams TW consecutive tokens through a register window of the last K inputs (and,
 // backward, the last K values of dpre), so every row is read once plus a
 // K-1 row halo.  Sequence boundaries enter only through each token's
 // position in its sequence (pos) and the tokens left after it (rem): tap s
@@ -31,22 +31,37 @@
 namespace gdn {
 namespace {
 
-constexpr int NW = 4;    // waves per workgroup (token sub-tiles)
-constexpr int TW = 16;   // tokens per wave
-constexpr int WIN = TW + 6;   // tokens whose (pos, rem) a wave needs: t_a - 3 .. t_a + TW + 2
+constexpr int NW = 4;     // waves per workgroup (token sub-tiles)
+// Tokens per wave: longer tiles cut the halo re-reads (the backward's is
+// two-sided), shorter ones give a narrow problem (few channels) enough waves.
+// The launcher picks per problem.
+constexpr int TWF = 16, TWF_NARROW = 8;    // forward
+constexpr int TWB = 32, TWB_NARROW = 16;   // backward
+constexpr long long FWD_MIN_WG = 1536, BWD_MIN_WG = 768;   // 6 and 3 workgroups per CU
 
-constexpr int CPT = 4;   // channels per lane
+__host__ __device__ constexpr long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+inline int conv_gx(int C) { return (C / 4 + 63) / 64; }
+inline int conv_fwd_tw(long long tokens, int C) {
+  return conv_gx(C) * cdiv(tokens, NW * TWF) >= FWD_MIN_WG ? TWF : TWF_NARROW;
+}
+inline int conv_bwd_tw(long long tokens, int C) {
+  const long long rows = cdiv(tokens, NW * TWB);
+  return conv_gx(C) * (rows < CONV_MAX_BWD_ROWS ? rows : CONV_MAX_BWD_ROWS) >= BWD_MIN_WG ? TWB : TWB_NARROW;
+}
 
-template <typename E> struct CPiece;
-template <> struct CPiece<bf16> {
-  using R = bf16x4;   // raw piece as stored
-  static __device__ __forceinline__ f32x4 to_f(R v) { return __builtin_convertvector(v, f32x4); }
-  static __device__ __forceinline__ R from_f(f32x4 f) { return __builtin_convertvector(f, bf16x4); }
+// A lane's piece of a row: N channels, raw as stored (R) and in fp32 (F).
+template <typename E, int N> struct CPiece;
+template <> struct CPiece<bf16, 4> {
+  using R = bf16x4;
+  using F = f32x4;
+  static __device__ __forceinline__ F to_f(R v) { return __builtin_convertvector(v, f32x4); }
+  static __device__ __forceinline__ R from_f(F f) { return __builtin_convertvector(f, bf16x4); }
 };
-template <> struct CPiece<float> {
+template <> struct CPiece<float, 4> {
   using R = f32x4;
-  static __device__ __forceinline__ f32x4 to_f(R v) { return v; }
-  static __device__ __forceinline__ R from_f(f32x4 f) { return f; }
+  using F = f32x4;
+  static __device__ __forceinline__ F to_f(R v) { return v; }
+  static __device__ __forceinline__ R from_f(F f) { return f; }
 };
 
 __device__ __forceinline__ float csigmoid(float u) { return __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
@@ -75,16 +90,22 @@ __device__ __forceinline__ void seq_pos(const ConvParams& p, long long t, int& p
   rem = (int)(p.cu[lo + 1] - 1 - t);
 }
 
-template <typename E>
-__device__ __forceinline__ typename CPiece<E>::R load_row(const ConvParams& p, const void* base, long long t, int cp, bool live) {
-  using R = typename CPiece<E>::R;
-  if (!live || t < 0 || t >= p.tokens) return R{0, 0, 0, 0};
-  return reinterpret_cast<const R*>(base)[t * (p.C / CPT) + cp];
+// Row t's piece cp, or zeros outside the tokens / channels.  The read is
+// unconditional (from row 0, piece 0 when out of range; tokens >= 1), so a
+// batch of these issues back to back instead of one branch and wait each.
+template <typename E, int CPT>
+__device__ __forceinline__ typename CPiece<E, CPT>::R load_row(const ConvParams& p, const void* base, long long t, int cp, bool live) {
+  using R = typename CPiece<E, CPT>::R;
+  const bool ok = live && t >= 0 && t < p.tokens;
+  const R v = reinterpret_cast<const R*>(base)[(ok ? t : 0) * (p.C / CPT) + (ok ? cp : 0)];
+  return ok ? v : R{};
 }
 
-template <typename E, int K>
+template <typename E, int K, int CPT, int TW>
 __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
-  using P = CPiece<E>;
+  using P = CPiece<E, CPT>;
+  using F = typename P::F;
+  constexpr int WIN = TW + 6;   // (pos, rem) of tokens t_a - 3 .. t_a + TW + 2
   const int lane = lane_id(), w = wave_id();
   const int cp = blockIdx.x * 64 + lane;        // channel piece of this lane
   const bool live = cp * CPT < p.C;
@@ -103,15 +124,15 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
     // (pos, rem) of tokens ta - 3 + l in lane l
     int pv = -1, rv = -1;
     if (lane < WIN) seq_pos(p, ta - 3 + lane, pv, rv);
-    f32x4 hist[4];   // x[t], x[t-1], x[t-2], x[t-3] once the step's shift is done
-    hist[3] = f32x4{0.f, 0.f, 0.f, 0.f};
+    F hist[4];   // x[t], x[t-1], x[t-2], x[t-3] once the step's shift is done
+    hist[3] = F{};
 #pragma unroll
-    for (int s = 1; s < 4; ++s) hist[s - 1] = P::to_f(load_row<E>(p, p.x, ta - s, cp, live && s < K));
+    for (int s = 1; s < 4; ++s) hist[s - 1] = P::to_f(load_row<E, CPT>(p, p.x, ta - s, cp, live && s < K));
 #pragma unroll
     for (int i0 = 0; i0 < TW; i0 += 8) {
       typename P::R xs[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xs[i] = load_row<E>(p, p.x, ta + i0 + i, cp, live);
+      for (int i = 0; i < 8; ++i) xs[i] = load_row<E, CPT>(p, p.x, ta + i0 + i, cp, live);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const long long t = ta + i0 + i;
@@ -121,7 +142,7 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
         hist[0] = P::to_f(xs[i]);
         const int pos = __builtin_amdgcn_readlane(pv, i0 + i + 3);
         if (t >= p.tokens) continue;
-        f32x4 o;
+        F o;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
           float acc = bs[e];
@@ -136,9 +157,11 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
   }
 }
 
-template <typename E, int K>
+template <typename E, int K, int TW>
 __global__ __launch_bounds__(64 * NW) void k_conv_bwd(ConvParams p) {
-  using P = CPiece<E>;
+  constexpr int CPT = 4;
+  using P = CPiece<E, CPT>;
+  constexpr int WIN = TW + 6;   // (pos, rem) of tokens t_a - 3 .. t_a + TW + 2
   constexpr int NP = CPT * (K + 1);   // per-lane partial sums: dw taps, then dbias
   __shared__ float red[NW][64][NP];
   const int lane = lane_id(), w = wave_id();
@@ -168,7 +191,7 @@ __global__ __launch_bounds__(64 * NW) void k_conv_bwd(ConvParams p) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) dh[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 1; s < 4; ++s) xh[s - 1] = P::to_f(load_row<E>(p, p.x, ta - s, cp, live && s < K));
+    for (int s = 1; s < 4; ++s) xh[s - 1] = P::to_f(load_row<E, CPT>(p, p.x, ta - s, cp, live && s < K));
     // steps t = ta .. ta + TW + K - 2: dpre[t]; dx[t - (K-1)] once its window is complete
 #pragma unroll
     for (int i0 = 0; i0 < TW + 8; i0 += 8) {
@@ -176,8 +199,8 @@ __global__ __launch_bounds__(64 * NW) void k_conv_bwd(ConvParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const bool need = i0 + i < TW + K - 1;
-        xs[i] = load_row<E>(p, p.x, ta + i0 + i, cp, live && need);
-        gs[i] = load_row<E>(p, p.dy, ta + i0 + i, cp, live && need);
+        xs[i] = load_row<E, CPT>(p, p.x, ta + i0 + i, cp, live && need);
+        gs[i] = load_row<E, CPT>(p, p.dy, ta + i0 + i, cp, live && need);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -287,20 +310,24 @@ hipError_t conv_fwd_t(const ConvParams& p, hipStream_t s) {
   if (p.tokens == 0 || p.C == 0) return hipSuccess;
   ConvParams a = p;
   void* args[] = {&a};
-  const int gx = (p.C / CPT + 63) / 64;
-  const long long tiles = (p.tokens + NW * TW - 1) / (NW * TW);
+  // 4 channels per lane: 16-byte bf16 pieces (8 channels) measured slower,
+  // the grid has half the waves
+  const int tw = conv_fwd_tw(p.tokens, p.C);
+  const long long tiles = cdiv(p.tokens, NW * tw);
   const int gy = (int)(tiles < 65535 ? tiles : 65535);
-  return hipLaunchKernel((const void*)k_conv_fwd<E, K>, dim3(gx, gy), dim3(64 * NW), args, 0, s);
+  const void* k = tw == TWF ? (const void*)k_conv_fwd<E, K, 4, TWF> : (const void*)k_conv_fwd<E, K, 4, TWF_NARROW>;
+  return hipLaunchKernel(k, dim3(conv_gx(p.C), gy), dim3(64 * NW), args, 0, s);
 }
 
 template <typename E, int K>
 hipError_t conv_bwd_t(const ConvParams& p, hipStream_t s) {
   ConvParams a = p;
-  a.ntiles = conv_bwd_rows(p.tokens);
+  a.ntiles = conv_bwd_rows(p.tokens, p.C);
   void* args[] = {&a};
   if (p.tokens > 0 && p.C > 0) {
-    const int gx = (p.C / CPT + 63) / 64;
-    hipError_t e = hipLaunchKernel((const void*)k_conv_bwd<E, K>, dim3(gx, a.ntiles), dim3(64 * NW), args, 0, s);
+    const void* k = conv_bwd_tw(p.tokens, p.C) == TWB ? (const void*)k_conv_bwd<E, K, TWB>
+                                                       : (const void*)k_conv_bwd<E, K, TWB_NARROW>;
+    hipError_t e = hipLaunchKernel(k, dim3(conv_gx(p.C), a.ntiles), dim3(64 * NW), args, 0, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -329,8 +356,8 @@ hipError_t conv_bwd_e(const ConvParams& p, hipStream_t s) {
 
 }  // namespace
 
-int conv_bwd_rows(long long tokens) {
-  const long long tiles = (tokens + NW * TW - 1) / (NW * TW);
+int conv_bwd_rows(long long tokens, int C) {
+  const long long tiles = cdiv(tokens, NW * conv_bwd_tw(tokens, C));
   if (tiles <= 0) return 0;
   return (int)(tiles < CONV_MAX_BWD_ROWS ? tiles : CONV_MAX_BWD_ROWS);
 }
@@ -345,7 +372,7 @@ hipError_t launch_conv_bwd(const ConvParams& p, bool is_bf16, hipStream_t s) {
 
 hipError_t launch_conv_dw(const ConvParams& p, hipStream_t s) {
   ConvParams a = p;
-  a.ntiles = conv_bwd_rows(p.tokens);
+  a.ntiles = conv_bwd_rows(p.tokens, p.C);
   void* args[] = {&a};
   const long long n = (long long)p.C * (p.K + 1);
   if (n == 0) return hipSuccess;

@@ -103,19 +103,6 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   const E* K = reinterpret_cast<const E*>(p.k);
   const E* V = reinterpret_cast<const E*>(p.v);
 
-  // chunk-local cumulative log decay; padded rows get g = 0, beta = 0
-  float gv = 0.f, bv = 0.f;
-  if (lane < L) {
-    gv = p.g[(size_t)(tok0 + lane) * H + h];
-    bv = p.beta[(size_t)(tok0 + lane) * H + h];
-  }
-  const float gam = wave_incl_scan(gv, lane);
-  if (w == 0) {
-    s_gam[lane] = gam;
-    s_beta[lane] = bv;
-    p.gamma[(size_t)ch * 64 + lane] = gam;
-  }
-
   // natural key fragments F(K; s, i) for all row blocks, and this wave's
   // value columns (used after the solve; their reads overlap it)
   // (raw keys: with normalisation the Gram tiles take both rows' reciprocal
@@ -130,6 +117,19 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
                            : zero_frag<E>();
     vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
                       : zero_frag<E>();
+  }
+  // chunk-local cumulative log decay (read after the key and value reads are
+  // in flight); padded rows get g = 0, beta = 0
+  float gv = 0.f, bv = 0.f;
+  if (lane < L) {
+    gv = p.g[(size_t)(tok0 + lane) * H + h];
+    bv = p.beta[(size_t)(tok0 + lane) * H + h];
+  }
+  const float gam = wave_incl_scan(gv, lane);
+  if (w == 0) {
+    s_gam[lane] = gam;
+    s_beta[lane] = bv;
+    p.gamma[(size_t)ch * 64 + lane] = gam;
   }
   if constexpr (NORM) {
     // sign-encoded reciprocal key norms; every wave holds whole rows, wave 0
@@ -508,24 +508,25 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   const size_t rowstride = (size_t)H * D;
   const size_t base = ((size_t)tok0 * H + h) * D;
 
-  if (w == 0) s_gam[lane] = p.gamma[(size_t)ch * 64 + lane];
+  // every global read is issued before the first use of any of them
+  const float gv = p.gamma[(size_t)ch * 64 + lane];
+  frag_t<E> hr[2][KB], vr[2][2];   // this wave's column blocks of h and V'
   {
     TileStage<E, D, NT> sq, sk;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
     sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
     sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) hr[hs][kb] = load_rec<E>(Hf + (((size_t)ch * NJ + 2 * w + hs) * KB + kb) * REC, lane);
+#pragma unroll
+      for (int skb = 0; skb < 2; ++skb) vr[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
+    }
+    if (w == 0) s_gam[lane] = gv;
     if constexpr (NORM) sq.norm_rows(L, tid, nullptr, 0);
     sq.store(tQ, tid);
     sk.store(tK, tid);
-  }
-  // this wave's column blocks of h and V'
-  frag_t<E> hr[2][KB], vr[2][2];
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hr[hs][kb] = load_rec<E>(Hf + (((size_t)ch * NJ + 2 * w + hs) * KB + kb) * REC, lane);
-#pragma unroll
-    for (int skb = 0; skb < 2; ++skb) vr[hs][skb] = load_rec<E>(Vf + (((size_t)ch * NJ + 2 * w + hs) * 2 + skb) * REC, lane);
   }
   // upper blocks of P are zero
   zero_off_blocks<E, true>(sP, LDE, tid, NT);

@@ -121,8 +121,8 @@ struct ConvParams {
   int C, K, act, ntiles;    // ntiles: set by the launchers
 };
 constexpr int CONV_MAX_BWD_ROWS = 64;
-// rows of the backward grid (and of its partials) for `tokens` tokens
-int conv_bwd_rows(long long tokens);
+// rows of the backward grid (and of its partials) for `tokens` tokens of C channels
+int conv_bwd_rows(long long tokens, int C);
 hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t s);
 hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t s);
 hipError_t launch_conv_dw(const ConvParams& p, hipStream_t s);

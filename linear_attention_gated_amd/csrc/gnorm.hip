@@ -81,13 +81,10 @@ __global__ __launch_bounds__(NT) void k_gnorm_fwd(GnormParams p) {
   for (long long q0 = (long long)blockIdx.x * NT + threadIdx.x; q0 < npieces; q0 += PPT * S) {
     i32x4 xv[PPT], zv[PPT];
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const long long q = q0 + k * S;
-      xv[k] = zv[k] = i32x4{0, 0, 0, 0};
-      if (q < npieces) {
-        xv[k] = X[q];
-        zv[k] = Z[q];
-      }
+    for (int k = 0; k < PPT; ++k) {   // unconditional reads (piece 0 out of range): all in flight
+      const long long q = q0 + k * S, qc = q < npieces ? q : 0;
+      xv[k] = X[qc];
+      zv[k] = Z[qc];
     }
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
@@ -130,14 +127,11 @@ __global__ __launch_bounds__(NT) void k_gnorm_bwd(GnormParams p) {
   for (long long q0 = (long long)blockIdx.x * NT + threadIdx.x; q0 < npieces; q0 += PPT * S) {
     i32x4 xv[PPT], zv[PPT], gv[PPT];
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const long long q = q0 + k * S;
-      xv[k] = zv[k] = gv[k] = i32x4{0, 0, 0, 0};
-      if (q < npieces) {
-        xv[k] = X[q];
-        zv[k] = Z[q];
-        gv[k] = DY[q];
-      }
+    for (int k = 0; k < PPT; ++k) {   // unconditional reads (piece 0 out of range): all in flight
+      const long long q = q0 + k * S, qc = q < npieces ? q : 0;
+      xv[k] = X[qc];
+      zv[k] = Z[qc];
+      gv[k] = DY[qc];
     }
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {

@@ -108,3 +108,17 @@ def test_no_tokens_writes_zero_gradients():
     dx, dw, db = gdn.causal_conv1d_bwd(x, w, x, b)
     torch.cuda.synchronize()
     assert torch.all(dw == 0) and torch.all(db == 0)
+
+
+def test_concatenated_channels_equal_separate_calls():
+    # the conv is per channel: one call over q, k, v concatenated (3 x 2048 channels) gives
+    # bitwise the same outputs as one call per part (how the operator's q, k, v are fed)
+    x = gi.make_conv_inputs(1, 300, 3 * 256, 4, "bf16", seed=8)
+    whole = run(x)
+    for i in range(3):
+        sl = slice(256 * i, 256 * (i + 1))
+        part = dict(x, x=np.ascontiguousarray(x["x"][..., sl]), dy=np.ascontiguousarray(x["dy"][..., sl]),
+                    w=np.ascontiguousarray(x["w"][sl]), bias=np.ascontiguousarray(x["bias"][sl]), C=256)
+        got = run(part)
+        assert np.array_equal(got[0], whole[0][..., sl]) and np.array_equal(got[1], whole[1][..., sl])
+        assert np.array_equal(got[2], whole[2][sl]) and np.array_equal(got[3], whole[3][sl])
