@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
   GDN_OK = 0,
@@ -141,6 +141,34 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                    const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
                    float* dh0, const void* fwd_workspace, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* ---- Recurrent (decoding) forward ----------------------------------------
+ * The same recurrence as gdn_fwd, taken token by token for the decoding
+ * regime: each sequence brings a few new tokens and its state is read and
+ * written once, in place.  (The article covers training only; the operator
+ * is the one of its §3.1.2.)  For each sequence and head, token by token:
+ *     S <- exp(g) S (I - beta k k^T) + beta v k^T,   o = scale S q
+ * with q, k L2-normalised first when qk_l2norm = 1, in fp32.
+ *
+ * The problem is a gdn_problem with these differences: dk and dv may differ
+ * (each in {64, 128}); `chunk` is ignored; seqlen is the number of new tokens
+ * per sequence (dense) or their packed total (cu_seqlens).  Layouts of q, k,
+ * v, g, beta and o as for gdn_fwd.
+ *   state          : device fp32 [num_slots][H][dk][dv] holding S^T, read and
+ *                    overwritten in place
+ *   state_indices  : NULL (sequence n uses slot n; num_slots >= N), or device
+ *                    int32 [N]: sequence n uses slot state_indices[n].  An
+ *                    index outside [0, num_slots) skips the sequence: its o
+ *                    rows are written as zeros and no state is touched.  Two
+ *                    sequences must not name the same slot.
+ * Ownership, streams and errors as for gdn_fwd; o must not overlap the
+ * inputs or the state.  Any number of tokens per sequence is allowed; the
+ * tokens of one sequence run one after another, so long prompts belong to
+ * gdn_fwd (which leaves the final state in ht for a following decode). */
+gdn_status gdn_recurrent_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* state_indices, int64_t num_slots, void* o,
+                             void* stream);
 
 /* ---- Gated RMSNorm on the operator's output ------------------------------
  * The output gate of the GDN layer, as the XTuner / Ascend 910C Qwen3.5
@@ -230,7 +258,8 @@ gdn_status gdn_causal_conv1d_bwd(const gdn_conv_problem* p, const void* x, const
 
 /* ---- Timing diagnostics ------------------------------------------------
  * gdn_profile_events: bracket each kernel launched by the following
- * gdn_fwd / gdn_bwd / gdn_gated_rmsnorm_* / gdn_causal_conv1d_* calls made on this thread with caller-created HIP events
+ * gdn_fwd / gdn_bwd / gdn_recurrent_fwd / gdn_gated_rmsnorm_* / gdn_causal_conv1d_* calls made on
+ * this thread with caller-created HIP events
  * (hipEvent_t passed as void*): events[2i] is recorded on the call's stream
  * just before launch i and events[2i+1] just after it, for the first n_pairs
  * launches; later launches run unbracketed.  Enabling restarts the launch

@@ -7,6 +7,7 @@ no fallback: if the library is missing or fails, these functions raise.
 
     o, ht = fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
     dq, dk, dv, dg, dbeta, dh0 = bwd(q, k, v, g, beta, do, ...)
+    o = recurrent_fwd(q, k, v, g, beta, state, state_indices=None)   # decoding, state in place
     y = gated_rmsnorm_fwd(x, z, w, eps=1e-6)          # the output gate: RMSNorm(x) w silu(z)
     dx, dz, dw = gated_rmsnorm_bwd(x, z, w, dy, eps=1e-6)
     y = causal_conv1d_fwd(x, w, bias=None, cu_seqlens=None, activation=True)   # x [B,T,C], w [C,K]
@@ -34,7 +35,7 @@ EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_byt
             "gdn_bwd", "gdn_status_string", "gdn_last_error_message", "gdn_profile_events",
             "gdn_profile_count", "gdn_profile_name", "gdn_gated_rmsnorm_bwd_workspace_bytes",
             "gdn_gated_rmsnorm_fwd", "gdn_gated_rmsnorm_bwd", "gdn_causal_conv1d_bwd_workspace_bytes",
-            "gdn_causal_conv1d_fwd", "gdn_causal_conv1d_bwd")
+            "gdn_causal_conv1d_fwd", "gdn_causal_conv1d_bwd", "gdn_recurrent_fwd")
 
 
 class GdnProblem(ctypes.Structure):
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_causal_conv1d_fwd.restype = ctypes.c_int
         L.gdn_causal_conv1d_bwd.argtypes = [cprob] + [p] * 7 + [p, sz, p]
         L.gdn_causal_conv1d_bwd.restype = ctypes.c_int
+        L.gdn_recurrent_fwd.argtypes = [prob] + [p] * 7 + [ctypes.c_int64, p, p]
+        L.gdn_recurrent_fwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -385,3 +388,27 @@ def causal_conv1d_bwd(x, w, dy, bias=None, cu_seqlens=None, activation=True, nee
     _check(L.gdn_causal_conv1d_bwd(ctypes.byref(p), _ptr(x), _ptr(w), _ptr(bias), _ptr(dy), _ptr(dx),
                                    _ptr(dw), _ptr(db), _ptr(workspace), nbytes, _stream(x.device)))
     return dx, dw, db
+
+
+# ---- recurrent (decoding) forward --------------------------------------------
+
+def recurrent_fwd(q, k, v, g, beta, state, state_indices=None, cu_seqlens=None, scale=1.0,
+                  qk_l2norm=False):
+    """Token-by-token forward for decoding; ``state`` [num_slots, H, dk, dv] fp32 (holding
+    S^T) is updated in place.  Sequence n uses slot n, or ``state_indices[n]`` (int32 on the
+    device; an index outside [0, num_slots) skips the sequence and gives zero outputs).
+    q, k [B, T, H, dk], v [B, T, H, dv] (B = 1 with cu_seqlens); dk and dv may differ.
+    Returns o [B, T, H, dv]."""
+    dev, dt = q.device, q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, dt, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(beta, "beta", torch.float32, dev)
+    _require(state, "state", torch.float32, dev)
+    _require(state_indices, "state_indices", torch.int32, dev)
+    cu_h, cu_d = _cu_pair(cu_seqlens, dev)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
+    o = torch.empty(v.shape, dtype=dt, device=dev)
+    _check(lib().gdn_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(state), _ptr(state_indices), state.shape[0], _ptr(o), _stream(dev)))
+    return o

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "gnorm.hip", "conv.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "gnorm.hip", "conv.hip", "recur.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -293,6 +293,50 @@ gdn::ConvParams conv_params(const gdn_conv_problem* p, const ConvPlan& P) {
   return c;
 }
 
+struct RecPlan {
+  int64_t tokens = 0, N = 0;
+  bool varlen = false, bf16 = false;
+};
+
+gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
+  if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (p->heads < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "heads = %lld < 1", (long long)p->heads);
+  if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "dk %lld / dv %lld not in {64, 128}", (long long)p->dk, (long long)p->dv);
+  if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "qk_l2norm = %d is not 0 or 1", (int)p->qk_l2norm);
+  if (p->reserved != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved field is %d, not 0", (int)p->reserved);
+  if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
+  const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
+  if (has_h != has_d)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
+  P->varlen = has_h;
+  P->bf16 = p->dtype == GDN_BF16;
+  if (P->varlen) {
+    if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
+    if (p->num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs = %lld < 1", (long long)p->num_seqs);
+    if (((uintptr_t)p->cu_seqlens_dev) % 4) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_dev misaligned");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d != 0", cu[0]);
+    for (int64_t n = 0; n < p->num_seqs; ++n)
+      if (cu[n + 1] < cu[n])
+        return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %lld (%d -> %d)", (long long)n, cu[n], cu[n + 1]);
+    if (cu[p->num_seqs] != p->seqlen)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens[N] = %d != seqlen %lld", cu[p->num_seqs], (long long)p->seqlen);
+    P->N = p->num_seqs;
+  } else {
+    if (p->batch < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "batch = %lld < 1", (long long)p->batch);
+    P->N = p->batch;
+  }
+  P->tokens = (P->varlen ? 1 : p->batch) * p->seqlen;
+  if (P->tokens * p->heads >= ((int64_t)1 << 31) || P->N * p->heads >= ((int64_t)1 << 31))
+    return fail(GDN_ERR_UNSUPPORTED, "problem too large");
+  return GDN_OK;
+}
+
 size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
   const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, p->dtype == GDN_BF16, true);
   return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)p->dim * sizeof(float));
@@ -455,6 +499,53 @@ gdn_status gdn_causal_conv1d_bwd(const gdn_conv_problem* p, const void* x, const
     return GDN_OK;
   } catch (...) {
     return fail(GDN_ERR_HIP, "unexpected exception in gdn_causal_conv1d_bwd");
+  }
+}
+
+gdn_status gdn_recurrent_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* state_indices, int64_t num_slots, void* o,
+                             void* stream) {
+  try {
+    RecPlan P;
+    gdn_status st = check_recurrent(p, &P);
+    if (st != GDN_OK) return st;
+    if (num_slots < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots < 0");
+    if (!state_indices && num_slots < P.N)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "num_slots %lld < %lld sequences without state_indices",
+                  (long long)num_slots, (long long)P.N);
+    if (state_indices && ((uintptr_t)state_indices) % 4)
+      return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices misaligned");
+    const size_t e = P.bf16 ? 2 : 4;
+    const size_t qb = (size_t)(P.tokens * p->heads * p->dk) * e, vb = (size_t)(P.tokens * p->heads * p->dv) * e;
+    const size_t gb = (size_t)(P.tokens * p->heads) * sizeof(float);
+    const size_t sb = (size_t)num_slots * (size_t)(p->heads * p->dk * p->dv) * sizeof(float);
+    const size_t ib = state_indices ? (size_t)P.N * sizeof(int32_t) : 0;
+    const Range req[] = {{q, qb, "q"}, {k, qb, "k"}, {v, vb, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {o, vb, "o"}, {state, P.N > 0 && num_slots > 0 ? sb : 0, "state"}};
+    const Range outs[] = {{o, vb, "o"}};
+    const Range ins[] = {{q, qb, "q"}, {k, qb, "k"}, {v, vb, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+                         {state, sb, "state"}, {state_indices, ib, "state_indices"}};
+    st = check_ptrs(req, 7, nullptr, 0, outs, 1, ins, 7);
+    if (st != GDN_OK) return st;
+    if (state_indices && overlaps({state_indices, ib, "state_indices"}, {state, sb, "state"}))
+      return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices overlaps state");
+    gdn::RecParams R;
+    std::memset(&R, 0, sizeof(R));
+    R.q = q; R.k = k; R.v = v; R.g = g; R.beta = beta; R.state = state; R.idx = state_indices; R.o = o;
+    R.cu = P.varlen ? p->cu_seqlens_dev : nullptr;
+    R.N = (int)P.N;
+    R.H = (int)p->heads;
+    R.dense_T = P.varlen ? 0 : (int)p->seqlen;
+    R.num_slots = num_slots;
+    R.scale = p->scale;
+    R.norm = p->qk_l2norm;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = timed("recurrent", s, [&] { return gdn::launch_recurrent(R, (int)p->dk, (int)p->dv, P.bf16, s); });
+    if (err != hipSuccess) return hip_fail(err, "recurrent forward launch");
+    return GDN_OK;
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_recurrent_fwd");
   }
 }
 

@@ -127,6 +127,22 @@ hipError_t launch_conv_fwd(const ConvParams& p, bool bf16, hipStream_t s);
 hipError_t launch_conv_bwd(const ConvParams& p, bool bf16, hipStream_t s);
 hipError_t launch_conv_dw(const ConvParams& p, hipStream_t s);
 
+// Recurrent (decoding) forward (recur.hip): the state [num_slots][H][dk][dv]
+// fp32 updated in place; sequence n uses slot idx[n] (or n when idx is null).
+struct RecParams {
+  const void *q, *k, *v;    // [tokens][H][dk], [tokens][H][dk], [tokens][H][dv]
+  const float *g, *beta;    // [tokens][H]
+  float* state;
+  const int32_t* idx;       // device [N] or nullptr
+  void* o;                  // [tokens][H][dv]
+  const int32_t* cu;        // device cu_seqlens or nullptr (dense)
+  int N, H, dense_T;
+  long long num_slots;
+  float scale;
+  int norm;                 // 1: q and k rows L2-normalised
+};
+hipError_t launch_recurrent(const RecParams& p, int dk, int dv, bool bf16, hipStream_t s);
+
 // Grid of the sequential kernels: one wave per (sequence, head, 16-column
 // block), padded so that the column blocks of one (sequence, head) share an
 // XCD (workgroup ids are dealt round-robin over the 8 XCDs).

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 4
+    assert gdn.lib().gdn_abi_version() == 5
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
@@ -314,3 +314,46 @@ def test_conv_varlen_validation_and_workspace():
     big = L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(conv_problem(batch=1, seqlen=1 << 20, channels=6144)))
     assert big == 64 * 6144 * 5 * 4
     assert L.gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(conv_problem(kernel_size=7))) == 0
+
+
+# ---- recurrent (decoding) entry point ------------------------------------------
+
+def call_rec(p, num_slots=4, **over):
+    ptrs = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30), b=FAKE + (4 << 30),
+                st=FAKE + (5 << 30), idx=None, o=FAKE + (7 << 30))
+    ptrs.update(over)
+    P = ctypes.c_void_p
+    st = gdn.lib().gdn_recurrent_fwd(ctypes.byref(p), *(P(ptrs[n]) if ptrs[n] else None for n in
+                                                     ("q", "k", "v", "g", "b", "st", "idx")),
+                                     num_slots, P(ptrs["o"]) if ptrs["o"] else None, None)
+    return st, gdn.last_error_message()
+
+
+REC_CASES = [
+    ("dk96", dict(dk=96, dv=96), {}, gdn.GDN_ERR_UNSUPPORTED, "dk"),
+    ("dv256", dict(dv=256), {}, gdn.GDN_ERR_UNSUPPORTED, "dv"),
+    ("l2norm3", dict(qk_l2norm=3), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "qk_l2norm"),
+    ("null_state", {}, dict(st=0), gdn.GDN_ERR_INVALID_ARGUMENT, "state is NULL"),
+    ("o_aliases_v", {}, dict(o=FAKE + (2 << 30) + 64), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("o_aliases_state", {}, dict(o=FAKE + (5 << 30) + 256), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
+    ("idx_misaligned", {}, dict(idx=FAKE + (6 << 30) + 2), gdn.GDN_ERR_INVALID_ARGUMENT, "state_indices"),
+]
+
+
+@pytest.mark.parametrize("name,pkw,pover,status,msg", REC_CASES, ids=[c[0] for c in REC_CASES])
+def test_recurrent_invalid_arguments(name, pkw, pover, status, msg):
+    p = base_problem(seqlen=3, batch=4, **pkw)
+    st, m = call_rec(p, **pover)
+    assert st == status, (st, m)
+    assert msg in m, m
+
+
+def test_recurrent_slots_and_shapes():
+    # without indices there must be a slot per sequence; dk != dv and any chunk are accepted
+    st, m = call_rec(base_problem(seqlen=1, batch=4), num_slots=3)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "num_slots" in m
+    st, m = call_rec(base_problem(seqlen=1, batch=4), num_slots=-1, idx=FAKE + (6 << 30))
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "num_slots" in m
+    # a valid problem with dk != dv and chunk 32 gets past validation to the overlap check
+    st, m = call_rec(base_problem(seqlen=1, batch=4, dk=128, dv=64, chunk=32), o=FAKE + 64)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps" in m
