@@ -180,6 +180,79 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
     print("copy calibration: %d x %d bytes" % (reps, nbytes), file=sys.stderr)
 
 
+def decode_bench(args):
+    """One step = one recurrent call: N sequences x 1 new token, H=16, d_k=d_v=128, bf16, the
+    fp32 states [N,16,128,128] read and written in place."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs as gi
+    import linear_attention_gated_amd as gdn
+
+    N, H, D = args.decode, 16, 128
+    cfg = gi.Config("decode", N, 1, H, D, D, "bf16", h0_std=0.1)
+    x = gi.make_inputs(cfg, 0)
+    dev = torch.device("cuda:0")
+
+    def t(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    q, k, v = (t(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
+    state = t(x["h0"], torch.float32)
+    L = gdn.lib()
+    for _ in range(args.warmup):
+        gdn.recurrent_fwd(q, k, v, g, beta, state)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        gdn.recurrent_fwd(q, k, v, g, beta, state)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_per_step = 1e3 * el / args.steps
+    # algorithmic bytes: the state both ways, q, k, v read and o written, g and beta
+    byts = N * H * (2 * D * D * 4 + 4 * D * 2 + 8)
+    roofline = None
+    if not args.no_profile_pass:
+        evs = HipEvents(2 * args.steps)
+        L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), args.steps)
+        for _ in range(args.steps):
+            gdn.recurrent_fwd(q, k, v, g, beta, state)
+        torch.cuda.synchronize()
+        cnt = L.gdn_profile_count()
+        L.gdn_profile_events(None, 0)
+        avg_us = 1e3 * sum(evs.elapsed_ms(2 * i, 2 * i + 1) for i in range(cnt)) / cnt
+        evs.close()
+        a_gbs = byts / (avg_us * 1e-6) / 1e9
+        roofline = {"kernel": "recurrent", "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": byts, "units_per_launch": N * H,
+                    "bytes_per_unit": byts // (N * H), "avg_us": round(avg_us, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = min(16, os.cpu_count() or 1)
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], nthreads=nthreads)
+            reps += 1
+            ce = time.perf_counter() - c0
+            if ce >= 5.0 or reps >= 50:
+                break
+        cpu = {"value": reps * N / ce, "unit": "tokens/s", "cores": oracle.threads_used(N, H, nthreads),
+               "kind": "oracle", "sample": "%d complete decode steps of the same workload (fp64 token "
+               "recurrence; %.1f s wall)" % (reps, ce)}
+    out = {
+        "metric": "GDN recurrent decode tokens/s", "value": round(N * args.steps / el, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gdn_decode_N%d_T1_H16_d128_bf16_state_inplace" % N, "N": N, "H": H, "dk": D,
+                   "dv": D, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "sources_sha": sources_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +269,9 @@ def main():
     ap.add_argument("--conv", action="store_true",
                     help="the layer's causal conv1d (K=4, SiLU) on raw q, k, v projections before the "
                          "operator, its backward after; implies --qk-l2norm; not the headline workload")
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="instead: the recurrent (decoding) forward, N sequences of one new token "
+                         "each with their states in place (H=16, d=128, bf16)")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
@@ -204,6 +280,8 @@ def main():
               "would shard across GPUs without any exchange, but no multi-GPU path is built); "
               "got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        return decode_bench(args)
 
     import numpy as np
     import torch
