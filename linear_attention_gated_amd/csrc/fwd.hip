@@ -104,19 +104,30 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   const E* V = reinterpret_cast<const E*>(p.v);
 
   // natural key fragments F(K; s, i) for all row blocks, and this wave's
-  // value columns (used after the solve; their reads overlap it)
+  // value columns (used after the solve; their reads overlap it).  Where the
+  // tiles fit the solver's buffers (not yet in use), K and V are staged
+  // through LDS with 16-byte row-contiguous reads; otherwise each fragment
+  // is read from global memory directly.
   // (raw keys: with normalisation the Gram tiles take both rows' reciprocal
   // norms, and this wave's key columns are scaled once selected)
+  constexpr bool kStage = NatTile<E, D>::BYTES <= 64 * LDA * 4;
   frag_t<E> kf[4][KB], vfw[4];
+  TileStage<E, D, 64 * NW> sk, sv;
+  if constexpr (kStage) {
+    const size_t base = ((size_t)tok0 * H + h) * D, rowstride = (size_t)H * D;
+    sk.load(K + base, rowstride, L, tid);
+    sv.load(V + base, rowstride, L, tid);
+  } else {
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    const int row = 16 * sb + li;
+    for (int sb = 0; sb < 4; ++sb) {
+      const int row = 16 * sb + li;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
-                           : zero_frag<E>();
-    vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
-                      : zero_frag<E>();
+      for (int kb = 0; kb < KB; ++kb)
+        kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
+                             : zero_frag<E>();
+      vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
+                        : zero_frag<E>();
+    }
   }
   // chunk-local cumulative log decay (read after the key and value reads are
   // in flight); padded rows get g = 0, beta = 0
@@ -130,6 +141,21 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
     s_gam[lane] = gam;
     s_beta[lane] = bv;
     p.gamma[(size_t)ch * 64 + lane] = gam;
+  }
+  if constexpr (kStage) {
+    char* tK = reinterpret_cast<char*>(sT);
+    char* tV = reinterpret_cast<char*>(sA);
+    sk.store(tK, tid);
+    sv.store(tV, tid);
+    __syncthreads();
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[sb][kb] = tile_frag<E, D>(tK, sb, kb, li, lg);
+      vfw[sb] = tile_frag<E, D>(tV, sb, w, li, lg);
+    }
+    // (the barrier below also keeps sA and sT from being rewritten while
+    // other waves still read their fragments)
   }
   if constexpr (NORM) {
     // sign-encoded reciprocal key norms; every wave holds whole rows, wave 0
