@@ -88,12 +88,12 @@ def sources_sha():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel):
+def traffic_for(kernel, summary="hbm_traffic_fwdbwd_T4096_H16_d128_bf16.txt"):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE from rocprofv3
     counter runs, scaled by a plain device copy of known size), read from the
-    committed summary; None if there is none or the kernel sources changed
-    since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_fwdbwd_T4096_H16_d128_bf16.txt")
+    committed summary of the workload; None if there is none or the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary)
     try:
         lines = open(path).read().splitlines()
     except OSError:
@@ -225,9 +225,12 @@ def decode_bench(args):
         evs.close()
         a_gbs = byts / (avg_us * 1e-6) / 1e9
         roofline = {"kernel": "recurrent", "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": traffic_for("recurrent", "hbm_traffic_decode_N%d_T1_H16_d128_bf16.txt" % N),
                     "algorithmic_bytes_per_launch": byts, "units_per_launch": N * H,
                     "bytes_per_unit": byts // (N * H), "avg_us": round(avg_us, 2)}
+    if args.copy_calib:
+        copy_calibration(torch, dev)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
