@@ -23,6 +23,10 @@
  *   v, o, do, dv : [B][T][H][d_v]      dtype of the problem
  *   g, beta, dg, dbeta : [B][T][H]     fp32 (g is the natural-log decay)
  *   h0, ht, dht, dh0   : [N][H][d_k][d_v] fp32
+ * With qkv_token_stride = s > 0, q, k, v, dq, dk, dv instead advance by s
+ * elements per token ([B*T][s] buffers in which each occupies H*d columns);
+ * o and do stay as above.  Interleaved outputs dq, dk, dv are allowed as long
+ * as no element is shared.
  * Dense problems have N = B sequences of T tokens each.  Packed
  * variable-length problems have B = 1, T = total tokens and N sequences
  * given by cu_seqlens (int32, N+1 entries, cu[0] = 0, non-decreasing,
@@ -68,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
   GDN_OK = 0,
@@ -97,7 +101,12 @@ typedef struct {
                       /* of q and of k is divided by max(||row||_2, 1e-12) inside  */
                       /* the operator (rounded to the problem dtype), and dq, dk   */
                       /* are the gradients with respect to the raw rows.           */
-  int32_t reserved;   /* must be 0                                                 */
+  int32_t qkv_token_stride;  /* 0: q, k, dq, dk hold H*dk and v, dv H*dv elements  */
+                             /* per token (contiguous).  > 0: all six advance by   */
+                             /* this many elements per token (slices of one        */
+                             /* [tokens][stride] buffer such as a conv1d output);  */
+                             /* >= H*max(dk, dv), a multiple of 8 (bf16) or 4      */
+                             /* (fp32); o and do stay contiguous                   */
 } gdn_problem;
 
 /* GDN_ABI_VERSION of the loaded library. */

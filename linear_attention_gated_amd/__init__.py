@@ -43,7 +43,7 @@ class GdnProblem(ctypes.Structure):
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int64),
                 ("num_seqs", ctypes.c_int64), ("cu_seqlens_host", ctypes.c_void_p),
                 ("cu_seqlens_dev", ctypes.c_void_p), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int), ("qk_l2norm", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("dtype", ctypes.c_int), ("qk_l2norm", ctypes.c_int32), ("qkv_token_stride", ctypes.c_int32)]
 
 
 class GdnGatedNormProblem(ctypes.Structure):
@@ -154,7 +154,8 @@ def _cu_pair(cu_seqlens, device):
     return host, dev
 
 
-def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0, qk_l2norm=False) -> GdnProblem:
+def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0, qk_l2norm=False,
+                 qkv_token_stride=0) -> GdnProblem:
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     p = GdnProblem()
@@ -165,7 +166,7 @@ def make_problem(q, v, heads=None, cu_host=None, cu_dev=None, scale=1.0, qk_l2no
     p.scale = float(scale)
     p.dtype = _dtype_code(q.dtype)
     p.qk_l2norm = 1 if qk_l2norm else 0
-    p.reserved = 0
+    p.qkv_token_stride = int(qkv_token_stride)
     return p
 
 
@@ -177,7 +178,41 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _require(t, name, dtype, device):
+def _qkv_stride(tensors, names, dtype, device):
+    """0 when q, k, v (or their like) are all contiguous; otherwise their common token
+    stride in elements: [B, T, H, d] views whose tokens are s elements apart (slices of
+    one [B, T, s] buffer, e.g. a conv1d output)."""
+    for t, n in zip(tensors, names):
+        _require(t, n, dtype, device, contiguous=False)
+    if all(t.is_contiguous() for t in tensors):
+        return 0
+    s = None
+    for t, n in zip(tensors, names):
+        B, T, H, d = t.shape
+        st = t.stride()
+        if st[3] != 1 or st[2] != d or (B > 1 and st[0] != T * st[1]):
+            raise ValueError("%s: a [B,T,H,d] view with rows of H*d elements, tokens evenly spaced, "
+                             "is needed (strides %r)" % (n, st))
+        if s is None:
+            s = st[1]
+        elif st[1] != s:
+            raise ValueError("q, k and v must share one token stride (%s has %d, expected %d)" % (n, st[1], s))
+    return s
+
+
+def _like_layout(tensors):
+    """Empty tensors laid out like `tensors` (views of one storage with equal strides):
+    one new buffer of the same size, viewed at the same offsets."""
+    base = tensors[0]
+    st = base.untyped_storage()
+    for t in tensors[1:]:
+        if t.untyped_storage().data_ptr() != st.data_ptr():
+            raise ValueError("strided q, k, v must be views of one buffer")
+    buf = torch.empty(st.nbytes() // base.element_size(), dtype=base.dtype, device=base.device)
+    return [buf.as_strided(t.shape, t.stride(), t.storage_offset()) for t in tensors]
+
+
+def _require(t, name, dtype, device, contiguous=True):
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -186,7 +221,7 @@ def _require(t, name, dtype, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
     if t.dtype != dtype:
         raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return t
 
@@ -206,13 +241,12 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
     the rows of q and k are L2-normalised inside the operator."""
     dev = q.device
     dt = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, dt, dev)
+    ld = _qkv_stride((q, k, v), ("q", "k", "v"), dt, dev)
     _require(g, "g", torch.float32, dev)
     _require(beta, "beta", torch.float32, dev)
     _require(initial_state, "initial_state", torch.float32, dev)
     cu_h, cu_d = _cu_pair(cu_seqlens, dev)
-    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm, qkv_token_stride=ld)
     L = lib()
     nbytes = L.gdn_fwd_workspace_bytes(ctypes.byref(p))
     if nbytes == 0:
@@ -229,7 +263,7 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
                      _ptr(initial_state), _ptr(o), _ptr(ht), _ptr(workspace), nbytes, _stream(dev)))
     if return_context:
         key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
-               float(scale), bool(qk_l2norm))
+               float(scale), bool(qk_l2norm), ld)
         return o, ht, Context(workspace, key)
     return o, ht
 
@@ -241,17 +275,17 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
     return_context=True)`` on the same inputs, the forward is not recomputed."""
     dev = q.device
     dt = q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
-        _require(t, name, dt, dev)
+    ld = _qkv_stride((q, k, v), ("q", "k", "v"), dt, dev)
+    _require(do, "do", dt, dev)
     _require(g, "g", torch.float32, dev)
     _require(beta, "beta", torch.float32, dev)
     _require(initial_state, "initial_state", torch.float32, dev)
     _require(dht, "dht", torch.float32, dev)
     cu_h, cu_d = _cu_pair(cu_seqlens, dev)
-    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm, qkv_token_stride=ld)
     if context is not None:
         key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
-               float(scale), bool(qk_l2norm))
+               float(scale), bool(qk_l2norm), ld)
         if key != context.problem_key:
             raise ValueError("context was computed for a different problem")
     L = lib()
@@ -262,9 +296,13 @@ def bwd(q, k, v, g, beta, do, initial_state=None, dht=None, cu_seqlens=None, sca
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     N = _num_seqs(q, cu_h)
     B, T, H, dk = q.shape
-    dq = torch.empty_like(q)
-    dk_ = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    if ld:
+        # gradients laid out like the inputs: views of one new buffer
+        dq, dk_, dv = _like_layout((q, k, v))
+    else:
+        dq = torch.empty_like(q)
+        dk_ = torch.empty_like(k)
+        dv = torch.empty_like(v)
     dg = torch.empty_like(g)
     dbeta = torch.empty_like(beta)
     dh0 = torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32, device=dev) if need_dh0 else None
@@ -400,14 +438,13 @@ def recurrent_fwd(q, k, v, g, beta, state, state_indices=None, cu_seqlens=None, 
     q, k [B, T, H, dk], v [B, T, H, dv] (B = 1 with cu_seqlens); dk and dv may differ.
     Returns o [B, T, H, dv]."""
     dev, dt = q.device, q.dtype
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, dt, dev)
+    ld = _qkv_stride((q, k, v), ("q", "k", "v"), dt, dev)
     _require(g, "g", torch.float32, dev)
     _require(beta, "beta", torch.float32, dev)
     _require(state, "state", torch.float32, dev)
     _require(state_indices, "state_indices", torch.int32, dev)
     cu_h, cu_d = _cu_pair(cu_seqlens, dev)
-    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm, qkv_token_stride=ld)
     o = torch.empty(v.shape, dtype=dt, device=dev)
     _check(lib().gdn_recurrent_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(state), _ptr(state_indices), state.shape[0], _ptr(o), _stream(dev)))

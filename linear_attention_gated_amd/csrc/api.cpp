@@ -66,10 +66,51 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// Token stride (elements) of q, k, v and their gradients: 0 means contiguous.
+gdn_status check_stride(const gdn_problem* p) {
+  const int64_t s = p->qkv_token_stride;
+  if (s == 0) return GDN_OK;
+  const int64_t wmax = p->heads * (p->dk > p->dv ? p->dk : p->dv);
+  const int64_t mult = p->dtype == GDN_BF16 ? 8 : 4;
+  if (s < 0 || s < wmax)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride %lld < H * max(dk, dv) = %lld", (long long)s, (long long)wmax);
+  if (s % mult) return fail(GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride %lld is not a multiple of %lld", (long long)s, (long long)mult);
+  return GDN_OK;
+}
+
+// Memory of a [tokens][width] tensor whose tokens are `stride` elements apart
+// (bytes from p): rows [p + t * stride * esz, + width * esz).
+struct Strided {
+  const void* p;
+  int64_t tokens, width, stride;   // elements
+  size_t esz;
+  const char* name;
+  size_t span() const { return tokens > 0 ? (size_t)((tokens - 1) * stride + width) * esz : 0; }
+};
+
+// Do two tensors share a byte?  Same stride: some rows r1, r2 of A and B
+// intersect, i.e. -wb < d + k * S < wa for d = pB - pA and some k = r2 - r1
+// with |k| < tokens; otherwise (or for contiguous tensors) by their spans.
+bool strided_overlap(const Strided& a, const Strided& b) {
+  if (!a.p || !b.p || a.span() == 0 || b.span() == 0) return false;
+  const long long pa = (long long)(uintptr_t)a.p, pb = (long long)(uintptr_t)b.p;
+  const long long wa = a.width * (long long)a.esz, wb = b.width * (long long)b.esz;
+  if (a.stride == b.stride && a.esz == b.esz && a.stride > a.width && b.stride > b.width && a.tokens == b.tokens) {
+    const long long S = a.stride * (long long)a.esz, d = pb - pa, T = a.tokens;
+    // integers k with (-wb - d) / S < k < (wa - d) / S
+    auto fdiv = [](long long x, long long y) { return x / y - ((x % y != 0) && ((x < 0) != (y < 0))); };
+    const long long klo = fdiv(-wb - d, S) + 1, khi = -fdiv(-(wa - d), S) - 1;
+    const long long lo = klo > -(T - 1) ? klo : -(T - 1), hi = khi < T - 1 ? khi : T - 1;
+    return lo <= hi;
+  }
+  return pa < pb + (long long)b.span() && pb < pa + (long long)a.span();
+}
+
 struct Layout {
   int64_t B = 0, T = 0, H = 0, D = 0, N = 0, NC = 0, tokens = 0;
   bool varlen = false, bf16 = false, l2norm = false;
   size_t esz = 0;
+  int64_t ld = 0;   // token stride (elements) of q, k, v and their gradients
   // byte offsets into a workspace
   size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0, Tm = 0;
   size_t qinv = 0, kinv = 0;
@@ -91,8 +132,11 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "qk_l2norm = %d is not 0 or 1", (int)p->qk_l2norm);
-  if (p->reserved != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved field is %d, not 0", (int)p->reserved);
   if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
+  {
+    gdn_status st = check_stride(p);
+    if (st != GDN_OK) return st;
+  }
   const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
   if (has_h != has_d)
     return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
@@ -103,6 +147,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->bf16 = p->dtype == GDN_BF16;
   L->l2norm = p->qk_l2norm == 1;
   L->esz = L->bf16 ? 2 : 4;
+  L->ld = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dk;
   const int64_t maxtok = (int64_t)1 << 31;
   if (L->varlen) {
     if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
@@ -158,14 +203,30 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   return GDN_OK;
 }
 
+// A buffer: n bytes from p, or, with a token stride, `tokens` rows of `width`
+// elements `stride` elements apart (n is then the span).
 struct Range {
   const void* p;
   size_t n;
   const char* name;
+  int64_t tokens = 0, width = 0, stride = 0;
+  size_t esz = 0;
 };
+
+Range strided(const void* p, int64_t tokens, int64_t width, int64_t stride, size_t esz, const char* name) {
+  Range r{p, tokens > 0 ? (size_t)((tokens - 1) * stride + width) * esz : 0, name};
+  r.tokens = tokens;
+  r.width = width;
+  r.stride = stride;
+  r.esz = esz;
+  return r;
+}
 
 bool overlaps(const Range& a, const Range& b) {
   if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  if (a.stride && b.stride)
+    return strided_overlap({a.p, a.tokens, a.width, a.stride, a.esz, a.name},
+                           {b.p, b.tokens, b.width, b.stride, b.esz, b.name});
   const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
   return a0 < b0 + b.n && b0 < a0 + a.n;
 }
@@ -211,6 +272,7 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Vf = ws + L.Vf;
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
   P.qk_l2norm = L.l2norm ? 1 : 0;
+  P.ldx = L.ld;
   if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
   return P;
 }
@@ -308,8 +370,11 @@ gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
     return fail(GDN_ERR_INVALID_ARGUMENT, "qk_l2norm = %d is not 0 or 1", (int)p->qk_l2norm);
-  if (p->reserved != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "reserved field is %d, not 0", (int)p->reserved);
   if (p->seqlen < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "seqlen < 0");
+  {
+    gdn_status st = check_stride(p);
+    if (st != GDN_OK) return st;
+  }
   const bool has_h = p->cu_seqlens_host != nullptr, has_d = p->cu_seqlens_dev != nullptr;
   if (has_h != has_d)
     return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
@@ -517,14 +582,18 @@ gdn_status gdn_recurrent_fwd(const gdn_problem* p, const void* q, const void* k,
     if (state_indices && ((uintptr_t)state_indices) % 4)
       return fail(GDN_ERR_INVALID_ARGUMENT, "state_indices misaligned");
     const size_t e = P.bf16 ? 2 : 4;
-    const size_t qb = (size_t)(P.tokens * p->heads * p->dk) * e, vb = (size_t)(P.tokens * p->heads * p->dv) * e;
+    const size_t vb = (size_t)(P.tokens * p->heads * p->dv) * e;
     const size_t gb = (size_t)(P.tokens * p->heads) * sizeof(float);
     const size_t sb = (size_t)num_slots * (size_t)(p->heads * p->dk * p->dv) * sizeof(float);
     const size_t ib = state_indices ? (size_t)P.N * sizeof(int32_t) : 0;
-    const Range req[] = {{q, qb, "q"}, {k, qb, "k"}, {v, vb, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+    const int64_t ldq = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dk;
+    const int64_t ldv = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dv;
+    const Range rq = strided(q, P.tokens, p->heads * p->dk, ldq, e, "q"), rk = strided(k, P.tokens, p->heads * p->dk, ldq, e, "k"),
+                rv = strided(v, P.tokens, p->heads * p->dv, ldv, e, "v");
+    const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
                          {o, vb, "o"}, {state, P.N > 0 && num_slots > 0 ? sb : 0, "state"}};
     const Range outs[] = {{o, vb, "o"}};
-    const Range ins[] = {{q, qb, "q"}, {k, qb, "k"}, {v, vb, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+    const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
                          {state, sb, "state"}, {state_indices, ib, "state_indices"}};
     st = check_ptrs(req, 7, nullptr, 0, outs, 1, ins, 7);
     if (st != GDN_OK) return st;
@@ -540,6 +609,8 @@ gdn_status gdn_recurrent_fwd(const gdn_problem* p, const void* q, const void* k,
     R.num_slots = num_slots;
     R.scale = p->scale;
     R.norm = p->qk_l2norm;
+    R.ldq = ldq;
+    R.ldv = ldv;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t err = timed("recurrent", s, [&] { return gdn::launch_recurrent(R, (int)p->dk, (int)p->dv, P.bf16, s); });
     if (err != hipSuccess) return hip_fail(err, "recurrent forward launch");
@@ -598,12 +669,13 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
     const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
     const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
-    const Range req[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+    const Range rq = strided(q, L.tokens, L.H * L.D, L.ld, L.esz, "q"), rk = strided(k, L.tokens, L.H * L.D, L.ld, L.esz, "k"),
+                rv = strided(v, L.tokens, L.H * L.D, L.ld, L.esz, "v");
+    const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
                          {o, qk, "o"}, {workspace, L.fwd_bytes, "workspace"}};
     const Range opt[] = {{h0, sb, "h0"}, {ht, sb, "ht"}};
     const Range outs[] = {{o, qk, "o"}, {ht, sb, "ht"}, {workspace, L.fwd_bytes, "workspace"}};
-    const Range ins[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
-                         {h0, sb, "h0"}};
+    const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {h0, sb, "h0"}};
     st = check_ptrs(req, 7, opt, 2, outs, 3, ins, 6);
     if (st != GDN_OK) return st;
     if (workspace && ((uintptr_t)workspace) % ALIGN)
@@ -639,14 +711,17 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
     const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
     const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
-    const Range req[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
-                         {d_o, qk, "do"}, {dq, qk, "dq"}, {dk, qk, "dk"}, {dv, qk, "dv"}, {dg, gb, "dg"},
+    auto st_ = [&](const void* x, const char* nm) { return strided(x, L.tokens, L.H * L.D, L.ld, L.esz, nm); };
+    const Range rq = st_(q, "q"), rk = st_(k, "k"), rv = st_(v, "v"), rdq = st_(dq, "dq"), rdk = st_(dk, "dk"),
+                rdv = st_(dv, "dv");
+    const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
+                         {d_o, qk, "do"}, rdq, rdk, rdv, {dg, gb, "dg"},
                          {dbeta, gb, "dbeta"}, {workspace, L.bwd_bytes, "workspace"}};
     const Range opt[] = {{h0, sb, "h0"}, {dht, sb, "dht"}, {dh0, sb, "dh0"},
                          {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
-    const Range outs[] = {{dq, qk, "dq"}, {dk, qk, "dk"}, {dv, qk, "dv"}, {dg, gb, "dg"}, {dbeta, gb, "dbeta"},
+    const Range outs[] = {rdq, rdk, rdv, {dg, gb, "dg"}, {dbeta, gb, "dbeta"},
                           {dh0, sb, "dh0"}, {workspace, L.bwd_bytes, "workspace"}};
-    const Range ins[] = {{q, qk, "q"}, {k, qk, "k"}, {v, qk, "v"}, {g, gb, "g"}, {beta, gb, "beta"},
+    const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
                          {h0, sb, "h0"}, {d_o, qk, "do"}, {dht, sb, "dht"},
                          {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
     st = check_ptrs(req, 12, opt, 4, outs, 7, ins, 9);

@@ -109,8 +109,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   {
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    // q, k: token stride ldx; dO: contiguous
+    const size_t xbase = (size_t)tok0 * p.ldx + (size_t)h * D;
+    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldx, L, tid);
+    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldx, L, tid, NORM ? p.kinv + nb : nullptr, H);
     so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
@@ -481,17 +483,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   const E* HPf = reinterpret_cast<const E*>(p.HPf);
   const E* dVf = reinterpret_cast<const E*>(p.dVf);
   const float sc = p.scale;
+  // q, k, v and their gradients: token stride ldx; dO: contiguous
   const size_t rowstride = (size_t)H * D;
   const size_t base = ((size_t)tok0 * H + h) * D;
+  const size_t xrow = (size_t)p.ldx;
+  const size_t xbase = (size_t)tok0 * xrow + (size_t)h * D;
 
-  auto gnat = [&](const E* X, int row, int kb) {
-    return row < L ? load_frag_row<E>(X + base + (size_t)row * rowstride + 32 * kb, lg) : zero_frag<E>();
+  auto gnat = [&](const E* X, size_t xb, size_t xr, int row, int kb) {
+    return row < L ? load_frag_row<E>(X + xb + (size_t)row * xr + 32 * kb, lg) : zero_frag<E>();
   };
   auto qf = [&](int ab, int kb) { return tile_frag<E, D>(tQ, ab, kb, li, lg); };
   auto kf = [&](int ab, int kb) { return tile_frag<E, D>(tK, ab, kb, li, lg); };
   auto of = [&](int ab, int kb) {
     if constexpr (S::kStageDO) return tile_frag<E, D>(tO, ab, kb, li, lg);
-    else return gnat(dO, 16 * ab + li, kb);
+    else return gnat(dO, base, rowstride, 16 * ab + li, kb);
   };
   // fp32 LDS matrix fragments: index rows 16ab.., contraction cols 32kb..
   auto mfrag32 = [&](const float* M, int ab, int kb) {
@@ -556,8 +561,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(Q + base, rowstride, L, tid, NORM ? p.qinv + nb : nullptr, H);
-    sk.load(K + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H);
+    sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H);
     if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
     // T = (I + diag(beta) A')^-1 as the forward solved it
     constexpr int TPER = 64 * 16 / NT;
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
     const int sbt = t - rbt * (rbt + 1) / 2;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, 16 * sbt + li, kb) : zero_frag<E>();
+    for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, xbase, xrow, 16 * sbt + li, kb) : zero_frag<E>();
   }
   __syncthreads();
 
@@ -859,7 +864,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // operands of the output phase that come from global memory
   frag_t<E> vw[4];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, 16 * sb + li, kw);
+  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, xbase, xrow, 16 * sb + li, kw);
   __syncthreads();
 
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = ir > 0.f ? (dy[rb][q] - yn[rb][q] * yd) * ir : -dy[rb][q] * ir;
-      if (r < L) *reinterpret_cast<quad_t<E>*>(dst + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(o);
+      if (r < L) *reinterpret_cast<quad_t<E>*>(dst + xbase + (size_t)r * xrow + 16 * w + 4 * lg) = to_quad<E>(o);
     }
   };
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
@@ -942,7 +947,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dqh[rb] = acc;
         qn4[rb] = qn;
       } else if (r < L) {
-        *reinterpret_cast<quad_t<E>*>(dQ + base + (size_t)r * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+        *reinterpret_cast<quad_t<E>*>(dQ + xbase + (size_t)r * xrow + 16 * w + 4 * lg) = to_quad<E>(acc);
       }
     }
     if constexpr (norm) {
@@ -1006,7 +1011,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dkh[sb] = acc;
         kn4[sb] = kn;
       } else if (s_ < L) {
-        *reinterpret_cast<quad_t<E>*>(dK + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(acc);
+        *reinterpret_cast<quad_t<E>*>(dK + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg) = to_quad<E>(acc);
       }
     }
     csum = sum_in_group(csum);
@@ -1037,7 +1042,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       dot = sum_groups(dot);
       add_col(dbc, sb, dot);
       if (s_ < L)
-        *reinterpret_cast<quad_t<E>*>(dV + base + (size_t)s_ * rowstride + 16 * w + 4 * lg) = to_quad<E>(scale4(acc[sb], bs));
+        *reinterpret_cast<quad_t<E>*>(dV + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg) = to_quad<E>(scale4(acc[sb], bs));
     }
   }
   {

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   frag_t<E> kf[4][KB], vfw[4];
   TileStage<E, D, 64 * NW> sk, sv;
   if constexpr (kStage) {
-    const size_t base = ((size_t)tok0 * H + h) * D, rowstride = (size_t)H * D;
+    const size_t base = (size_t)tok0 * p.ldx + (size_t)h * D, rowstride = (size_t)p.ldx;
     sk.load(K + base, rowstride, L, tid);
     sv.load(V + base, rowstride, L, tid);
   } else {
@@ -123,9 +123,9 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
       const int row = 16 * sb + li;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        kf[sb][kb] = row < L ? load_frag_row<E>(K + ((size_t)(tok0 + row) * H + h) * D + 32 * kb, lg)
+        kf[sb][kb] = row < L ? load_frag_row<E>(K + (size_t)(tok0 + row) * p.ldx + (size_t)h * D + 32 * kb, lg)
                              : zero_frag<E>();
-      vfw[sb] = row < L ? load_frag_row<E>(V + ((size_t)(tok0 + row) * H + h) * D + 32 * w, lg)
+      vfw[sb] = row < L ? load_frag_row<E>(V + (size_t)(tok0 + row) * p.ldx + (size_t)h * D + 32 * w, lg)
                         : zero_frag<E>();
     }
   }
@@ -540,8 +540,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   {
     TileStage<E, D, NT> sq, sk;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(reinterpret_cast<const E*>(p.q) + base, rowstride, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + base, rowstride, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    // q, k: token stride ldx (the output keeps the contiguous layout)
+    const size_t xbase = (size_t)tok0 * p.ldx + (size_t)h * D;
+    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldx, L, tid);
+    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldx, L, tid, NORM ? p.kinv + nb : nullptr, H);
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll

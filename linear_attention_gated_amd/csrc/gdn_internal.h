@@ -54,6 +54,7 @@ struct Params {
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
   float* Tm;
   int qk_l2norm;          // 1: q and k rows L2-normalised inside the operator
+  long long ldx;          // token stride (elements) of q, k, v, dq, dk, dv
   float* kinv;            // reciprocal key norms [tokens][H] (forward context), sign-encoded
   float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;
@@ -140,6 +141,7 @@ struct RecParams {
   long long num_slots;
   float scale;
   int norm;                 // 1: q and k rows L2-normalised
+  long long ldq, ldv;       // token strides (elements) of q, k and of v
 };
 hipError_t launch_recurrent(const RecParams& p, int dk, int dv, bool bf16, hipStream_t s);
 

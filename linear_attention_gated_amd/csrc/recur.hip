@@ -59,12 +59,12 @@ __global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
   for (long long t = t0; t < t1; ++t) {
     const size_t th = (size_t)t * p.H + hh;
     for (int i = j; i < DK; i += DV) {
-      sq[i] = ld<E>(p.q, th * DK + i);
-      sk[i] = ld<E>(p.k, th * DK + i);
+      sq[i] = ld<E>(p.q, (size_t)t * p.ldq + (size_t)hh * DK + i);
+      sk[i] = ld<E>(p.k, (size_t)t * p.ldq + (size_t)hh * DK + i);
     }
     const float a = __expf(p.g[th]);
     const float b = p.beta[th];
-    const float vj = ld<E>(p.v, th * DV + j);
+    const float vj = ld<E>(p.v, (size_t)t * p.ldv + (size_t)hh * DV + j);
     __syncthreads();
     float iq = 1.f, ik = 1.f;
     if constexpr (NORM) {

@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 5
+    assert gdn.lib().gdn_abi_version() == 6
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
@@ -120,7 +120,9 @@ CASES = [
     ("o_aliases_q", {}, dict(o=FAKE), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
     ("ht_aliases_h0", {}, dict(ht="h0"), gdn.GDN_ERR_INVALID_ARGUMENT, "overlaps"),
     ("l2norm_2", dict(qk_l2norm=2), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "qk_l2norm"),
-    ("reserved_1", dict(reserved=1), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "reserved"),
+    ("stride_small", dict(qkv_token_stride=64), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride"),
+    ("stride_odd", dict(qkv_token_stride=3 * 2 * 64 + 4), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "multiple"),
+    ("stride_neg", dict(qkv_token_stride=-8), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride"),
 ]
 
 
@@ -357,3 +359,43 @@ def test_recurrent_slots_and_shapes():
     # a valid problem with dk != dv and chunk 32 gets past validation to the overlap check
     st, m = call_rec(base_problem(seqlen=1, batch=4, dk=128, dv=64, chunk=32), o=FAKE + 64)
     assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps" in m
+
+
+# ---- token-strided q, k, v and gradients ------------------------------------
+
+def _bwd_strided(dq_off, dk_off, dv_off, ws_short=True):
+    # q, k, v interleaved in one [T][3*H*d] buffer A, dq, dk, dv in buffer Bf at the given byte offsets
+    p = base_problem(qkv_token_stride=3 * 2 * 64)
+    A, Bf = FAKE, FAKE + (1 << 34)
+    P = ctypes.c_void_p
+    ptrs = [A, A + 256, A + 512, FAKE + (2 << 30), FAKE + (3 << 30), None, FAKE + (4 << 30), None,
+            Bf + dq_off, Bf + dk_off, Bf + dv_off, FAKE + (5 << 30), FAKE + (6 << 30), None, None]
+    need = gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(p))
+    st = gdn.lib().gdn_bwd(ctypes.byref(p), *(P(x) if x else None for x in ptrs), P(FAKE + (1 << 38)),
+                           need - 256 if ws_short else need, None)
+    return st, gdn.last_error_message()
+
+
+def test_strided_interleaved_outputs_are_accepted():
+    # dq, dk, dv side by side in each token row share no element: the checks pass (and the
+    # call then stops at the short workspace, before any launch)
+    st, m = _bwd_strided(0, 256, 512)
+    assert st == gdn.GDN_ERR_WORKSPACE_TOO_SMALL, m
+
+
+@pytest.mark.parametrize("offs", [(0, 128, 512), (0, 256, 256 + 3 * 2 * 64 * 2 + 64), (512, 256, 608)])
+def test_strided_overlapping_outputs_are_rejected(offs):
+    st, m = _bwd_strided(*offs)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlap" in m, (offs, m)
+
+
+def test_strided_output_over_an_input_is_rejected():
+    p = base_problem(qkv_token_stride=3 * 2 * 64)
+    P = ctypes.c_void_p
+    A = FAKE
+    # dq placed in the gap of buffer A that k occupies
+    ptrs = [A, A + 256, A + 512, FAKE + (2 << 30), FAKE + (3 << 30), None, FAKE + (4 << 30), None,
+            A + 256, FAKE + (8 << 30), FAKE + (9 << 30), FAKE + (5 << 30), FAKE + (6 << 30), None, None]
+    st = gdn.lib().gdn_bwd(ctypes.byref(p), *(P(x) if x else None for x in ptrs), P(FAKE + (1 << 38)),
+                           1, None)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps k" in gdn.last_error_message()
