@@ -53,10 +53,10 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
         "gnorm_fwd": 3 * C * D * E,
         # reads x, z, dy; writes dx, dz (the dw partials are per workgroup, not counted)
         "gnorm_bwd": 5 * C * D * E,
-        # causal conv1d on one of q, k, v (one head's D channels per unit): reads x, writes y
-        "conv_fwd": 2 * C * D * E,
+        # causal conv1d on q, k, v side by side (three heads' D channels per unit): reads x, writes y
+        "conv_fwd": 3 * 2 * C * D * E,
         # reads x, dy; writes dx (the dw/dbias partials are per workgroup, not counted)
-        "conv_bwd": 3 * C * D * E,
+        "conv_bwd": 3 * 3 * C * D * E,
     }
     out = {k: v * units for k, v in per_unit.items()}
     if with_ht:
@@ -112,6 +112,8 @@ def traffic_for(kernel, summary="hbm_traffic_fwdbwd_T4096_H16_d128_bf16.txt"):
 
 
 def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
+    import numpy as np
+
     import oracle
     nthreads = min(16, os.cpu_count() or 1)
     used = oracle.threads_used(x["N"], x["H"], nthreads)
@@ -120,7 +122,9 @@ def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
     while True:
         qkv = [x["q"], x["k"], x["v"]]
         if cv is not None:
-            qkv = [oracle.causal_conv1d_fwd(c["x"], c["w"]).reshape(x["q"].shape) for c in cv]
+            y = oracle.causal_conv1d_fwd(cv["x"], cv["w"])
+            w_ = x["q"].shape[2] * x["q"].shape[3]
+            qkv = [y[..., i * w_:(i + 1) * w_].reshape(x["q"].shape) for i in range(3)]
         o, _ = oracle.fwd(*qkv, x["g"], x["beta"], nthreads=nthreads, qk_l2norm=l2)
         do = x["do"]
         if gn is not None:
@@ -128,16 +132,18 @@ def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
             do = oracle.gated_rmsnorm_bwd(o, gn["z"].reshape(o.shape), gn["w"], gn["dy"].reshape(o.shape))[0]
         grads = oracle.bwd(*qkv, x["g"], x["beta"], do, nthreads=nthreads, qk_l2norm=l2)
         if cv is not None:
-            for c, gq in zip(cv, grads[:3]):
-                oracle.causal_conv1d_bwd(c["x"], c["w"], gq.reshape(c["x"].shape))
+            dqkv = np.concatenate([gq.reshape(cv["x"].shape[:2] + (-1,)) for gq in grads[:3]], axis=-1)
+            oracle.causal_conv1d_bwd(cv["x"], cv["w"], dqkv)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= max_reps:
             break
     tokens = x["B"] * x["T"]
     return {"value": reps * tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "%d complete fwd+bwd passes of the B=1,T=4096,H=16,d=128 workload "
-                      "(fp64 token recurrence; %.1f s wall)" % (reps, el)}
+            "sample": "%d complete fwd+bwd passes of the B=1,T=4096,H=16,d=128 workload%s%s "
+                      "(fp64 token recurrence; %.1f s wall)"
+                      % (reps, " with the conv1d" if cv is not None else "",
+                         " with the gated RMSNorm" if gn is not None else "", el)}
 
 
 class HipEvents:
@@ -308,11 +314,12 @@ def main():
     g, beta = t(x["g"], torch.float32), t(x["beta"], torch.float32)
     cv = None
     if args.conv:
-        # raw projections of q, k, v, each [B, T, H*D] channels last, and their conv weights
-        cv = [gi.make_conv_inputs(B, T, H * D, 4, "bf16", seed=20 + i) for i in range(3)]
-        cvx = [t(c["x"], torch.bfloat16) for c in cv]
-        cvw = [t(c["w"], torch.float32) for c in cv]
-        pc = gdn.make_conv_problem(cvx[0], 4)
+        # raw projections of q, k, v side by side, [B, T, 3*H*D] channels last, and the conv
+        # weights; one conv call covers all three, the operator reads slices of its output
+        cv = gi.make_conv_inputs(B, T, 3 * H * D, 4, "bf16", seed=20)
+        cvx = t(cv["x"], torch.bfloat16)
+        cvw = t(cv["w"], torch.float32)
+        pc = gdn.make_conv_problem(cvx, 4)
         wsc = torch.empty(gdn.lib().gdn_causal_conv1d_bwd_workspace_bytes(ctypes.byref(pc)), dtype=torch.uint8,
                           device=dev)
     gn = None
@@ -334,7 +341,8 @@ def main():
     def step():
         qq, kk, vv = q, k, v
         if cv is not None:
-            qq, kk, vv = (gdn.causal_conv1d_fwd(xx, ww).view(B, T, H, D) for xx, ww in zip(cvx, cvw))
+            y = gdn.causal_conv1d_fwd(cvx, cvw)
+            qq, kk, vv = (y[..., i * H * D:(i + 1) * H * D].view(B, T, H, D) for i in range(3))
         o, ht, ctx = gdn.fwd(qq, kk, vv, g, beta, return_context=True, workspace=wsf, qk_l2norm=l2)
         dO = do
         if gn is not None:
@@ -342,8 +350,9 @@ def main():
             dO = gdn.gated_rmsnorm_bwd(o, zt, wt, dyt, workspace=wsn)[0]
         grads = gdn.bwd(qq, kk, vv, g, beta, dO, context=ctx, need_dh0=False, workspace=wsb, qk_l2norm=l2)
         if cv is not None:
-            for xx, ww, gg in zip(cvx, cvw, grads[:3]):
-                gdn.causal_conv1d_bwd(xx, ww, gg.view(B, T, H * D), workspace=wsc)
+            # dq, dk, dv are slices of one [B, T, 3*H*D] buffer laid out like the conv output
+            dqkv = grads[0].as_strided((B, T, 3 * H * D), (T * 3 * H * D, 3 * H * D, 1), grads[0].storage_offset())
+            gdn.causal_conv1d_bwd(cvx, cvw, dqkv, workspace=wsc)
         return grads
 
     for _ in range(args.warmup):
@@ -362,7 +371,7 @@ def main():
     step_roof = None
     units = int(np.sum(np.ceil(np.full(B, T) / C))) * H
     if not args.no_profile_pass:
-        launches_per_step = 8 + (3 if gn is not None else 0) + (9 if cv is not None else 0)
+        launches_per_step = 8 + (3 if gn is not None else 0) + (3 if cv is not None else 0)
         n = launches_per_step * args.steps
         evs = HipEvents(2 * n)
         L.gdn_profile_events(ctypes.cast(evs.ev, ctypes.c_void_p), n)
