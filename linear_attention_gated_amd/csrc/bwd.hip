@@ -555,6 +555,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
   __shared__ float s_inv[NORM ? 128 : 1];   // sign-encoded reciprocal norms of the q, k rows
+  // value rows of this wave's dT tiles, read with the setup's reads (used
+  // several phases later)
+  constexpr int NTT = (10 + NW - 1) / NW;   // dT tiles per wave, at most
+  frag_t<E> vn[NTT][KB];
   // ---- setup: decays, staged tiles, and the records the transposes need
   {
     const float gv = p.gamma[(size_t)ch * 64 + lane];
@@ -564,6 +568,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H);
     sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H);
     if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
+#pragma unroll
+    for (int k = 0; k < NTT; ++k) {
+      const int t = w + NW * k;
+      const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
+      const int sbt = t - rbt * (rbt + 1) / 2;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, xbase, xrow, 16 * sbt + li, kb) : zero_frag<E>();
+    }
     // T = (I + diag(beta) A')^-1 as the forward solved it
     constexpr int TPER = 64 * 16 / NT;
     f32x4 tv[TPER];
@@ -704,17 +716,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 #pragma unroll
     for (int rbp = 0; rbp < 4; ++rbp)
       store_half(sdW + (rbp * KB + kw) * REC, mma(dWir[rbp >> 1], (rbp & 1) ? id1 : id0, zero4()));
-  }
-  // value rows of this wave's dT tiles
-  constexpr int NTT = (10 + NW - 1) / NW;   // dT tiles per wave, at most
-  frag_t<E> vn[NTT][KB];
-#pragma unroll
-  for (int k = 0; k < NTT; ++k) {
-    const int t = w + NW * k;
-    const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-    const int sbt = t - rbt * (rbt + 1) / 2;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, xbase, xrow, 16 * sbt + li, kb) : zero_frag<E>();
   }
   __syncthreads();
 
