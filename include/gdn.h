@@ -31,6 +31,10 @@
  * variable-length problems have B = 1, T = total tokens and N sequences
  * given by cu_seqlens (int32, N+1 entries, cu[0] = 0, non-decreasing,
  * cu[N] = T; zero-length sequences are allowed and pass their state through).
+ * The host copy of cu_seqlens is validated and sizes the launches; the device
+ * copy, which the kernels read, must hold the same values.  If it does not,
+ * the results are unspecified, but the kernels clamp what they take from it
+ * so that no read or write leaves the buffers the host copy describes.
  *
  * Ownership and execution:
  *  - The caller owns every buffer.  The library never allocates, frees or

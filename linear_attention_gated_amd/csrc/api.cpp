@@ -606,6 +606,7 @@ gdn_status gdn_recurrent_fwd(const gdn_problem* p, const void* q, const void* k,
     R.N = (int)P.N;
     R.H = (int)p->heads;
     R.dense_T = P.varlen ? 0 : (int)p->seqlen;
+    R.tokens = P.tokens;
     R.num_slots = num_slots;
     R.scale = p->scale;
     R.norm = p->qk_l2norm;

@@ -73,7 +73,9 @@ __global__ __launch_bounds__(1024) void k_plan(Params p) {
     }
     const int4 s = p.seq_tab[lo];
     const int j = c - s.x;
-    const int t0 = min(s.z + CHUNK * j, p.total_tokens);
+    // t0 stays a valid token even for a chunk clamped to length 0, so that
+    // row reads clamped to the chunk's rows never leave the tensors
+    const int t0 = min(s.z + CHUNK * j, p.total_tokens - 1);
     const int len = max(0, min(min(CHUNK, s.w - CHUNK * j), p.total_tokens - t0));
     p.chunk_tab[c] = make_int4(t0, len, lo, j);
   }

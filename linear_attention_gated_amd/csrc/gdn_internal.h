@@ -138,6 +138,7 @@ struct RecParams {
   void* o;                  // [tokens][H][dv]
   const int32_t* cu;        // device cu_seqlens or nullptr (dense)
   int N, H, dense_T;
+  long long tokens;         // B * T: cu values are clamped to [0, tokens]
   long long num_slots;
   float scale;
   int norm;                 // 1: q and k rows L2-normalised

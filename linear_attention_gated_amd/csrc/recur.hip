@@ -35,8 +35,10 @@ __global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
   const int j = threadIdx.x;
   long long t0, t1;
   if (p.cu) {
-    t0 = p.cu[n];
-    t1 = p.cu[n + 1];
+    // clamped to the tokens the host copy describes, so a device copy that
+    // differs from it cannot send the reads and writes outside the tensors
+    t0 = min(max((long long)p.cu[n], 0LL), p.tokens);
+    t1 = min(max((long long)p.cu[n + 1], t0), p.tokens);
   } else {
     t0 = (long long)n * p.dense_T;
     t1 = t0 + p.dense_T;
