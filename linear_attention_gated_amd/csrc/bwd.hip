@@ -227,7 +227,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
 // registers.  The chunk operands (Kt, -W^T, this block of Z and dVl, gamma)
 // are streamed through an LDS ring by loader waves (ring.h), last chunk first.
 // Per chunk: store H' (fragment-native), dV' = dVl + Kt H', store dV',
-// H' <- exp(gamma_L) H' + Z - W^T dV'.
+// H' <- exp(gamma_L) H' + Z - W^T dV'.  H' and dV' are stored non-temporal:
+// right after a forward, the caches hold its freshly written context, and
+// these 48 MB (at 4096 x 16 x 128) written into the caches would evict it
+// during this pass, whose operand reads then wait behind the write-backs.
 template <typename E, int D>
 struct BwdRing {
   static constexpr int KB = D / 32, NJ = D / 16;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         asm volatile("" : "+v"(hs[ib]));
       }
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) store_rec<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
+      for (int kb = 0; kb < KB; ++kb) store_rec_nt<E>(HPf + ((ch * NJ + jb) * KB + kb) * REC, lane, hfr[kb]);
       frag_t<E> dvf[2];
 #pragma unroll
       for (int rkb = 0; rkb < 2; ++rkb) {
@@ -363,7 +366,7 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         }
       }
 #pragma unroll
-      for (int rkb = 0; rkb < 2; ++rkb) store_rec<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
+      for (int rkb = 0; rkb < 2; ++rkb) store_rec_nt<E>(dVf + ((ch * NJ + jb) * 2 + rkb) * REC, lane, dvf[rkb]);
     };
     if constexpr (kPipe) {
       if (nc > 0) {

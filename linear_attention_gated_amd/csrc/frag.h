@@ -129,6 +129,17 @@ template <typename E> __device__ __forceinline__ frag_t<E> load_rec(const E* rec
 template <typename E> __device__ __forceinline__ void store_rec(E* rec, int lane, frag_t<E> f) {
   *reinterpret_cast<frag_t<E>*>(rec + 8 * lane) = f;
 }
+// The same store with the non-temporal hint, for records that nothing reads
+// for a while: they go to HBM rather than staying dirty in the caches, where
+// they would be evicted (written back) in the middle of later kernels' reads.
+template <typename E> __device__ __forceinline__ void store_rec_nt(E* rec, int lane, frag_t<E> f) {
+  constexpr int NP = (int)sizeof(frag_t<E>) / 16;   // 16-byte pieces: 1 (bf16) or 2 (fp32)
+  static_assert(NP * 16 == (int)sizeof(frag_t<E>), "a fragment is whole 16-byte pieces");
+  const i32x4* src = reinterpret_cast<const i32x4*>(&f);
+  i32x4* dst = reinterpret_cast<i32x4*>(rec + 8 * lane);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) __builtin_nontemporal_store(src[i], dst + i);
+}
 // Accumulator-native record: 64 lanes x 4 elements.
 template <typename E> __device__ __forceinline__ f32x4 load_acc(const E* rec, int lane) {
   return quad_to_f32<E>(*reinterpret_cast<const quad_t<E>*>(rec + 4 * lane));

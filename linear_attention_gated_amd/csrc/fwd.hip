@@ -220,12 +220,14 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   }
   __syncthreads();
 
-  // T = (I + A)^-1 (ends with a barrier); kept for the backward
+  // T = (I + A)^-1 (ends with a barrier); kept for the backward, which is
+  // the next to read it: stored non-temporal, so that it does not sit dirty
+  // in the caches until then
   tri_inverse64(sA, nullptr, sT, LDA, NW);
   for (int e = tid; e < 64 * 16; e += 64 * NW) {
     const int r = e >> 4, c4 = e & 15;
-    *reinterpret_cast<float4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4) =
-        *reinterpret_cast<const float4*>(&sT[r * LDA + 4 * c4]);
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sT[r * LDA + 4 * c4]),
+                                reinterpret_cast<f32x4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4));
   }
 
   // T fragments F(T; r, s), read where used (lower triangular: (rb <= 1, skb = 1) is zero)

@@ -122,8 +122,11 @@ __global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
     o[th * DV + j] = (E)(p.scale * iq * ((o0 + o1) + (o2 + o3)));
     __syncthreads();   // sq, sk are rewritten by the next token
   }
+  // written back non-temporal: the next reader is the next call, and a state
+  // pool of this size would otherwise be evicted from the caches (written
+  // back) in the middle of that call's reads
 #pragma unroll
-  for (int i = 0; i < DK; ++i) st[i * DV + j] = h[i];
+  for (int i = 0; i < DK; ++i) __builtin_nontemporal_store(h[i], st + i * DV + j);
 }
 
 template <typename E, int DK, int DV>
