@@ -186,6 +186,55 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
     print("copy calibration: %d x %d bytes" % (reps, nbytes), file=sys.stderr)
 
 
+def measured_peak_gbs(torch, dev, nbytes=1 << 30, reps=5):
+    """HBM bandwidth that library kernels reach on this GPU, the measured peak beside the
+    vendor one: a 1 GiB device-to-device copy (bytes read plus written) and a 1 GiB fp32
+    sum (bytes read), each the median of `reps`.  Returns (best, copy, read) in GB/s."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    af = a.view(torch.float32)
+
+    def med(fn, moved):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return moved / sorted(ts)[reps // 2] / 1e9
+
+    cp = med(lambda: b.copy_(a), 2 * nbytes)
+    rd = med(lambda: af.sum(), nbytes)
+    del a, b, af
+    return max(cp, rd), cp, rd
+
+
+def step_percentiles(torch, dev, step, n, flush_bytes):
+    """Per-step times (ms) over n steps, each bracketed by events on the current stream;
+    with flush_bytes > 0 a write of that many bytes runs before each step, outside the
+    events, so that the step starts with nothing of its own in the L2 and memory-side caches."""
+    import numpy as np
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device=dev) if flush_bytes else None
+    ts = []
+    for _ in range(n):
+        if junk is not None:
+            junk.fill_(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del junk
+    q = np.percentile(np.array(ts), [10, 50, 90])
+    return {"steps": n, "p10_ms": round(float(q[0]), 4), "median_ms": round(float(q[1]), 4),
+            "p90_ms": round(float(q[2]), 4)}
+
+
 def decode_bench(args):
     """One step = one recurrent call: N sequences x 1 new token, H=16, d_k=d_v=128, bf16, the
     fp32 states [N,16,128,128] read and written in place."""
@@ -235,6 +284,11 @@ def decode_bench(args):
                     "traffic": traffic_for("recurrent", "hbm_traffic_decode_N%d_T1_H16_d128_bf16.txt" % N),
                     "algorithmic_bytes_per_launch": byts, "units_per_launch": N * H,
                     "bytes_per_unit": byts // (N * H), "avg_us": round(avg_us, 2)}
+        best, cp, rd = measured_peak_gbs(torch, dev)
+        roofline["measured_peak"] = round(best, 1)
+        roofline["frac_of_measured_peak"] = round(a_gbs / best, 4)
+        roofline["measured_copy_GBps"] = round(cp, 1)
+        roofline["measured_read_GBps"] = round(rd, 1)
     if args.copy_calib:
         copy_calibration(torch, dev)
     cpu = None
@@ -417,6 +471,18 @@ def main():
                      "mfma_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
                      "kernel_sum_us": round(sum(1e3 * tot[k_] / args.steps for k_ in tot), 1)}
 
+    # per-step percentiles, warm (steps back to back) and cold (1 GiB written before each step)
+    timing = None
+    if not args.no_profile_pass:
+        timing = {"warm": step_percentiles(torch, dev, step, 30, 0),
+                  "cold": step_percentiles(torch, dev, step, 30, 1 << 30)}
+        best, cp, rd = measured_peak_gbs(torch, dev)
+        if roofline is not None:
+            roofline["measured_peak"] = round(best, 1)
+            roofline["frac_of_measured_peak"] = round(roofline["achieved"] / best, 4)
+            roofline["measured_copy_GBps"] = round(cp, 1)
+            roofline["measured_read_GBps"] = round(rd, 1)
+
     if args.copy_calib:
         copy_calibration(torch, dev)
 
@@ -431,6 +497,7 @@ def main():
                    "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,
+        "step_timing": timing,
         "sources_sha": sources_sha(),
     }
     print(json.dumps(out), flush=True)
