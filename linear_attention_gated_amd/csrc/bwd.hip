@@ -871,8 +871,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, xbase, xrow, 16 * sb + li, kw);
   __syncthreads();
 
-  // ---- per-wave outputs.  With in-operator normalisation the gradients just
-  // computed are those of the normalised rows, y = x / ||x||; their per-row
+  // ---- per-wave outputs, stored non-temporal: another kernel reads them
+  // next, and a step's 48 MB of them left dirty in the caches would be
+  // written back in the middle of later kernels' reads.  With in-operator
+  // normalisation the gradients just computed are those of the normalised
+  // rows, y = x / ||x||; their per-row
   // dots y . dy over all D columns are gathered in LDS (the M1 region is
   // free now) and dx = (dy - y (y . dy)) / ||x|| is written after a barrier:
   // dq's right after its products (its stores overlap the dk work), dk's at
@@ -898,7 +901,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = ir > 0.f ? (dy[rb][q] - yn[rb][q] * yd) * ir : -dy[rb][q] * ir;
-      if (r < L) *reinterpret_cast<quad_t<E>*>(dst + xbase + (size_t)r * xrow + 16 * w + 4 * lg) = to_quad<E>(o);
+      if (r < L) store_quad_nt<E>(dst + xbase + (size_t)r * xrow + 16 * w + 4 * lg, o);
     }
   };
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
@@ -951,7 +954,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dqh[rb] = acc;
         qn4[rb] = qn;
       } else if (r < L) {
-        *reinterpret_cast<quad_t<E>*>(dQ + xbase + (size_t)r * xrow + 16 * w + 4 * lg) = to_quad<E>(acc);
+        store_quad_nt<E>(dQ + xbase + (size_t)r * xrow + 16 * w + 4 * lg, acc);
       }
     }
     if constexpr (norm) {
@@ -1015,7 +1018,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dkh[sb] = acc;
         kn4[sb] = kn;
       } else if (s_ < L) {
-        *reinterpret_cast<quad_t<E>*>(dK + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg) = to_quad<E>(acc);
+        store_quad_nt<E>(dK + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg, acc);
       }
     }
     csum = sum_in_group(csum);
@@ -1046,7 +1049,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       dot = sum_groups(dot);
       add_col(dbc, sb, dot);
       if (s_ < L)
-        *reinterpret_cast<quad_t<E>*>(dV + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg) = to_quad<E>(scale4(acc[sb], bs));
+        store_quad_nt<E>(dV + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg, scale4(acc[sb], bs));
     }
   }
   {

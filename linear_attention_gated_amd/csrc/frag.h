@@ -140,6 +140,17 @@ template <typename E> __device__ __forceinline__ void store_rec_nt(E* rec, int l
 #pragma unroll
   for (int i = 0; i < NP; ++i) __builtin_nontemporal_store(src[i], dst + i);
 }
+// Four converted values to dst with the non-temporal hint (one 8-byte
+// store for bf16, one 16-byte store for fp32), for outputs whose next reader
+// is another kernel.
+template <typename E> __device__ __forceinline__ void store_quad_nt(E* dst, f32x4 x) {
+  const quad_t<E> v = to_quad<E>(x);
+  if constexpr (sizeof(quad_t<E>) == 8) {
+    __builtin_nontemporal_store(*reinterpret_cast<const long long*>(&v), reinterpret_cast<long long*>(dst));
+  } else {
+    __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(&v), reinterpret_cast<i32x4*>(dst));
+  }
+}
 // Accumulator-native record: 64 lanes x 4 elements.
 template <typename E> __device__ __forceinline__ f32x4 load_acc(const E* rec, int lane) {
   return quad_to_f32<E>(*reinterpret_cast<const quad_t<E>*>(rec + 4 * lane));
