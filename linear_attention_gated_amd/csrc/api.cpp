@@ -689,7 +689,8 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0; P.o = o; P.ht = ht;
     const int D = (int)L.D;
     hipError_t e;
-    if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+    // (packed input only: for dense input the chunk tables are arithmetic and nothing is launched)
+    if (L.varlen && (e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
     if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
     if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
@@ -747,7 +748,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     const int D = (int)L.D;
     hipError_t e;
     if (!fwd_workspace) {
-      if ((e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+      if (L.varlen && (e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
       if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
       if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, false, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
     }
