@@ -871,22 +871,37 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, xbase, xrow, 16 * sb + li, kw);
   __syncthreads();
 
-  // ---- per-wave outputs, stored non-temporal: another kernel reads them
-  // next, and a step's 48 MB of them left dirty in the caches would be
-  // written back in the middle of later kernels' reads.  With in-operator
-  // normalisation the gradients just computed are those of the normalised
-  // rows, y = x / ||x||; their per-row
+  // ---- per-wave outputs.  With in-operator normalisation the gradients just
+  // computed are those of the normalised rows, y = x / ||x||; their per-row
   // dots y . dy over all D columns are gathered in LDS (the M1 region is
-  // free now) and dx = (dy - y (y . dy)) / ||x|| is written after a barrier:
-  // dq's right after its products (its stores overlap the dk work), dk's at
-  // the end.
+  // free now) and dx = (dy - y (y . dy)) / ||x|| is formed after a barrier:
+  // dq's right after its products, dk's at the end.
   constexpr bool norm = NORM;
   float* s_qd = sM1;             // [64][NW] partial q . dq
   float* s_kd = sM1 + NW * 64;   // [64][NW] partial k . dk
+  // dq, dk, dv leave through LDS: each wave holds 16 columns of a row (32
+  // bytes in bf16), so its own stores would write partial lines; staged, the
+  // rows go out whole, 16 bytes a lane, after the last barrier.  Staging
+  // rows are unpadded, their 16-byte pieces XOR-swizzled by the row so that
+  // the column-block writes of a wave fall in distinct banks.  Regions: dq in
+  // T's (free after the dA phase); dk in M1's (free after the dA phase) or,
+  // normalised, in Q's tile (free after the last barrier); dv in K's tile.
+  constexpr int RB = D * (int)sizeof(E);   // bytes of a staged row
+  constexpr int PPR = RB / 16;             // 16-byte pieces per row
+  static_assert(64 * RB <= S::MAT && 64 * RB <= S::TILE, "a staged output tile fits its region");
+  char* stq = reinterpret_cast<char*>(sT);
+  char* stk = norm ? tQ : reinterpret_cast<char*>(sM1);
+  char* stv = tK;
+  // columns 16 w + 4 lg .. + 3 of row r (this lane's four values) into a staging tile
+  auto stage4 = [&](char* st, int r, f32x4 x) {
+    const int byte = (16 * w + 4 * lg) * (int)sizeof(E);
+    const int pc = (byte >> 4) ^ (r % PPR);
+    *reinterpret_cast<quad_t<E>*>(st + r * RB + 16 * pc + (byte & 15)) = to_quad<E>(x);
+  };
   f32x4 dqh[4], dkh[4], qn4[4], kn4[4];
   // dx for rows 16 rb + li of this wave's columns (rows above the floor:
-  // (dy - y (y . dy)) / ||x||; below it: dy / floor)
-  auto norm_out = [&](const f32x4 (&dy)[4], const f32x4 (&yn)[4], const float* part, const float* iv, E* dst) {
+  // (dy - y (y . dy)) / ||x||; below it: dy / floor), into a staging tile
+  auto norm_out = [&](const f32x4 (&dy)[4], const f32x4 (&yn)[4], const float* part, const float* iv, char* dst) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = 16 * rb + li;
@@ -901,7 +916,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = ir > 0.f ? (dy[rb][q] - yn[rb][q] * yd) * ir : -dy[rb][q] * ir;
-      if (r < L) store_quad_nt<E>(dst + xbase + (size_t)r * xrow + 16 * w + 4 * lg, o);
+      stage4(dst, r, o);
     }
   };
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
@@ -922,7 +937,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 
   // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s])
   {
-    E* dQ = reinterpret_cast<E*>(p.dq);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int r = 16 * rb + li;
@@ -953,20 +967,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         if (lg == 0) s_qd[r * NW + w] = yd;
         dqh[rb] = acc;
         qn4[rb] = qn;
-      } else if (r < L) {
-        store_quad_nt<E>(dQ + xbase + (size_t)r * xrow + 16 * w + 4 * lg, acc);
+      } else {
+        stage4(stq, r, acc);
       }
     }
     if constexpr (norm) {
       __syncthreads();
-      norm_out(dqh, qn4, s_qd, s_inv, dQ);
+      norm_out(dqh, qn4, s_qd, s_inv, stq);
     }
   }
 
   // dK^T[i][s] = scale sum_r Q[r][i] dPD[r][s] + exp(gL - g_s) sum_j H'[i][j] V'[s][j]
   //            + beta_s Gam_s sum_r dW[r][i] T[r][s] + sum_r K[r][i] (E + E^T)[s][r]
   {
-    E* dK = reinterpret_cast<E*>(p.dk);
     f32x4 ta[4], tb[4], tc[4], td[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
@@ -1017,8 +1030,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         if (lg == 0) s_kd[s_ * NW + w] = yd;
         dkh[sb] = acc;
         kn4[sb] = kn;
-      } else if (s_ < L) {
-        store_quad_nt<E>(dK + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg, acc);
+      } else {
+        stage4(stk, s_, acc);
       }
     }
     csum = sum_in_group(csum);
@@ -1026,8 +1039,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
 
   // dV^T[j][s] = beta_s sum_r dV'[r][j] T[r][s]; dbeta_s += v_s . (T^T dV')_s
+  // (kept in registers until K's tile is free for its staging)
+  f32x4 dvo[4];
   {
-    E* dV = reinterpret_cast<E*>(p.dv);
     f32x4 acc[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
@@ -1048,8 +1062,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       for (int q = 0; q < 4; ++q) dot += vv[q] * acc[sb][q];
       dot = sum_groups(dot);
       add_col(dbc, sb, dot);
-      if (s_ < L)
-        store_quad_nt<E>(dV + xbase + (size_t)s_ * xrow + 16 * w + 4 * lg, scale4(acc[sb], bs));
+      dvo[sb] = scale4(acc[sb], bs);
     }
   }
   {
@@ -1065,7 +1078,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
   __syncthreads();
 
-  if constexpr (norm) norm_out(dkh, kn4, s_kd, s_inv + 64, reinterpret_cast<E*>(p.dk));
+  if constexpr (norm) norm_out(dkh, kn4, s_kd, s_inv + 64, stk);
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) stage4(stv, 16 * sb + li, dvo[sb]);
+  __syncthreads();
+  // whole rows of dq, dk, dv, 16 bytes a lane, non-temporal: another kernel
+  // reads them next, and a step's 48 MB of them left dirty in the caches
+  // would be written back in the middle of later kernels' reads
+  static_assert((64 * PPR) % NT == 0, "the staged rows divide over the threads");
+#pragma unroll
+  for (int e0 = 0; e0 < 64 * PPR; e0 += NT) {
+    const int e = e0 + tid, r = e / PPR, pc = e - r * PPR;
+    if (r < L) {
+      const int off = r * RB + 16 * (pc ^ (r % PPR));
+      const size_t dst = (xbase + (size_t)r * xrow) * sizeof(E) + 16 * (size_t)pc;
+      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stq + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dq) + dst));
+      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stk + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dk) + dst));
+      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stv + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dv) + dst));
+    }
+  }
 
   // ---- dgamma -> dg (reverse chunk-local cumsum), dbeta
   if (w == 0) {
