@@ -20,10 +20,14 @@
 // K-1 row halo.  Sequence boundaries enter only through each token's
 // position in its sequence (pos) and the tokens left after it (rem): tap s
 // of y[t] reads x[t - s] iff s <= pos(t), and dx[t'] takes dpre[t' + d] iff
-// d <= rem(t').  dw and dbias: per-lane sums over the lane's tokens, then a
+// d <= rem(t').  A forward tile whose reach lies inside one sequence (nearly
+// all of them) runs a copy of the body without these checks.  dw and dbias:
+// per-lane sums over the lane's tokens, then a
 // fixed-order sum over the waves of a workgroup (one partial per workgroup
 // row of the grid) and, in k_conv_dw, over the partials.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "frag.h"
 #include "gdn_internal.h"
@@ -93,10 +97,11 @@ __device__ __forceinline__ void seq_pos(const ConvParams& p, long long t, int& p
 // Row t's piece cp, or zeros outside the tokens / channels.  The read is
 // unconditional (from row 0, piece 0 when out of range; tokens >= 1), so a
 // batch of these issues back to back instead of one branch and wait each.
-template <typename E, int CPT>
+// CHECK = false: the caller knows 0 <= t < tokens.
+template <typename E, int CPT, bool CHECK = true>
 __device__ __forceinline__ typename CPiece<E, CPT>::R load_row(const ConvParams& p, const void* base, long long t, int cp, bool live) {
   using R = typename CPiece<E, CPT>::R;
-  const bool ok = live && t >= 0 && t < p.tokens;
+  const bool ok = CHECK ? live && t >= 0 && t < p.tokens : live;
   const R v = reinterpret_cast<const R*>(base)[(ok ? t : 0) * (p.C / CPT) + (ok ? cp : 0)];
   return ok ? v : R{};
 }
@@ -118,12 +123,9 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
     bs[e] = p.bias ? p.bias[c] : 0.f;
   }
   typename P::R* Y = reinterpret_cast<typename P::R*>(p.y);
-  for (long long tile = blockIdx.y; tile * (NW * TW) < p.tokens; tile += gridDim.y) {
-    const long long ta = tile * (NW * TW) + (long long)w * TW;
-    if (ta >= p.tokens) break;
-    // (pos, rem) of tokens ta - 3 + l in lane l
-    int pv = -1, rv = -1;
-    if (lane < WIN) seq_pos(p, ta - 3 + lane, pv, rv);
+  // one tile of TW tokens starting at ta; INNER: no sequence boundary in reach
+  auto fwd_tile = [&](auto inner_c, long long ta, int pv) {
+    constexpr bool INNER = decltype(inner_c)::value;
     F hist[4];   // x[t], x[t-1], x[t-2], x[t-3] once the step's shift is done
     hist[3] = F{};
 #pragma unroll
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
     for (int i0 = 0; i0 < TW; i0 += 8) {
       typename P::R xs[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xs[i] = load_row<E, CPT>(p, p.x, ta + i0 + i, cp, live);
+      for (int i = 0; i < 8; ++i) xs[i] = load_row<E, CPT, !INNER>(p, p.x, ta + i0 + i, cp, live);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const long long t = ta + i0 + i;
@@ -141,19 +143,30 @@ __global__ __launch_bounds__(64 * NW) void k_conv_fwd(ConvParams p) {
         hist[1] = hist[0];
         hist[0] = P::to_f(xs[i]);
         const int pos = __builtin_amdgcn_readlane(pv, i0 + i + 3);
-        if (t >= p.tokens) continue;
+        if (!INNER && t >= p.tokens) continue;
         F o;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
           float acc = bs[e];
 #pragma unroll
           for (int s = 0; s < K; ++s)
-            if (s <= pos) acc += wt[K - 1 - s][e] * hist[s][e];
+            if (INNER || s <= pos) acc += wt[K - 1 - s][e] * hist[s][e];
           o[e] = p.act ? acc * csigmoid(acc) : acc;
         }
         if (live) Y[t * (p.C / CPT) + cp] = P::from_f(o);
       }
     }
+  };
+  for (long long tile = blockIdx.y; tile * (NW * TW) < p.tokens; tile += gridDim.y) {
+    const long long ta = tile * (NW * TW) + (long long)w * TW;
+    if (ta >= p.tokens) break;
+    // (pos, rem) of tokens ta - 3 + l in lane l
+    int pv = -1, rv = -1;
+    if (lane < WIN) seq_pos(p, ta - 3 + lane, pv, rv);
+    // tokens ta - 3 .. ta + TW - 1 in one sequence (so inside the tokens): no
+    // tap of the tile crosses a boundary, and the body runs without checks
+    if (__builtin_amdgcn_readlane(pv, TW + 2) >= TW + 2) fwd_tile(std::true_type{}, ta, pv);
+    else fwd_tile(std::false_type{}, ta, pv);
   }
 }
 
