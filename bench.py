@@ -470,6 +470,12 @@ def main():
                      "achieved_TFLOPs": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
                      "mfma_frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5),
                      "kernel_sum_us": round(sum(1e3 * tot[k_] / args.steps for k_ in tot), 1)}
+        # the sequential passes are latency-bound: their critical path is the dependent
+        # chunk steps of the longest sequence times the time of one step
+        nsteps = int(np.ceil(T / C))
+        step_roof["critical_path"] = {
+            k_: {"dependent_steps": nsteps, "us_per_step": round(1e3 * tot[k_] / num[k_] / nsteps, 3)}
+            for k_ in ("fwd_state", "bwd_state") if k_ in tot}
 
     # per-step percentiles, warm (steps back to back) and cold (1 GiB written before each step)
     timing = None
