@@ -128,6 +128,18 @@ def test_full_packed_varlen_fwd_bwd():
     compare(x, label="c2 packed fwd+bwd")
 
 
+def test_thousands_of_short_sequences():
+    # 2500 sequences of 0..80 tokens: the planner's scan runs three passes of 1024 sequences
+    # (with the carry between them), empty sequences pass h0 through, most chunks are partial
+    lengths = [int(v) for v in np.random.default_rng(23).integers(0, 81, 2500)]
+    lengths[:5] = [0, 0, 1, 64, 65]
+    cfg = small_cfg("bf16", 64, H=2, h0_std=0.05, with_grad=True)
+    x = gi.make_inputs(cfg, 24, lengths=lengths)
+    assert x["N"] == 2500
+    dht = np.random.default_rng(25).standard_normal((x["N"], 2, 64, 64)) * 0.05
+    compare(x, dht=dht, scale=0.5, label="2500 packed sequences")
+
+
 def test_packed_varlen_with_states_and_scale():
     # packed sequences with initial states, a final-state gradient and scale != 1
     cfg = small_cfg("bf16", 128, H=3, h0_std=0.05, with_grad=True)

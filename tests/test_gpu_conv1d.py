@@ -75,6 +75,14 @@ def test_packed_with_short_and_empty_sequences(dtype, K):
     check(x, True, True, "packed short")
 
 
+def test_thousands_of_short_sequences():
+    # 3000 sequences of 0..9 tokens (more than one planner pass of 1024, many empty): every
+    # token's window is clipped by a nearby sequence start or end
+    lengths = [int(v) for v in np.random.default_rng(9).integers(0, 10, 3000)]
+    x = gi.make_conv_inputs(1, 0, 256, 4, "bf16", seed=9, lengths=lengths)
+    check(x, True, True, "3000 short sequences")
+
+
 def test_throughput_workload_qkv_channels():
     # the short conv of the throughput workload: T = 4096 tokens, q, k, v of 16 heads x 128
     # concatenated (6144 channels), K = 4, SiLU, bf16

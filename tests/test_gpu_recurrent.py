@@ -91,6 +91,18 @@ def test_packed_sequences():
     check_pair("state", st, rht, "bf16", "frob")
 
 
+def test_thousands_of_sequences():
+    lengths = [int(v) for v in np.random.default_rng(66).integers(0, 4, 3000)]
+    cfg = small_cfg("bf16", 64, H=2)
+    x = gi.make_inputs(cfg, 67, lengths=lengths)
+    s0 = initial_state(x["N"], 2, 64, 64, 6, std=0.2)
+    say("case recurrent 3000 packed sequences")
+    o, st = run_rec(x, s0)
+    ro, rht = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], s0, cu_seqlens=x["cu_seqlens"])
+    check_pair("o", o, ro, "bf16", "maxrel")
+    check_pair("state", st, rht, "bf16", "frob")
+
+
 def test_one_call_equals_token_by_token_calls():
     N, H, T, d = 4, 2, 5, 64
     x = gi.make_inputs(small_cfg("fp32", d, B=N, T=T, H=H), 63)
