@@ -193,3 +193,33 @@ def make_conv_inputs(B: int, T: int, C: int, K: int, dtype: str, seed: int = 0, 
     bias = round_fp32(rng.uniform(-bound, bound, C))
     dy = round_to(rng.standard_normal((B, T, C)), dtype)
     return dict(x=x, w=w, bias=bias, dy=dy, cu_seqlens=cu, dtype=dtype, B=B, T=T, C=C, K=K)
+
+
+def make_inputs_device(B: int, T: int, H: int, D: int, seed: int, device, h0_std: float = 0.02,
+                       dht_std: float = 0.02, g_scale: float = 0.1) -> dict:
+    """The dense bf16 workload drawn on the GPU, for shapes whose host-side fp64 draws would
+    take minutes (tensors past 2^31 elements): the same distributions as make_inputs (unit
+    q, k rows per head, v and do ~ N(0,1), g = -softplus(N)*g_scale, beta = sigmoid(N), h0
+    and dht ~ N(0, std^2)), drawn in fp32 by torch's seeded device generator (order: q, k,
+    v, g, beta, h0, do, dht) and rounded once to bf16 / fp32.  Checks read back the exact
+    stored values, so the draws need not match the host generator's."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def rn(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit_rows(x):
+        return (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-12)).to(torch.bfloat16)
+
+    q = unit_rows(rn(B, T, H, D))
+    k = unit_rows(rn(B, T, H, D))
+    v = rn(B, T, H, D).to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(rn(B, T, H)) * g_scale
+    beta = torch.sigmoid(rn(B, T, H))
+    h0 = rn(B, H, D, D) * h0_std
+    do = rn(B, T, H, D).to(torch.bfloat16)
+    dht = rn(B, H, D, D) * dht_std
+    return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0, do=do, dht=dht)
+
