@@ -10,10 +10,10 @@
 //     h <- a h + k_t u^T,           o_t = scale h^T q_t
 // (S_t = a S_{t-1} (I - beta k k^T) + beta v k^T, o_t = scale S_t q_t).
 //
-// The columns of h are independent, so one workgroup per (sequence, head)
-// gives thread j the column j of h, its d_k values in registers for the whole
-// call; q_t and k_t (normalised if asked) are staged in LDS and read by every
-// thread.  HBM traffic: the state once each way plus the tokens' q, k, v, o.
+// One workgroup per (sequence, head) holds h in registers for the whole call,
+// each thread a 16 x 4 block of it; q_t and k_t (normalised if asked) are
+// staged in LDS and read by every thread.  HBM traffic: the state once each
+// way plus the tokens' q, k, v, o.
 #include <hip/hip_runtime.h>
 
 #include "frag.h"
@@ -26,13 +26,24 @@ template <typename E> __device__ __forceinline__ float ld(const void* p, size_t 
   return (float)reinterpret_cast<const E*>(p)[i];
 }
 
+// Thread (rg, cg) holds rows 16 rg .. 16 rg + 15 and columns 4 cg .. 4 cg + 3 of
+// h: its state moves in 16-byte pieces, sixteen reads in flight at once.  The
+// column sums h^T k and h^T q are per-thread partials over its rows, added
+// across the row groups of a wave by a lane butterfly (bitwise the same in
+// every lane) and across the waves through LDS in wave order.
 template <typename E, int DK, int DV, bool NORM>
-__global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
-  constexpr int NWV = DV / 64;
+__global__ __launch_bounds__(DK * DV / 64) void k_recurrent(RecParams p) {
+  constexpr int CG = DV / 4;        // column groups of 4
+  constexpr int RG = DK / 16;       // row groups of 16
+  constexpr int NT = CG * RG;       // threads
+  constexpr int NWV = NT / 64;      // waves
+  static_assert(NT % 64 == 0 && 64 % CG == 0 && NT >= DK, "thread layout");
   __shared__ float sq[DK], sk[DK];
+  __shared__ f32x4 s_part[2][NWV][CG];
   __shared__ float s_red[2][NWV];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
   const int n = blockIdx.x / p.H, hh = blockIdx.x - n * p.H;
-  const int j = threadIdx.x;
   long long t0, t1;
   if (p.cu) {
     // clamped to the tokens the host copy describes, so a device copy that
@@ -43,47 +54,56 @@ __global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
     t0 = (long long)n * p.dense_T;
     t1 = t0 + p.dense_T;
   }
+  quad_t<E>* O = reinterpret_cast<quad_t<E>*>(p.o);
   const long long slot = p.idx ? (long long)p.idx[n] : (long long)n;
   if (slot < 0 || slot >= p.num_slots) {
     // no state for this sequence: its outputs are zero, no state is touched
-    for (long long t = t0; t < t1; ++t) {
-      E* o = reinterpret_cast<E*>(p.o);
-      o[((size_t)t * p.H + hh) * DV + j] = (E)0.f;
-    }
+    if (rg == 0)
+      for (long long t = t0; t < t1; ++t) O[(((size_t)t * p.H + hh) * DV) / 4 + cg] = to_quad<E>(zero4());
     return;
   }
-  // the (slot, head) block of the state: a uniform base and 32-bit offsets, so
-  // the d_k reads and writes of a thread need no address registers each
+  // the (slot, head) block of the state: a uniform base and 32-bit offsets
   float* st = p.state + ((size_t)__builtin_amdgcn_readfirstlane((int)slot) * p.H + hh) * DK * DV;
-  float h[DK];
+  f32x4 h[16];
 #pragma unroll
-  for (int i = 0; i < DK; ++i) h[i] = st[i * DV + j];
+  for (int r = 0; r < 16; ++r) h[r] = *reinterpret_cast<const f32x4*>(st + (16 * rg + r) * DV + 4 * cg);
+  // the sum over all row groups of a per-thread column partial
+  auto col_sum = [&](f32x4 x, int which) {
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] += __shfl_xor(x[e], off, 64);
+    if constexpr (NWV > 1) {
+      if (lane < CG) s_part[which][wv][cg] = x;
+      __syncthreads();
+      x = s_part[which][0][cg];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) x = x + s_part[which][w][cg];
+    }
+    return x;
+  };
   for (long long t = t0; t < t1; ++t) {
     const size_t th = (size_t)t * p.H + hh;
-    for (int i = j; i < DK; i += DV) {
-      sq[i] = ld<E>(p.q, (size_t)t * p.ldq + (size_t)hh * DK + i);
-      sk[i] = ld<E>(p.k, (size_t)t * p.ldq + (size_t)hh * DK + i);
+    if (tid < DK) {
+      sq[tid] = ld<E>(p.q, (size_t)t * p.ldq + (size_t)hh * DK + tid);
+      sk[tid] = ld<E>(p.k, (size_t)t * p.ldq + (size_t)hh * DK + tid);
     }
     const float a = __expf(p.g[th]);
     const float b = p.beta[th];
-    const float vj = ld<E>(p.v, (size_t)t * p.ldv + (size_t)hh * DV + j);
+    const f32x4 vj = quad_to_f32<E>(*reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(p.v) + (size_t)t * p.ldv + (size_t)hh * DV + 4 * cg));
     __syncthreads();
     float iq = 1.f, ik = 1.f;
     if constexpr (NORM) {
-      // reciprocal norms y = x / max(||x||, 1e-12): per-wave partial sums, then the waves in order
-      float a2 = 0.f, b2 = 0.f;
-      for (int i = j; i < DK; i += DV) {
-        a2 += sq[i] * sq[i];
-        b2 += sk[i] * sk[i];
-      }
+      // reciprocal norms y = x / max(||x||, 1e-12): per-wave sums, then the waves in order
+      float a2 = tid < DK ? sq[tid] * sq[tid] : 0.f, b2 = tid < DK ? sk[tid] * sk[tid] : 0.f;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) {
         a2 += __shfl_xor(a2, off, 64);
         b2 += __shfl_xor(b2, off, 64);
       }
-      if ((j & 63) == 0) {
-        s_red[0][j >> 6] = a2;
-        s_red[1][j >> 6] = b2;
+      if (lane == 0) {
+        s_red[0][wv] = a2;
+        s_red[1][wv] = b2;
       }
       __syncthreads();
       float nq = 0.f, nk = 0.f;
@@ -95,38 +115,31 @@ __global__ __launch_bounds__(DV) void k_recurrent(RecParams p) {
       iq = 1.f / fmaxf(sqrtf(nq), 1e-12f);
       ik = 1.f / fmaxf(sqrtf(nk), 1e-12f);
     }
-    // r = h^T k (four partial chains), then the rank-one update and the output
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    // r = h^T k over this thread's rows, then over all rows
+    f32x4 rp = zero4();
 #pragma unroll
-    for (int i = 0; i < DK; i += 4) {
-      r0 += h[i] * sk[i];
-      r1 += h[i + 1] * sk[i + 1];
-      r2 += h[i + 2] * sk[i + 2];
-      r3 += h[i + 3] * sk[i + 3];
-    }
-    const float r = ((r0 + r1) + (r2 + r3)) * ik;
-    const float u = b * (vj - a * r) * ik;   // k enters the update as ik * k
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int r = 0; r < 16; ++r) rp = rp + h[r] * sk[16 * rg + r];
+    const f32x4 rr = col_sum(rp, 0);
+    f32x4 u;   // beta (v - a r) with k entering the update as ik * k
 #pragma unroll
-    for (int i = 0; i < DK; i += 4) {
-      h[i] = a * h[i] + sk[i] * u;
-      h[i + 1] = a * h[i + 1] + sk[i + 1] * u;
-      h[i + 2] = a * h[i + 2] + sk[i + 2] * u;
-      h[i + 3] = a * h[i + 3] + sk[i + 3] * u;
-      o0 += h[i] * sq[i];
-      o1 += h[i + 1] * sq[i + 1];
-      o2 += h[i + 2] * sq[i + 2];
-      o3 += h[i + 3] * sq[i + 3];
+    for (int e = 0; e < 4; ++e) u[e] = b * (vj[e] - a * rr[e] * ik) * ik;
+    // the rank-one update of this thread's block and its part of h^T q
+    f32x4 op = zero4();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      h[r] = a * h[r] + sk[16 * rg + r] * u;
+      op = op + h[r] * sq[16 * rg + r];
     }
-    E* o = reinterpret_cast<E*>(p.o);
-    o[th * DV + j] = (E)(p.scale * iq * ((o0 + o1) + (o2 + o3)));
-    __syncthreads();   // sq, sk are rewritten by the next token
+    const f32x4 oo = col_sum(op, 1);
+    if (rg == 0) O[(th * DV) / 4 + cg] = to_quad<E>(oo * (p.scale * iq));
+    __syncthreads();   // sq, sk, s_part are rewritten by the next token
   }
   // written back non-temporal: the next reader is the next call, and a state
   // pool of this size would otherwise be evicted from the caches (written
   // back) in the middle of that call's reads
 #pragma unroll
-  for (int i = 0; i < DK; ++i) __builtin_nontemporal_store(h[i], st + i * DV + j);
+  for (int r = 0; r < 16; ++r)
+    __builtin_nontemporal_store(h[r], reinterpret_cast<f32x4*>(st + (16 * rg + r) * DV + 4 * cg));
 }
 
 template <typename E, int DK, int DV>
@@ -135,7 +148,7 @@ hipError_t rec_t(const RecParams& p, hipStream_t s) {
   RecParams a = p;
   void* args[] = {&a};
   const void* k = p.norm ? (const void*)k_recurrent<E, DK, DV, true> : (const void*)k_recurrent<E, DK, DV, false>;
-  return hipLaunchKernel(k, dim3((unsigned)(p.N * p.H)), dim3(DV), args, 0, s);
+  return hipLaunchKernel(k, dim3((unsigned)(p.N * p.H)), dim3(DK * DV / 64), args, 0, s);
 }
 
 template <typename E>
