@@ -103,18 +103,31 @@ def test_thousands_of_sequences():
     check_pair("state", st, rht, "bf16", "frob")
 
 
-def test_one_call_equals_token_by_token_calls():
-    N, H, T, d = 4, 2, 5, 64
-    x = gi.make_inputs(small_cfg("fp32", d, B=N, T=T, H=H), 63)
+@pytest.mark.parametrize("dtype,d,l2", [("fp32", 64, False), ("bf16", 128, True)])
+def test_one_call_equals_token_by_token_calls(dtype, d, l2):
+    # d = 128 spreads a head's state over four waves (sums across waves in LDS)
+    N, H, T = 4, 2, 5
+    x = gi.make_inputs(small_cfg(dtype, d, B=N, T=T, H=H, qk_normalized=not l2), 63 + d)
     s0 = initial_state(N, H, d, d, 4)
-    o_all, st_all = run_rec(x, s0)
+    say("case recurrent token by token", dtype, "d", d, "qk_l2norm", l2)
+    o_all, st_all = run_rec(x, s0, l2=l2)
     st = s0.copy()
     for t in range(T):
         xt = dict(x, q=x["q"][:, t:t + 1], k=x["k"][:, t:t + 1], v=x["v"][:, t:t + 1], g=x["g"][:, t:t + 1],
                   beta=x["beta"][:, t:t + 1], do=None, h0=None)
-        o_t, st = run_rec(xt, st)
+        o_t, st = run_rec(xt, st, l2=l2)
         assert np.array_equal(o_t[:, 0], o_all[:, t]), t
     assert np.array_equal(st, st_all)
+
+
+def test_repeated_calls_are_bitwise_equal():
+    N, H, T, d = 8, 4, 3, 128
+    x = gi.make_inputs(small_cfg("bf16", d, B=N, T=T, H=H, qk_normalized=False), 66)
+    s0 = initial_state(N, H, d, d, 6)
+    say("case recurrent repeated", "N", N, "T", T, "H", H, "d", d)
+    o1, st1 = run_rec(x, s0, l2=True)
+    o2, st2 = run_rec(x, s0, l2=True)
+    assert np.array_equal(o1, o2) and np.array_equal(st1, st2)
 
 
 def test_prefill_then_decode():
