@@ -152,3 +152,17 @@ def test_long_single_call():
     ro, rht = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], s0)
     check_pair("o", o, ro, "fp32", "maxrel")
     check_pair("state", st, rht, "fp32", "frob")
+
+
+def test_decode_workload_sampled_sequences():
+    # the decoding workload of the benchmark, in its launch configuration:
+    # 256 sequences x 1 token, H = 16, d = 128, bf16, fp32 states in place;
+    # sampled sequences (every head) against the oracle
+    N, H, d = 256, 16, 128
+    x = gi.make_inputs(gi.Config("decode", N, 1, H, d, d, "bf16", h0_std=0.1), 0)
+    say("case recurrent decode workload N", N, "H", H, "d", d)
+    o, st = run_rec(x, x["h0"])
+    pick = [0, 1, 63, 64, 127, 128, 200, 255]
+    ro, rht = oracle.fwd(x["q"][pick], x["k"][pick], x["v"][pick], x["g"][pick], x["beta"][pick], x["h0"][pick])
+    check_pair("o", o[pick], ro, "bf16", "maxrel")
+    check_pair("state", st[pick], rht, "bf16", "frob")
