@@ -289,6 +289,14 @@ def decode_bench(args):
         roofline["frac_of_measured_peak"] = round(a_gbs / best, 4)
         roofline["measured_copy_GBps"] = round(cp, 1)
         roofline["measured_read_GBps"] = round(rd, 1)
+        # back to back, part of the state pool is still in the memory-side cache
+        # from the previous call; "cold" writes 1 GiB before each call (as the
+        # rest of a model would between two decoding steps)
+        call = lambda: gdn.recurrent_fwd(q, k, v, g, beta, state)
+        timing = {"warm": step_percentiles(torch, dev, call, 30, 0),
+                  "cold": step_percentiles(torch, dev, call, 30, 1 << 30)}
+        for tm in timing.values():
+            tm["GBps_at_median"] = round(byts / (tm["median_ms"] * 1e-3) / 1e9, 1)
     if args.copy_calib:
         copy_calibration(torch, dev)
     cpu = None
@@ -313,6 +321,8 @@ def decode_bench(args):
                    "dv": D, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "sources_sha": sources_sha(),
     }
+    if roofline is not None:
+        out["step_timing"] = timing
     print(json.dumps(out), flush=True)
 
 
