@@ -244,7 +244,7 @@ struct BwdRing {
   static constexpr int S = ring_slots(SLOT);
 };
 
-template <typename E, int D>
+template <typename E, int D, bool ROT>
 __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p) {
   using R = BwdRing<E, D>;
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
@@ -261,13 +261,19 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
   const E* WnT = reinterpret_cast<const E*>(p.WnT);
   E* HPf = reinterpret_cast<E*>(p.HPf);
   E* dVf = reinterpret_cast<E*>(p.dVf);
+  const int rot = jb;   // ROT: rotated shared reads, as in the forward pass
 
   // step t handles chunk nc - 1 - t
   auto issue = [&](int t) {
     const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
     char* sl = ring + (t % S) * R::SLOT;
-    dma_kib(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane);
-    dma_kib(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane);
+    if constexpr (ROT) {
+      dma_kib_rot(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJ);
+      dma_kib_rot(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJ);
+    } else {
+      dma_kib(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane);
+      dma_kib(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane);
+    }
     dma_kib(reinterpret_cast<const E*>(p.Z) + (ch * NJ + jb) * NJ * AREC, sl + R::oZ, NJ * AREC * (int)sizeof(E), lane);
     dma_kib(reinterpret_cast<const E*>(p.dVl) + (ch * NJ + jb) * 4 * AREC, sl + R::oV, 4 * AREC * (int)sizeof(E), lane);
     dma_256(p.gamma + ch * 64, sl + R::oG, lane);
@@ -1138,7 +1144,7 @@ static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
   if (p.N * p.H == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel((const void*)k_bwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D>::S), args, 0, s);
+  return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true> : (const void*)k_bwd_state<E, D, false>, dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D>::S), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {

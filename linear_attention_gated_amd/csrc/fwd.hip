@@ -336,7 +336,7 @@ struct FwdRing {
   static constexpr int S = ring_slots(SLOT);
 };
 
-template <typename E, int D>
+template <typename E, int D, bool ROT>
 __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p, int write_ht) {
   using R = FwdRing<E, D>;
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
@@ -354,12 +354,21 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
   const E* Ua = reinterpret_cast<const E*>(p.Ua);
   E* Hf = reinterpret_cast<E*>(p.Hf);
   E* Vf = reinterpret_cast<E*>(p.Vf);
+  // the NJ workgroups of a (sequence, head) read the same -W and Kt^T records;
+  // with many of them resident, each starts at its own piece (spread over the
+  // L2 channels instead of all on one)
+  const int rot = jb;
 
   auto issue = [&](int ci) {
     const size_t ch = (size_t)(c0 + ci) * p.H + h;
     char* sl = ring + (ci % S) * R::SLOT;
-    dma_kib(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane);
-    dma_kib(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane);
+    if constexpr (ROT) {
+      dma_kib_rot(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJ);
+      dma_kib_rot(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJ);
+    } else {
+      dma_kib(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane);
+      dma_kib(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane);
+    }
     dma_kib(Ua + (ch * NJ + jb) * 4 * AREC, sl + R::oU, R::UB, lane);
     dma_256(p.gamma + ch * 64, sl + R::oG, lane);
   };
@@ -633,7 +642,7 @@ static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
   Params a = p;
   int wh = write_ht ? 1 : 0;
   void* args[] = {&a, &wh};
-  return hipLaunchKernel((const void*)k_fwd_state<E, D>, dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D>::S), args, 0, s);
+  return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true> : (const void*)k_fwd_state<E, D, false>, dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D>::S), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t fwd_out_t(const Params& p, hipStream_t s) {

@@ -59,6 +59,7 @@ struct Params {
   float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;
   void *Z, *dVl;
+  int dma_rot;             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
 };
 
 // Chunk c: (first token, length, sequence, index in sequence).  Dense

@@ -29,6 +29,18 @@ __device__ __forceinline__ void dma_kib(const void* src, void* dst, int bytes, i
     __builtin_amdgcn_global_load_lds(s + off + 16 * lane, (lds_void_ptr)(d + off), 16, 0, 0);
 }
 
+// As dma_kib, with the 1 KiB pieces taken in rotated order from piece `rot`
+// (0 <= rot): the same bytes, a different first address.
+__device__ __forceinline__ void dma_kib_rot(const void* src, void* dst, int bytes, int lane, int rot) {
+  const char* s = reinterpret_cast<const char*>(src);
+  char* d = reinterpret_cast<char*>(dst);
+  const int n = bytes / 1024;
+  for (int i = 0; i < n; ++i) {
+    const int off = ((i + rot) % n) * 1024;
+    __builtin_amdgcn_global_load_lds(s + off + 16 * lane, (lds_void_ptr)(d + off), 16, 0, 0);
+  }
+}
+
 // One wave copies 256 bytes (64 lanes x 4 bytes).
 __device__ __forceinline__ void dma_256(const void* src, void* dst, int lane) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + 4 * lane, (lds_void_ptr)dst, 4, 0, 0);
