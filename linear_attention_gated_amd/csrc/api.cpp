@@ -273,9 +273,13 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
   P.qk_l2norm = L.l2norm ? 1 : 0;
   P.ldx = L.ld;
-  // more state-pass workgroups than half the CUs: rotated shared reads (measured
-  // 8-11% faster there, 1-2% slower with fewer workgroups)
-  P.dma_rot = L.N * L.H * (L.D / 16) > 128 ? 1 : 0;
+  // State-pass workgroups, one per (sequence, head, 16-column block): with
+  // more than half the CUs' worth, rotated shared reads (measured 8-11% faster
+  // there, 1-2% slower with fewer); with more than one round's worth, two
+  // column blocks per workgroup (24% faster at 512, 4-18% slower at 256).
+  const int64_t state_wgs = L.N * L.H * (L.D / 16);
+  P.dma_rot = state_wgs > 128 ? 1 : 0;
+  P.state_cpw = state_wgs > 256 ? 2 : 1;
   if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
   return P;
 }

@@ -231,27 +231,35 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
 // right after a forward, the caches hold its freshly written context, and
 // these 48 MB (at 4096 x 16 x 128) written into the caches would evict it
 // during this pass, whose operand reads then wait behind the write-backs.
-template <typename E, int D>
+template <typename E, int D, int CPW = 1>
 struct BwdRing {
   static constexpr int KB = D / 32, NJ = D / 16;
   static constexpr int RECB = REC * (int)sizeof(E);
   static constexpr int oK = 0;
   static constexpr int oW = oK + 4 * KB * RECB;
   static constexpr int oZ = oW + NJ * 2 * RECB;
-  static constexpr int oV = oZ + NJ * AREC * (int)sizeof(E);
-  static constexpr int oG = oV + 4 * AREC * (int)sizeof(E);
+  static constexpr int ZB = NJ * AREC * (int)sizeof(E), VB = 4 * AREC * (int)sizeof(E);   // one column block
+  static constexpr int oV = oZ + CPW * ZB;
+  static constexpr int oG = oV + CPW * VB;
   static constexpr int SLOT = oG + 256;
-  static constexpr int S = ring_slots(SLOT);
+  // at most four waves (one per SIMD, so a compute wave may use 512 VGPRs):
+  // with two compute waves, at most two loaders and three slots
+  static constexpr int S = CPW == 1 ? ring_slots(SLOT) : (ring_slots(SLOT) < 3 ? ring_slots(SLOT) : 3);
+  static constexpr int WAVES = CPW + S - 1;   // compute waves, then loaders
+  static_assert(WAVES <= 4, "one wave per SIMD");
 };
 
-template <typename E, int D, bool ROT>
-__global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p) {
-  using R = BwdRing<E, D>;
+template <typename E, int D, bool ROT, int CPW>
+__global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(Params p) {
+  using R = BwdRing<E, D, CPW>;
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
   __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
+  // CPW column blocks per workgroup (one compute wave each), as in the forward pass
+  constexpr int NJP = NJ / CPW;
+  const int unit = (slot / NJP) * 8 + xcd, jbp = slot % NJP;
+  const int jb0 = CPW * jbp, jb = jb0 + (CPW > 1 && w < CPW ? w : 0);
   if (unit >= p.N * p.H) return;
   const int n = unit / p.H, h = unit - n * p.H;
   const int4 st = seq_info(p, n);
@@ -261,26 +269,26 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
   const E* WnT = reinterpret_cast<const E*>(p.WnT);
   E* HPf = reinterpret_cast<E*>(p.HPf);
   E* dVf = reinterpret_cast<E*>(p.dVf);
-  const int rot = jb;   // ROT: rotated shared reads, as in the forward pass
+  const int rot = jbp;   // ROT: rotated shared reads, as in the forward pass
 
   // step t handles chunk nc - 1 - t
   auto issue = [&](int t) {
     const size_t ch = (size_t)(c0 + nc - 1 - t) * p.H + h;
     char* sl = ring + (t % S) * R::SLOT;
     if constexpr (ROT) {
-      dma_kib_rot(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJ);
-      dma_kib_rot(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJ);
+      dma_kib_rot(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJP);
+      dma_kib_rot(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJP);
     } else {
       dma_kib(Ktn + ch * 4 * KB * REC, sl + R::oK, 4 * KB * R::RECB, lane);
       dma_kib(WnT + ch * NJ * 2 * REC, sl + R::oW, NJ * 2 * R::RECB, lane);
     }
-    dma_kib(reinterpret_cast<const E*>(p.Z) + (ch * NJ + jb) * NJ * AREC, sl + R::oZ, NJ * AREC * (int)sizeof(E), lane);
-    dma_kib(reinterpret_cast<const E*>(p.dVl) + (ch * NJ + jb) * 4 * AREC, sl + R::oV, 4 * AREC * (int)sizeof(E), lane);
+    dma_kib(reinterpret_cast<const E*>(p.Z) + (ch * NJ + jb0) * NJ * AREC, sl + R::oZ, CPW * R::ZB, lane);
+    dma_kib(reinterpret_cast<const E*>(p.dVl) + (ch * NJ + jb0) * 4 * AREC, sl + R::oV, CPW * R::VB, lane);
     dma_256(p.gamma + ch * 64, sl + R::oG, lane);
   };
-  if (w >= 1 && w - 1 < nc) issue(w - 1);
+  if (w >= CPW && w - CPW < nc) issue(w - CPW);
 
-  if (w == 0) {
+  if (w < CPW) {
     f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
@@ -311,14 +319,14 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
         for (int kb = 0; kb < KB; ++kb)
           o.kn[sb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oK) + (sb * KB + kb) * REC, lane);
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) o.dv[sb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oV) + sb * AREC + 4 * lane);
+      for (int sb = 0; sb < 4; ++sb) o.dv[sb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oV) + (CPW > 1 ? (jb - jb0) * 4 * AREC : 0) + sb * AREC + 4 * lane);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib)
 #pragma unroll
         for (int rkb = 0; rkb < 2; ++rkb)
           o.wt[ib][rkb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (ib * 2 + rkb) * REC, lane);
 #pragma unroll
-      for (int ib = 0; ib < NJ; ++ib) o.z[ib] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oZ) + ib * AREC + 4 * lane);
+      for (int ib = 0; ib < NJ; ++ib) o.z[ib] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oZ) + (CPW > 1 ? (jb - jb0) * NJ * AREC : 0) + ib * AREC + 4 * lane);
       o.gL = reinterpret_cast<const float*>(sl + R::oG)[63];
     };
     auto step = [&](int t, Ops& cur, Ops& nxt) {
@@ -404,9 +412,9 @@ __global__ __launch_bounds__((64 * BwdRing<E, D>::S)) void k_bwd_state(Params p)
       }
     }
   } else {
-    // loader wave w: steps t with t % (S - 1) == w - 1, S - 1 ahead
+    // loader wave w: steps t with t % (S - 1) == w - CPW, S - 1 ahead
     for (int t = 0; t < nc; ++t) {
-      const bool mine = (t % (S - 1)) == w - 1;
+      const bool mine = (t % (S - 1)) == w - CPW;
       if (mine) wait_vmem();
       ring_barrier();
       if (mine && t + S - 1 < nc) issue(t + S - 1);
@@ -1144,7 +1152,11 @@ static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
   if (p.N * p.H == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true> : (const void*)k_bwd_state<E, D, false>, dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D>::S), args, 0, s);
+  if (p.state_cpw == 2)
+    return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true, 2> : (const void*)k_bwd_state<E, D, false, 2>,
+                           dim3(state_grid(p.N * p.H, D, 2)), dim3(64 * BwdRing<E, D, 2>::WAVES), args, 0, s);
+  return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true, 1> : (const void*)k_bwd_state<E, D, false, 1>,
+                         dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D, 1>::WAVES), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {

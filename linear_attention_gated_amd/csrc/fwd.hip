@@ -323,7 +323,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
 // streamed through an LDS ring by loader waves (ring.h).
 // Per chunk: store the entering state (fragment-native), V' = U - W h,
 // store V', h <- exp(gamma_L) h + Kt^T V'.
-template <typename E, int D>
+template <typename E, int D, int CPW = 1>
 struct FwdRing {
   static constexpr int KB = D / 32, NJ = D / 16;
   static constexpr int RECB = REC * (int)sizeof(E);
@@ -331,19 +331,27 @@ struct FwdRing {
   static constexpr int oK = oW + 4 * KB * RECB;
   static constexpr int oU = oK + NJ * 2 * RECB;
   static constexpr int UB = 4 * AREC * (int)sizeof(E);
-  static constexpr int oG = oU + UB;
+  static constexpr int oG = oU + CPW * UB;
   static constexpr int SLOT = oG + 256;
-  static constexpr int S = ring_slots(SLOT);
+  // at most four waves (one per SIMD, so a compute wave may use 512 VGPRs):
+  // with two compute waves, at most two loaders and three slots
+  static constexpr int S = CPW == 1 ? ring_slots(SLOT) : (ring_slots(SLOT) < 3 ? ring_slots(SLOT) : 3);
+  static constexpr int WAVES = CPW + S - 1;   // compute waves, then loaders
+  static_assert(WAVES <= 4, "one wave per SIMD");
 };
 
-template <typename E, int D, bool ROT>
-__global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p, int write_ht) {
-  using R = FwdRing<E, D>;
+template <typename E, int D, bool ROT, int CPW>
+__global__ __launch_bounds__((64 * FwdRing<E, D, CPW>::WAVES)) void k_fwd_state(Params p, int write_ht) {
+  using R = FwdRing<E, D, CPW>;
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
   __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int unit = (slot / NJ) * 8 + xcd, jb = slot % NJ;
+  // CPW column blocks per workgroup (one compute wave each) share its ring:
+  // the -W and Kt^T records are read once for all of them
+  constexpr int NJP = NJ / CPW;
+  const int unit = (slot / NJP) * 8 + xcd, jbp = slot % NJP;
+  const int jb0 = CPW * jbp, jb = jb0 + (CPW > 1 && w < CPW ? w : 0);
   if (unit >= p.N * p.H) return;
   const int n = unit / p.H, h = unit - n * p.H;
   const int4 st = seq_info(p, n);
@@ -357,24 +365,24 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
   // the NJ workgroups of a (sequence, head) read the same -W and Kt^T records;
   // with many of them resident, each starts at its own piece (spread over the
   // L2 channels instead of all on one)
-  const int rot = jb;
+  const int rot = jbp;
 
   auto issue = [&](int ci) {
     const size_t ch = (size_t)(c0 + ci) * p.H + h;
     char* sl = ring + (ci % S) * R::SLOT;
     if constexpr (ROT) {
-      dma_kib_rot(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJ);
-      dma_kib_rot(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJ);
+      dma_kib_rot(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane, rot * (4 * KB * R::RECB / 1024) / NJP);
+      dma_kib_rot(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane, rot * (NJ * 2 * R::RECB / 1024) / NJP);
     } else {
       dma_kib(Wn + ch * 4 * KB * REC, sl + R::oW, 4 * KB * R::RECB, lane);
       dma_kib(Ktf + ch * NJ * 2 * REC, sl + R::oK, NJ * 2 * R::RECB, lane);
     }
-    dma_kib(Ua + (ch * NJ + jb) * 4 * AREC, sl + R::oU, R::UB, lane);
+    dma_kib(Ua + (ch * NJ + jb0) * 4 * AREC, sl + R::oU, CPW * R::UB, lane);
     dma_256(p.gamma + ch * 64, sl + R::oG, lane);
   };
-  if (w >= 1 && w - 1 < nc) issue(w - 1);
+  if (w >= CPW && w - CPW < nc) issue(w - CPW);
 
-  if (w == 0) {
+  if (w < CPW) {
     f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
@@ -406,7 +414,7 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
           o.wf[rb][kb] = load_rec<E>(reinterpret_cast<const E*>(sl + R::oW) + (rb * KB + kb) * REC, lane);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
-        o.u[rb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oU) + rb * AREC + 4 * lane);
+        o.u[rb] = *reinterpret_cast<const quad_t<E>*>(reinterpret_cast<const E*>(sl + R::oU) + (CPW > 1 ? (jb - jb0) * 4 * AREC : 0) + rb * AREC + 4 * lane);
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib)
 #pragma unroll
@@ -497,9 +505,9 @@ __global__ __launch_bounds__((64 * FwdRing<E, D>::S)) void k_fwd_state(Params p,
       }
     }
   } else {
-    // loader wave w: chunks ci with ci % (S - 1) == w - 1, S - 1 ahead
+    // loader wave w: chunks ci with ci % (S - 1) == w - CPW, S - 1 ahead
     for (int ci = 0; ci < nc; ++ci) {
-      const bool mine = (ci % (S - 1)) == w - 1;
+      const bool mine = (ci % (S - 1)) == w - CPW;
       if (mine) wait_vmem();
       ring_barrier();
       if (mine && ci + S - 1 < nc) issue(ci + S - 1);
@@ -642,7 +650,11 @@ static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
   Params a = p;
   int wh = write_ht ? 1 : 0;
   void* args[] = {&a, &wh};
-  return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true> : (const void*)k_fwd_state<E, D, false>, dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D>::S), args, 0, s);
+  if (p.state_cpw == 2)
+    return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true, 2> : (const void*)k_fwd_state<E, D, false, 2>,
+                           dim3(state_grid(p.N * p.H, D, 2)), dim3(64 * FwdRing<E, D, 2>::WAVES), args, 0, s);
+  return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true, 1> : (const void*)k_fwd_state<E, D, false, 1>,
+                         dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D, 1>::WAVES), args, 0, s);
 }
 template <typename E, int D>
 static hipError_t fwd_out_t(const Params& p, hipStream_t s) {

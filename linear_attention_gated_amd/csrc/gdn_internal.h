@@ -59,7 +59,8 @@ struct Params {
   float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;
   void *Z, *dVl;
-  int dma_rot;             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
+  int dma_rot;
+  int state_cpw;           // 16-column blocks of d_v per state-pass workgroup: 1 or 2             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
 };
 
 // Chunk c: (first token, length, sequence, index in sequence).  Dense
@@ -150,8 +151,8 @@ hipError_t launch_recurrent(const RecParams& p, int dk, int dv, bool bf16, hipSt
 // Grid of the sequential kernels: one wave per (sequence, head, 16-column
 // block), padded so that the column blocks of one (sequence, head) share an
 // XCD (workgroup ids are dealt round-robin over the 8 XCDs).
-inline int state_grid(int units, int D) {
-  const int nj = D / 16;
+inline int state_grid(int units, int D, int cpw = 1) {
+  const int nj = D / 16 / cpw;   // workgroups per (sequence, head): cpw column blocks each
   const int groups = (units + 7) / 8;
   return groups * 8 * nj;
 }
