@@ -225,7 +225,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
 // K5: reverse state-gradient pass.  One compute wave per (sequence, head,
 // 16-column block jb of d_v); the d_k x 16 slice of H' stays in accumulator
 // registers.  The chunk operands (Kt, -W^T, this block of Z and dVl, gamma)
-// are streamed through an LDS ring by loader waves (ring.h), last chunk first.
+// are streamed through an LDS ring by loader waves (ring.h), last chunk first;
+// a workgroup holds CPW column blocks, as in the forward pass.
 // Per chunk: store H' (fragment-native), dV' = dVl + Kt H', store dV',
 // H' <- exp(gamma_L) H' + Z - W^T dV'.  H' and dV' are stored non-temporal:
 // right after a forward, the caches hold its freshly written context, and

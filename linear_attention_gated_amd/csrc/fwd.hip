@@ -320,7 +320,8 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
 // block jb of d_v); the columns of the state are independent, so the compute
 // wave needs no communication: its d_k x 16 state stays in accumulator
 // registers.  The chunk operands (-W, Kt^T, this block of U, gamma) are
-// streamed through an LDS ring by loader waves (ring.h).
+// streamed through an LDS ring by loader waves (ring.h).  A workgroup holds
+// CPW column blocks (CPW compute waves sharing the ring's -W and Kt^T).
 // Per chunk: store the entering state (fragment-native), V' = U - W h,
 // store V', h <- exp(gamma_L) h + Kt^T V'.
 template <typename E, int D, int CPW = 1>
