@@ -217,3 +217,23 @@ def test_l2norm_rows_below_the_floor(dtype, d):
             mr, fr = maxrel(u, v), frob(u, v)
             say("  %-6s maxrel %.3e  frob %.3e" % (name, mr, fr))
             assert mr <= tol["maxrel"] and fr <= tol["frob"], (name, mr, fr)
+
+
+@pytest.mark.parametrize("dtype,d,B,H", [("fp32", 64, 20, 4), ("bf16", 128, 5, 8), ("bf16", 64, 40, 2)])
+def test_state_passes_grid_past_one_round(dtype, d, B, H):
+    # more than 256 (sequence, head, 16-column block) workgroups in both state
+    # passes: two column blocks per workgroup, rotated shared reads
+    assert B * H * (d // 16) > 256
+    cfg = small_cfg(dtype, d, B=B, T=100, H=H, h0_std=0.05, with_grad=True)
+    x = gi.make_inputs(cfg, 41 + d)
+    dht = np.random.default_rng(42).standard_normal((B, H, d, d)) * 0.05
+    compare(x, dht=dht, scale=0.8, label="state grids past one round")
+
+
+def test_state_passes_grid_of_one_round_rotated():
+    # 129..256 workgroups: one column block per workgroup, rotated shared reads
+    B, H, d = 3, 8, 128
+    assert 128 < B * H * (d // 16) <= 256
+    x = gi.make_inputs(small_cfg("bf16", d, B=B, T=130, H=H, h0_std=0.05, with_grad=True), 43)
+    dht = np.random.default_rng(44).standard_normal((B, H, d, d)) * 0.05
+    compare(x, dht=dht, scale=0.8, label="state grids of one round, rotated")

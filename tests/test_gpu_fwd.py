@@ -129,3 +129,12 @@ def test_l2norm_is_a_no_op_on_unit_rows():
     a, _ = run_fwd(x)
     b, _ = run_fwd(x, l2=True)
     assert np.max(np.abs(a - b)) <= 2e-2 * np.max(np.abs(a))
+
+
+@pytest.mark.parametrize("dtype,d,B,H", [("fp32", 64, 20, 4), ("fp32", 128, 5, 8), ("bf16", 128, 5, 8)])
+def test_state_pass_grid_past_one_round(dtype, d, B, H):
+    # more than 256 (sequence, head, 16-column block) workgroups: the state pass
+    # takes two column blocks per workgroup and rotates its shared reads
+    assert B * H * (d // 16) > 256
+    x = gi.make_inputs(small_cfg(dtype, d, B=B, T=100, H=H, h0_std=0.05), 31 + d)
+    compare(x, scale=0.8, label="state grid past one round")
