@@ -13,6 +13,7 @@
 // the local dv step and the dq/dk/dw/dg step.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -252,6 +253,20 @@ gdn_status check_ptrs(const Range* req, int nreq, const Range* opt, int nopt, co
   return GDN_OK;
 }
 
+// Compute units of the current device, cached per device (256 on a whole
+// MI355X; fewer when the GPU is partitioned).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   gdn::Params P;
   std::memset(&P, 0, sizeof(P));
@@ -273,13 +288,14 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
   P.qk_l2norm = L.l2norm ? 1 : 0;
   P.ldx = L.ld;
-  // State-pass workgroups, one per (sequence, head, 16-column block): with
-  // more than half the CUs' worth, rotated shared reads (measured 8-11% faster
-  // there, 1-2% slower with fewer); with more than one round's worth, two
-  // column blocks per workgroup (24% faster at 512, 4-18% slower at 256).
-  const int64_t state_wgs = L.N * L.H * (L.D / 16);
-  P.dma_rot = state_wgs > 128 ? 1 : 0;
-  P.state_cpw = state_wgs > 256 ? 2 : 1;
+  // State-pass workgroups, one per (sequence, head, 16-column block), one
+  // resident per CU: with more than half the CUs' worth, rotated shared reads
+  // (measured 8-11% faster there, 1-2% slower with fewer); with more than one
+  // round's worth, two column blocks per workgroup (24% faster at twice the
+  // CUs, 4-18% slower at one round).
+  const int64_t state_wgs = L.N * L.H * (L.D / 16), cus = device_cus();
+  P.dma_rot = state_wgs > cus / 2 ? 1 : 0;
+  P.state_cpw = state_wgs > cus ? 2 : 1;
   if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
   return P;
 }
