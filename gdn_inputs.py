@@ -21,6 +21,14 @@ values, so the oracle sees the bits the GPU sees.
 Varlen lengths: L = floor(exp(U(ln lo, ln hi))) drawn until the total reaches
 ``total``; the last length is cut to fit (it is never zero).
 
+Clustered keys (``k_cluster`` = sigma > 0; the stress regime of the intra-chunk
+triangular solve, where beta * k_r.k_s * decay approaches 1): after the draws
+above, one random unit direction u_h per head, then k = u_h + sigma * N(0, I/d)
+per (token, head), L2-normalised (replacing the keys drawn above).  With
+``beta_range`` = (lo, hi), beta ~ U(lo, hi) is drawn after that (replacing the
+sigmoid draw).  The earlier draws are left as they are, so every other input
+keeps its values.
+
 Gated RMSNorm on the operator's output (``make_gated_norm_inputs``, its own
 stream, draws in the order x, row scales, z, w, dy):
   x      ~ N(0, 1) rows times U(0.1, 3) per row, unless given (the operator's o)
@@ -60,6 +68,8 @@ class Config:
     with_grad: bool = False
     chunk: int = 64
     qk_normalized: bool = True   # False: raw q, k rows (norms spread over [0.5, 4]) for in-operator normalisation
+    k_cluster: float = 0.0       # > 0: keys clustered around one direction per head (spread sigma)
+    beta_range: tuple | None = None   # (lo, hi): beta ~ U(lo, hi) instead of sigmoid(N(0, 1))
 
 
 # The five workloads, plus the training-step shape the throughput metric uses.
@@ -152,6 +162,13 @@ def make_inputs(cfg: Config, seed: int = 0, *, T: int | None = None, B: int | No
     beta = _sigmoid(rng.standard_normal((B, T, H)))
     h0 = rng.standard_normal((N, H, cfg.dk, cfg.dv)) * cfg.h0_std if cfg.h0_std > 0 else None
     do = rng.standard_normal((B, T, H, cfg.dv)) if cfg.with_grad else None
+    if cfg.k_cluster > 0:
+        u = _l2norm(rng.standard_normal((H, cfg.dk)))
+        k = _l2norm(u[None, None] + cfg.k_cluster * rng.standard_normal((B, T, H, cfg.dk)) / math.sqrt(cfg.dk))
+        if not cfg.qk_normalized:
+            k = k * rng.uniform(0.5, 4.0, (B, T, H, 1))
+    if cfg.beta_range is not None:
+        beta = rng.uniform(cfg.beta_range[0], cfg.beta_range[1], (B, T, H))
     out = dict(q=round_to(q, dt), k=round_to(k, dt), v=round_to(v, dt), g=round_fp32(g),
                beta=round_fp32(beta), h0=None if h0 is None else round_fp32(h0),
                do=None if do is None else round_to(do, dt), cu_seqlens=cu, dtype=dt,

@@ -1,27 +1,23 @@
-// tri.h -- T = (I + A)^-1 for a 64x64 strictly lower A in fp32, in LDS,
-// with 16x16x4 fp32 MFMAs (the intra-chunk triangular solve).
+// tri.h -- T = (I + A)^-1 for a 64x64 strictly lower A in fp32, in LDS
+// (the intra-chunk triangular solve).
 //
-// 16x16 blocks (a, b), a >= b.  Diagonal blocks use the exact product form
-// for a nilpotent matrix (A_bb^16 = 0):
-//     T_bb = (I - A)(I + A^2)(I + A^4)(I + A^8),          A = A_bb,
-// computed in registers: a 16x16 accumulator of X read by lane l as
-// X[4 lg + q][li] is the B operand of a product as it stands and the A
-// operand of the transposed product, so each intermediate is carried in
-// both orientations and the chain needs no LDS traffic.  Off-diagonal
-// blocks follow by levels (forward substitution on blocks):
+// 16x16 blocks (a, b), a >= b.  Each diagonal block is inverted by forward
+// substitution over its four 4-row groups, entirely in the VALU: lane l
+// (li = l % 16, lg = l / 16) owns column li of the block and rows 4 lg .. 4 lg
+// + 3, i.e. it ends holding T_bb in the 16x16 accumulator layout.  Row group
+// H is finished at step H: its residual rows are fetched from lane group H by
+// a lane shuffle, the 4x4 unit-lower system (I + A_HH) y = residual is solved
+// in every lane, and the later row groups subtract A_GH y.  Every value is a
+// plain substitution result, so the rounding error stays that of forward
+// substitution when entries of A approach 1 (an explicit product of powers of
+// A, e.g. (I - A)(I + A^2)(I + A^4)(I + A^8), would form entries far larger
+// than T's and lose digits to cancellation).  Off-diagonal blocks follow by
+// levels (forward substitution on blocks) with 16x16x4 fp32 MFMAs:
 //     T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb.
 #pragma once
 #include "frag.h"
 
 namespace gdn {
-
-// acc += sum_k X[k][m] Y[k][n] where lane l holds X[4lg+e][li] in x[e]
-// and Y[4lg+e][li] in y[e] (both accumulator layout): the product X^T Y.
-__device__ __forceinline__ f32x4 mm16_tt(f32x4 x, f32x4 y, f32x4 acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
-  return acc;
-}
 
 // Row block of a row-major LDS matrix as an A operand: lane gets M[r0+li][c0+4lg+e].
 __device__ __forceinline__ f32x4 rows16(const float* M, int ld, int r0, int c0, int li, int lg) {
@@ -46,38 +42,41 @@ __device__ __forceinline__ void store_acc16(float* M, int ld, int r0, int c0, in
 __device__ inline void tri_inverse64(const float* M, const float* rs, float* T, int ld, int nw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
   zero_off_blocks<float, true>(T, ld, threadIdx.x, 64 * nw);
-  // diagonal blocks
+  // diagonal blocks: lane (li, lg) solves column li, row group lg
   for (int b = w; b < 4; b += nw) {
     const int o = 16 * b;
-    // A (accumulator layout) and A^T, masked to the strict lower triangle, rows scaled
-    f32x4 A, At;
-    {
-      const f32x4 a = acc16(M, ld, o, o, li, lg);   // M[o+4lg+q][o+li]
-      const f32x4 t = rows16(M, ld, o, o, li, lg);  // M[o+li][o+4lg+q]
+    f32x4 r, x = zero4();   // residual and result rows o + 4 lg + q of column o + li
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 4 * lg + q;  // row of a / column index of t
-        const float sr = rs ? rs[o + r] : 1.f, sl = rs ? rs[o + li] : 1.f;
-        A[q] = li < r ? sr * a[q] : 0.f;           // A[r][li]
-        At[q] = r < li ? sl * t[q] : 0.f;          // A^T[r][li] = A[li][r]
+    for (int q = 0; q < 4; ++q) r[q] = (4 * lg + q == li) ? 1.f : 0.f;
+#pragma unroll
+    for (int H = 0; H < 4; ++H) {
+      // the residual of row group H in this column (held by lane group H)
+      f32x4 y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = __shfl(r[q], li + 16 * H, 64);
+      // (I + A_HH) y = residual; A_HH is the same in every lane
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        const float* arow = M + (o + 4 * H + q) * ld + o + 4 * H;
+        const float sr = rs ? rs[o + 4 * H + q] : 1.f;
+#pragma unroll
+        for (int qq = 0; qq < q; ++qq) y[q] -= (sr * arow[qq]) * y[qq];
+      }
+      if (lg == H) x = y;
+      if (H < 3) {
+        // later row groups take this group's part: r -= A_{lg,H} y
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(M + (o + 4 * lg + q) * ld + o + 4 * H);
+          const float sr = rs ? rs[o + 4 * lg + q] : 1.f;
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t += (sr * a[e]) * y[e];
+          if (lg > H) r[q] -= t;
+        }
       }
     }
-    f32x4 I;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) I[q] = (4 * lg + q == li) ? 1.f : 0.f;
-    const f32x4 z = zero4();
-    // powers: P1 = A^2, P2 = A^4, P3 = A^8 (and transposes)
-    const f32x4 P1 = mm16_tt(At, A, z), P1t = mm16_tt(A, At, z);
-    const f32x4 P2 = mm16_tt(P1t, P1, z), P2t = mm16_tt(P1, P1t, z);
-    const f32x4 P3 = mm16_tt(P2t, P2, z);
-    // F1 = (I - A)(I + P1) = I - A + P1 - A P1
-    const f32x4 AP1 = mm16_tt(At, P1, z), AP1t = mm16_tt(P1, At, z);
-    const f32x4 F1 = I - A + P1 - AP1, F1t = I - At + P1t - AP1t;
-    // F2 = F1 (I + P2)
-    const f32x4 F2 = F1 + mm16_tt(F1t, P2, z), F2t = F1t + mm16_tt(P2, F1t, z);
-    // T = F2 (I + P3)
-    const f32x4 Tb = F2 + mm16_tt(F2t, P3, z);
-    store_acc16(T, ld, o, o, li, lg, Tb);
+    store_acc16(T, ld, o, o, li, lg, x);
   }
   __syncthreads();
   // off-diagonal blocks by level d = a - b
