@@ -39,7 +39,9 @@
  * Ownership and execution:
  *  - The caller owns every buffer.  The library never allocates, frees or
  *    synchronises device memory and is reentrant; its only state is
- *    thread-local (the last error message and the timing diagnostics below).
+ *    thread-local (the last error message and the timing diagnostics below),
+ *    apart from the static scratch array of gdn_fwd_noalloc (one per GPU, see
+ *    there).
  *  - All device work is enqueued on the caller's stream (hipStream_t passed
  *    as void*, NULL = the null stream); the calls return without waiting.
  *  - Inputs are read-only.  Outputs are fully overwritten (never
@@ -76,7 +78,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum {
   GDN_OK = 0,
@@ -154,6 +156,28 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
                    const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta,
                    float* dh0, const void* fwd_workspace, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* ---- Allocation-free forward ---------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation and kernels as gdn_fwd (bitwise the same o and ht), with the
+ * workspace taken from a static device array inside the library instead of
+ * from the caller: GDN_NOALLOC_SCRATCH_BYTES (128 MiB), one copy on every GPU
+ * the library runs on, held until the process ends.  The call allocates
+ * nothing; the first call on a GPU looks up that GPU's copy.
+ *   - A problem whose gdn_fwd_workspace_bytes exceeds the limit returns
+ *     GDN_ERR_UNSUPPORTED before any HIP call (at d = 128 in bf16 the limit
+ *     holds about 1,150 (64-token chunk, head) pairs, e.g. T = 4096, H = 16).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that
+ *     overlap in time on one GPU (other streams, other threads) race; the
+ *     caller must order them.  For the same reason the forward context left in
+ *     the array is not for gdn_bwd: pass gdn_fwd's own workspace there.
+ * Arguments, layouts, streams and errors as for gdn_fwd. */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+gdn_status gdn_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* h0, void* o, float* ht,
+                           void* stream);
 
 /* ---- Recurrent (decoding) forward ----------------------------------------
  * The same recurrence as gdn_fwd, taken token by token for the decoding

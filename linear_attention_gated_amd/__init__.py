@@ -6,6 +6,7 @@ HIP kernels; PyTorch supplies device memory and the current stream.  There is
 no fallback: if the library is missing or fails, these functions raise.
 
     o, ht = fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0)
+    o, ht = fwd_noalloc(q, k, v, g, beta, ...)       # the same, on the library's static scratch
     dq, dk, dv, dg, dbeta, dh0 = bwd(q, k, v, g, beta, do, ...)
     o = recurrent_fwd(q, k, v, g, beta, state, state_indices=None)   # decoding, state in place
     y = gated_rmsnorm_fwd(x, z, w, eps=1e-6)          # the output gate: RMSNorm(x) w silu(z)
@@ -35,7 +36,7 @@ EXPORTED = ("gdn_abi_version", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_byt
             "gdn_bwd", "gdn_status_string", "gdn_last_error_message", "gdn_profile_events",
             "gdn_profile_count", "gdn_profile_name", "gdn_gated_rmsnorm_bwd_workspace_bytes",
             "gdn_gated_rmsnorm_fwd", "gdn_gated_rmsnorm_bwd", "gdn_causal_conv1d_bwd_workspace_bytes",
-            "gdn_causal_conv1d_fwd", "gdn_causal_conv1d_bwd", "gdn_recurrent_fwd")
+            "gdn_causal_conv1d_fwd", "gdn_causal_conv1d_bwd", "gdn_recurrent_fwd", "gdn_fwd_noalloc")
 
 
 class GdnProblem(ctypes.Structure):
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_bwd_workspace_bytes.restype = sz
         L.gdn_fwd.argtypes = [prob] + [p] * 8 + [p, sz, p]
         L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_fwd_noalloc.argtypes = [prob] + [p] * 8 + [p]
+        L.gdn_fwd_noalloc.restype = ctypes.c_int
         L.gdn_bwd.argtypes = [prob] + [p] * 15 + [p, sz, p]
         L.gdn_bwd.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -265,6 +268,34 @@ def fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
         key = (tuple(q.shape), tuple(v.shape), dt, None if cu_h is None else tuple(cu_h.tolist()),
                float(scale), bool(qk_l2norm), ld)
         return o, ht, Context(workspace, key)
+    return o, ht
+
+
+def fwd_noalloc(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=1.0,
+                output_final_state=True, qk_l2norm=False, out=None, final_state=None):
+    """The forward of ``fwd`` through ``gdn_fwd_noalloc``: the library allocates nothing and
+    takes its workspace from its static per-GPU scratch (so no context for ``bwd``).  With
+    ``out`` / ``final_state`` (preallocated o [B,T,H,dv] and ht [N,H,dk,dv]) this function
+    allocates nothing either.  Returns (o, ht)."""
+    dev = q.device
+    dt = q.dtype
+    ld = _qkv_stride((q, k, v), ("q", "k", "v"), dt, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(beta, "beta", torch.float32, dev)
+    _require(initial_state, "initial_state", torch.float32, dev)
+    cu_h, cu_d = _cu_pair(cu_seqlens, dev)
+    p = make_problem(q, v, cu_host=cu_h, cu_dev=cu_d, scale=scale, qk_l2norm=qk_l2norm, qkv_token_stride=ld)
+    B, T, H, dk = q.shape
+    N = _num_seqs(q, cu_h)
+    o = out if out is not None else torch.empty((B, T, H, v.shape[-1]), dtype=dt, device=dev)
+    _require(o, "out", dt, dev)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty((N, H, dk, v.shape[-1]), dtype=torch.float32,
+                                                                     device=dev)
+        _require(ht, "final_state", torch.float32, dev)
+    _check(lib().gdn_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(initial_state), _ptr(o), _ptr(ht), _stream(dev)))
     return o, ht
 
 

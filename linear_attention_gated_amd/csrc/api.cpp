@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/gdn.h"
@@ -253,12 +254,18 @@ gdn_status check_ptrs(const Range* req, int nreq, const Range* opt, int nopt, co
   return GDN_OK;
 }
 
-// Compute units of the current device, cached per device (256 on a whole
+// Device that work enqueued on stream s runs on (the null stream: the
+// calling thread's current device).
+hipError_t stream_device(hipStream_t s, int* dev) {
+  return s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev);
+}
+
+// Compute units of the device of stream s, cached per device (256 on a whole
 // MI355X; fewer when the GPU is partitioned).
-int device_cus() {
+int device_cus(hipStream_t s) {
   static std::atomic<int> cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (stream_device(s, &dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
@@ -267,7 +274,7 @@ int device_cus() {
   return n;
 }
 
-gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
+gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws, hipStream_t s) {
   gdn::Params P;
   std::memset(&P, 0, sizeof(P));
   P.H = (int)L.H;
@@ -293,7 +300,7 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws) {
   // (measured 8-11% faster there, 1-2% slower with fewer); with more than one
   // round's worth, two column blocks per workgroup (24% faster at twice the
   // CUs, 4-18% slower at one round).
-  const int64_t state_wgs = L.N * L.H * (L.D / 16), cus = device_cus();
+  const int64_t state_wgs = L.N * L.H * (L.D / 16), cus = device_cus(s);
   P.dma_rot = state_wgs > cus / 2 ? 1 : 0;
   P.state_cpw = state_wgs > cus ? 2 : 1;
   if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
@@ -428,6 +435,77 @@ gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
 size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
   const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, p->dtype == GDN_BF16, true);
   return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)p->dim * sizeof(float));
+}
+
+// Forward arguments; with_ws: a caller workspace of L.fwd_bytes is required
+// (gdn_fwd), without it none is passed (gdn_fwd_noalloc).
+gdn_status check_fwd_args(const Layout& L, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* h0, const void* o, const float* ht,
+                          const void* workspace, bool with_ws) {
+  const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
+  const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
+  const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
+  const Range rq = strided(q, L.tokens, L.H * L.D, L.ld, L.esz, "q"), rk = strided(k, L.tokens, L.H * L.D, L.ld, L.esz, "k"),
+              rv = strided(v, L.tokens, L.H * L.D, L.ld, L.esz, "v");
+  const size_t wb = with_ws ? L.fwd_bytes : 0;
+  const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {o, qk, "o"}, {workspace, wb, "workspace"}};
+  const Range opt[] = {{h0, sb, "h0"}, {ht, sb, "ht"}};
+  const Range outs[] = {{o, qk, "o"}, {ht, sb, "ht"}, {workspace, wb, "workspace"}};
+  const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {h0, sb, "h0"}};
+  return check_ptrs(req, with_ws ? 7 : 6, opt, 2, outs, 3, ins, 6);
+}
+
+// The forward's launch sequence on stream s, with its workspace at ws.
+gdn_status fwd_launch(const gdn_problem* p, const Layout& L, const void* q, const void* k, const void* v,
+                      const float* g, const float* beta, const float* h0, void* o, float* ht, char* ws,
+                      hipStream_t s) {
+  gdn::Params P = base_params(p, L, ws, s);
+  P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0; P.o = o; P.ht = ht;
+  const int D = (int)L.D;
+  hipError_t e;
+  // (packed input only: for dense input the chunk tables are arithmetic and nothing is launched)
+  if (L.varlen && (e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
+  if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
+  if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
+  if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
+  return GDN_OK;
+}
+
+}  // namespace
+
+// Scratch of gdn_fwd_noalloc: a static device array, one copy on every GPU the
+// library runs on, held until the process ends.  In host code `scratch`
+// names a host-side stand-in; its device address on each GPU is looked up
+// once (hipGetSymbolAddress, with that GPU current) and only that address is
+// handed to kernels.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch_dev[64] = {};
+
+// Device address of GPU dev's copy of `scratch`.
+hipError_t static_scratch(int dev, char** out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!ptr || ((uintptr_t)ptr) % ALIGN) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = reinterpret_cast<char*>(ptr);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -690,36 +768,42 @@ gdn_status gdn_fwd(const gdn_problem* p, const void* q, const void* k, const voi
     Layout L;
     gdn_status st = plan_problem(p, &L);
     if (st != GDN_OK) return st;
-    const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
-    const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
-    const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
-    const Range rq = strided(q, L.tokens, L.H * L.D, L.ld, L.esz, "q"), rk = strided(k, L.tokens, L.H * L.D, L.ld, L.esz, "k"),
-                rv = strided(v, L.tokens, L.H * L.D, L.ld, L.esz, "v");
-    const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
-                         {o, qk, "o"}, {workspace, L.fwd_bytes, "workspace"}};
-    const Range opt[] = {{h0, sb, "h0"}, {ht, sb, "ht"}};
-    const Range outs[] = {{o, qk, "o"}, {ht, sb, "ht"}, {workspace, L.fwd_bytes, "workspace"}};
-    const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {h0, sb, "h0"}};
-    st = check_ptrs(req, 7, opt, 2, outs, 3, ins, 6);
+    st = check_fwd_args(L, q, k, v, g, beta, h0, o, ht, workspace, true);
     if (st != GDN_OK) return st;
     if (workspace && ((uintptr_t)workspace) % ALIGN)
       return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     if (workspace_bytes < L.fwd_bytes)
       return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, L.fwd_bytes);
-
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    gdn::Params P = base_params(p, L, reinterpret_cast<char*>(workspace));
-    P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0; P.o = o; P.ht = ht;
-    const int D = (int)L.D;
-    hipError_t e;
-    // (packed input only: for dense input the chunk tables are arithmetic and nothing is launched)
-    if (L.varlen && (e = timed("plan", s, [&] { return gdn::launch_plan(P, s); })) != hipSuccess) return hip_fail(e, "plan launch");
-    if ((e = timed("fwd_prep", s, [&] { return gdn::launch_fwd_prep(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_prep launch");
-    if ((e = timed("fwd_state", s, [&] { return gdn::launch_fwd_state(P, D, L.bf16, true, s); })) != hipSuccess) return hip_fail(e, "fwd_state launch");
-    if ((e = timed("fwd_out", s, [&] { return gdn::launch_fwd_out(P, D, L.bf16, s); })) != hipSuccess) return hip_fail(e, "fwd_out launch");
-    return GDN_OK;
+    return fwd_launch(p, L, q, k, v, g, beta, h0, o, ht, reinterpret_cast<char*>(workspace),
+                      reinterpret_cast<hipStream_t>(stream));
   } catch (...) {
     return fail(GDN_ERR_HIP, "unexpected exception in gdn_fwd");
+  }
+}
+
+gdn_status gdn_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* h0, void* o, float* ht,
+                           void* stream) {
+  try {
+    Layout L;
+    gdn_status st = plan_problem(p, &L);
+    if (st != GDN_OK) return st;
+    st = check_fwd_args(L, q, k, v, g, beta, h0, o, ht, nullptr, false);
+    if (st != GDN_OK) return st;
+    if (L.fwd_bytes > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+      return fail(GDN_ERR_UNSUPPORTED,
+                  "gdn_fwd_noalloc: the problem needs %zu bytes of scratch, more than the library's static "
+                  "%zu bytes (use gdn_fwd with a workspace)",
+                  L.fwd_bytes, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int dev = 0;
+    hipError_t e = stream_device(s, &dev);
+    if (e != hipSuccess) return hip_fail(e, "gdn_fwd_noalloc: device of the stream");
+    char* ws = nullptr;
+    if ((e = static_scratch(dev, &ws)) != hipSuccess) return hip_fail(e, "gdn_fwd_noalloc: static scratch address");
+    return fwd_launch(p, L, q, k, v, g, beta, h0, o, ht, ws, s);
+  } catch (...) {
+    return fail(GDN_ERR_HIP, "unexpected exception in gdn_fwd_noalloc");
   }
 }
 
@@ -762,7 +846,7 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     char* ws = reinterpret_cast<char*>(workspace);
     // forward context: from the caller's forward workspace, or recomputed here
     char* ctx = fwd_workspace ? const_cast<char*>(reinterpret_cast<const char*>(fwd_workspace)) : ws;
-    gdn::Params P = base_params(p, L, ctx);
+    gdn::Params P = base_params(p, L, ctx, s);
     P.q = q; P.k = k; P.v = v; P.g = g; P.beta = beta; P.h0 = h0;
     P.dO = d_o; P.dht = dht; P.dq = dq; P.dk = dk; P.dv = dv; P.dg = dg; P.dbeta = dbeta; P.dh0 = dh0;
     P.Z = ws + L.Z; P.WnT = ws + L.WnT; P.Ktn = ws + L.Ktn;

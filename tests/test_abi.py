@@ -29,7 +29,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.lib().gdn_abi_version() == 6
+    assert gdn.lib().gdn_abi_version() == 7
     assert gdn.status_string(0) == "GDN_OK"
     assert gdn.status_string(3) == "GDN_ERR_WORKSPACE_TOO_SMALL"
 
@@ -399,3 +399,31 @@ def test_strided_output_over_an_input_is_rejected():
     st = gdn.lib().gdn_bwd(ctypes.byref(p), *(P(x) if x else None for x in ptrs), P(FAKE + (1 << 38)),
                            1, None)
     assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps k" in gdn.last_error_message()
+
+
+def call_fwd_noalloc(p, **over):
+    ptrs, _ = fwd_ptrs(p, **over)
+    P = ctypes.c_void_p
+    st = gdn.lib().gdn_fwd_noalloc(ctypes.byref(p), P(ptrs["q"]), P(ptrs["k"]), P(ptrs["v"]), P(ptrs["g"]),
+                                   P(ptrs["beta"]), P(ptrs["h0"]), P(ptrs["o"]), P(ptrs["ht"]), None)
+    return st, gdn.last_error_message()
+
+
+def test_noalloc_forward_rejects_what_the_static_scratch_cannot_hold():
+    # the allocation-free forward takes its workspace from a 128 MiB static array: problems that
+    # need more are rejected on the host, before any HIP call (so nothing is launched here)
+    limit = 128 * 1024 * 1024
+    L = gdn.lib()
+    big = base_problem(seqlen=16384, heads=16)
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(big)) > limit
+    st, m = call_fwd_noalloc(big)
+    assert st == gdn.GDN_ERR_UNSUPPORTED and "static" in m, (st, m)
+    fits = base_problem(seqlen=4096, heads=16)
+    assert L.gdn_fwd_workspace_bytes(ctypes.byref(fits)) <= limit
+    # argument checks are the forward's (no workspace argument)
+    st, m = call_fwd_noalloc(base_problem(dk=96, dv=96))
+    assert st == gdn.GDN_ERR_UNSUPPORTED, m
+    st, m = call_fwd_noalloc(base_problem(), q=0)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "q is NULL" in m, m
+    st, m = call_fwd_noalloc(base_problem(), o=FAKE)
+    assert st == gdn.GDN_ERR_INVALID_ARGUMENT and "overlaps" in m, m
