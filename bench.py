@@ -26,15 +26,17 @@ if ROOT not in sys.path:
 
 METRIC = "GDN fwd+bwd tokens/s at T=4096,H=16,d=128 bf16; % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ORACLE_THREADS = 16            # the host's CPU share for one GPU
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 C = 64
 
 
 def kernel_bytes(D, E, units, state_units, with_ht=True):
-    """Algorithmic HBM bytes per launch of each kernel: each input it needs
-    read once and each output written once, at storage size.  Per
-    (chunk, head) unit unless noted; state kernels add their per-(sequence,
-    head) state I/O."""
+    """Bytes each kernel reads and writes per launch, counting every tensor it
+    touches once at storage size, the forward/backward context records in the
+    workspace included (the kernels' own data-movement model).  Per (chunk,
+    head) unit unless noted; state kernels add their per-(sequence, head) state
+    I/O."""
     per_unit = {
         # reads K, V (2CD E), g, beta; writes gamma, -W, Kt^T, U (3CD E), T (C^2 fp32)
         "fwd_prep": 5 * C * D * E + 3 * C * 4 + C * C * 4,
@@ -64,16 +66,50 @@ def kernel_bytes(D, E, units, state_units, with_ht=True):
     return out, per_unit
 
 
+def op_bytes(D, E, units, state_units, with_ht=True):
+    """The operator's algorithmic bytes (its inputs read once and its outputs
+    written once, nothing of the workspace), per launch of the kernel that
+    moves them.  Per token and head: the forward reads q, k, v (3DE) and g,
+    beta and writes o (DE): 1,032 B at D = 128 in bf16; the backward reads q,
+    k, v, dO (4DE) and g, beta and writes dq, dk, dv (3DE) and dg, dbeta:
+    1,808 B.  The backward's bytes all go through bwd_grad (which reads g as
+    the chunk decays); of the forward's, fwd_prep reads k, v, g, beta and
+    fwd_out reads q, k and writes o (k is an input of both); the state passes
+    move only the states."""
+    per_tok = {
+        "fwd_prep": 2 * D * E + 8,
+        "fwd_out": 3 * D * E,
+        "bwd_prep": 0,
+        "bwd_grad": 7 * D * E + 16,
+        "fwd_state": 0,
+        "bwd_state": 0,
+    }
+    per_unit = {k: v * C for k, v in per_tok.items()}
+    out = {k: v * units for k, v in per_unit.items()}
+    if with_ht:
+        out["fwd_state"] += state_units * D * D * 4
+    return out, per_unit
+
+
 def kernel_flops(D, units):
     """Algorithmic flops per launch (2mnk per product, triangular operands at
-    one half, no recompute, no transposes)."""
+    one half, no recompute, no transposes), split by kernel so that the six
+    sum to the operator's 5C^2 D + 6C D^2 + C^3/3 (forward) and 12C^2 D +
+    12C D^2 + 2C^3/3 (backward) per chunk: 438,272 per token and head at
+    C = 64, D = 128."""
     per_unit = {
+        # K K^T (lower), the solve, W = T Xw, U = T Xu
         "fwd_prep": C * C * D + C ** 3 // 3 + 2 * C * C * D,
+        # W h, Kt^T V'
         "fwd_state": 4 * C * D * D,
+        # Q h, Q K^T (lower), P V'
         "fwd_out": 2 * C * D * D + 2 * C * C * D,
+        # P = Q K^T recomputed (lower), P^T dO, Z = (Gam Q)^T dO
         "bwd_prep": 2 * C * C * D + 2 * C * D * D,
+        # Kt H', W^T dV'
         "bwd_state": 4 * C * D * D,
-        "bwd_grad": 8 * C * D * D + 8 * C * C * D + 2 * C ** 3 // 3,
+        # dP, dQ, dK, dW, dT, T^T dW, T^T dU, dA, K K^T and (E + E^T) K
+        "bwd_grad": 10 * C * C * D + 6 * C * D * D + 2 * C ** 3 // 3,
     }
     return {k: v * units for k, v in per_unit.items()}
 
@@ -115,7 +151,7 @@ def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
     import numpy as np
 
     import oracle
-    nthreads = min(16, os.cpu_count() or 1)
+    nthreads = min(ORACLE_THREADS, os.cpu_count() or 1)
     used = oracle.threads_used(x["N"], x["H"], nthreads)
     reps = 0
     t0 = time.perf_counter()
@@ -139,11 +175,14 @@ def cpu_baseline(x, budget_s=10.0, max_reps=20, l2=False, gn=None, cv=None):
         if el >= budget_s or reps >= max_reps:
             break
     tokens = x["B"] * x["T"]
-    return {"value": reps * tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": "%d complete fwd+bwd passes of the B=1,T=4096,H=16,d=128 workload%s%s "
-                      "(fp64 token recurrence; %.1f s wall)"
-                      % (reps, " with the conv1d" if cv is not None else "",
-                         " with the gated RMSNorm" if gn is not None else "", el)}
+    out = {"value": reps * tokens / el, "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": "%d complete fwd+bwd passes of the B=1,T=4096,H=16,d=128 workload%s%s "
+                     "(fp64 token recurrence; %.1f s wall)"
+                     % (reps, " with the conv1d" if cv is not None else "",
+                        " with the gated RMSNorm" if gn is not None else "", el)}
+    out.update(cpu_info())
+    out["threads_note"] = "threads = min(%d, N*H): the host's CPU share for one GPU" % ORACLE_THREADS
+    return out
 
 
 class HipEvents:
@@ -186,16 +225,22 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=3):
     print("copy calibration: %d x %d bytes" % (reps, nbytes), file=sys.stderr)
 
 
-def measured_peak_gbs(torch, dev, nbytes=1 << 30, reps=5):
-    """HBM bandwidth that library kernels reach on this GPU, the measured peak beside the
-    vendor one: a 1 GiB device-to-device copy (bytes read plus written) and a 1 GiB fp32
-    sum (bytes read), each the median of `reps`.  Returns (best, copy, read) in GB/s."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    a.fill_(1)
-    af = a.view(torch.float32)
+def measured_peaks(torch, dev, reps=5):
+    """Peaks of this GPU measured by the microbenchmarks of libgdn_peak.so (dense bf16
+    MFMA issue on independent accumulators; a 2 GiB streaming copy and read, 16 bytes
+    per lane), each the median of `reps` runs timed with events on the current stream.
+    Returns {"mfma_bf16_TFLOPs", "hbm_copy_GBps", "hbm_read_GBps"}."""
+    import numpy as np
+    path = os.path.join(ROOT, "linear_attention_gated_amd", "libgdn_peak.so")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.gdn_peak_mfma_bf16.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+    lib.gdn_peak_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P]
+    lib.gdn_peak_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_int, P]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = P(torch.cuda.current_stream(dev).cuda_stream)
 
-    def med(fn, moved):
+    def med(fn):
         fn()
         ts = []
         for _ in range(reps):
@@ -205,12 +250,43 @@ def measured_peak_gbs(torch, dev, nbytes=1 << 30, reps=5):
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e-3)
-        return moved / sorted(ts)[reps // 2] / 1e9
+        return float(np.median(ts))
 
-    cp = med(lambda: b.copy_(a), 2 * nbytes)
-    rd = med(lambda: af.sum(), nbytes)
-    del a, b, af
-    return max(cp, rd), cp, rd
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("peak microbenchmark launch failed (hipError %d)" % rc)
+
+    blocks, iters = 4 * cus, 2000       # four 4-wave workgroups per CU: four waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t = med(lambda: ok(lib.gdn_peak_mfma_bf16(P(out.data_ptr()), blocks, iters, stream)))
+    mfma = blocks * 4 * iters * 8 * 16384 / t / 1e12
+    nbytes = 2 << 30
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    sink = torch.empty(8 * cus * 256, dtype=torch.int32, device=dev)
+    tc = med(lambda: ok(lib.gdn_peak_copy(P(a.data_ptr()), P(b.data_ptr()), nbytes, 8 * cus, stream)))
+    tr = med(lambda: ok(lib.gdn_peak_read(P(a.data_ptr()), nbytes, P(sink.data_ptr()), 8 * cus, stream)))
+    del a, b, sink, out
+    return {"mfma_bf16_TFLOPs": round(mfma, 1), "hbm_copy_GBps": round(2 * nbytes / tc / 1e9, 1),
+            "hbm_read_GBps": round(nbytes / tr / 1e9, 1)}
+
+
+def cpu_info():
+    """CPU model and counts of the host (the oracle's baseline runs on it)."""
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": aff}
 
 
 def step_percentiles(torch, dev, step, n, flush_bytes):
@@ -284,11 +360,11 @@ def decode_bench(args):
                     "traffic": traffic_for("recurrent", "hbm_traffic_decode_N%d_T1_H16_d128_bf16.txt" % N),
                     "algorithmic_bytes_per_launch": byts, "units_per_launch": N * H,
                     "bytes_per_unit": byts // (N * H), "avg_us": round(avg_us, 2)}
-        best, cp, rd = measured_peak_gbs(torch, dev)
-        roofline["measured_peak"] = round(best, 1)
+        pk = measured_peaks(torch, dev)
+        best = max(pk["hbm_copy_GBps"], pk["hbm_read_GBps"])
+        roofline["measured_peak"] = best
         roofline["frac_of_measured_peak"] = round(a_gbs / best, 4)
-        roofline["measured_copy_GBps"] = round(cp, 1)
-        roofline["measured_read_GBps"] = round(rd, 1)
+        roofline["measured_peaks"] = pk
         # back to back, part of the state pool is still in the memory-side cache
         # from the previous call; "cold" writes 1 GiB before each call (as the
         # rest of a model would between two decoding steps)
@@ -302,7 +378,7 @@ def decode_bench(args):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        nthreads = min(16, os.cpu_count() or 1)
+        nthreads = min(ORACLE_THREADS, os.cpu_count() or 1)
         reps, c0 = 0, time.perf_counter()
         while True:
             oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], nthreads=nthreads)
@@ -313,6 +389,7 @@ def decode_bench(args):
         cpu = {"value": reps * N / ce, "unit": "tokens/s", "cores": oracle.threads_used(N, H, nthreads),
                "kind": "oracle", "sample": "%d complete decode steps of the same workload (fp64 token "
                "recurrence; %.1f s wall)" % (reps, ce)}
+        cpu.update(cpu_info())
     out = {
         "metric": "GDN recurrent decode tokens/s", "value": round(N * args.steps / el, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -323,6 +400,98 @@ def decode_bench(args):
     }
     if roofline is not None:
         out["step_timing"] = timing
+    print(json.dumps(out), flush=True)
+
+
+def config_sweep(args):
+    """Every workload configuration once: the GPU path's time per call (median of 20, warm:
+    calls back to back; cold: 1 GiB written before each call, outside the events), its
+    error against the fp64 oracle, and the oracle's own time on the host (median of 3 on
+    the CPU share of one GPU, plus one single-thread run of the T=4096 forward).  Prints
+    one JSON line; not the headline."""
+    import numpy as np
+    import torch
+
+    import gdn_inputs as gi
+    import linear_attention_gated_amd as gdn
+    import oracle
+
+    dev = torch.device("cuda:0")
+    nthreads = min(ORACLE_THREADS, os.cpu_count() or 1)
+
+    def t(a, dt):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    def err(a, ref, kind):
+        a = a.detach().double().cpu().numpy()
+        if kind == "frob":
+            return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
+        return float(np.max(np.abs(a - ref)) / np.max(np.abs(ref)))
+
+    def med_wall(fn, n=3):
+        ts = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            r = fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)), r
+
+    rows = {}
+    for name in ("c0", "c1", "c2", "c3", "c4"):
+        cfg = gi.CONFIGS[name]
+        x = gi.make_inputs(cfg, 0)
+        dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+        q, k, v = (t(x[n_], dt) for n_ in ("q", "k", "v"))
+        g, beta, h0 = t(x["g"], torch.float32), t(x["beta"], torch.float32), t(x["h0"], torch.float32)
+        cu = None if x["cu_seqlens"] is None else (torch.from_numpy(x["cu_seqlens"]), t(x["cu_seqlens"], torch.int32))
+        tokens = x["B"] * x["T"]
+        p = gdn.make_problem(q, v, cu_host=None if cu is None else cu[0], cu_dev=None if cu is None else cu[1])
+        wsf = torch.empty(gdn.lib().gdn_fwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+        if cfg.with_grad:
+            do = t(x["do"], dt)
+            wsb = torch.empty(gdn.lib().gdn_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+
+            def call():
+                o, ht, ctx = gdn.fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu, return_context=True,
+                                     workspace=wsf)
+                return (o, ht) + tuple(gdn.bwd(q, k, v, g, beta, do, initial_state=h0, cu_seqlens=cu,
+                                               context=ctx, workspace=wsb))
+        else:
+            def call():
+                return gdn.fwd(q, k, v, g, beta, initial_state=h0, cu_seqlens=cu, workspace=wsf)
+        got = call()
+        torch.cuda.synchronize()
+        warm = step_percentiles(torch, dev, call, 20, 0)
+        cold = step_percentiles(torch, dev, call, 20, 1 << 30)
+        ot, ref = med_wall(lambda: oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"],
+                                              cu_seqlens=x["cu_seqlens"], nthreads=nthreads))
+        errs = {"o_maxrel": err(got[0], ref[0], "maxrel")}
+        errs["ht_maxrel" if cfg.dtype == "fp32" else "ht_frob"] = err(got[1], ref[1], "maxrel" if cfg.dtype == "fp32" else "frob")
+        if cfg.with_grad:
+            bt, rg = med_wall(lambda: oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["h0"],
+                                                 cu_seqlens=x["cu_seqlens"], nthreads=nthreads))
+            ot += bt
+            for n_, a, b in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got[2:], rg):
+                errs[n_ + "_maxrel"] = err(a, b, "maxrel")
+                errs[n_ + "_frob"] = err(a, b, "frob")
+        row = {"pass": "fwd+bwd" if cfg.with_grad else "fwd", "tokens": tokens, "H": x["H"], "d": x["dk"],
+               "dtype": cfg.dtype, "sequences": x["N"],
+               "gpu_warm_ms": warm["median_ms"], "gpu_cold_ms": cold["median_ms"],
+               "gpu_warm_tokens_per_s": round(tokens / (warm["median_ms"] * 1e-3), 1),
+               "gpu_cold_tokens_per_s": round(tokens / (cold["median_ms"] * 1e-3), 1),
+               "oracle_s": round(ot, 3), "oracle_tokens_per_s": round(tokens / ot, 1),
+               "oracle_threads": oracle.threads_used(x["N"], x["H"], nthreads),
+               "errors": {k_: float("%.3e" % v_) for k_, v_ in errs.items()}}
+        if name == "c1":
+            st, _ = med_wall(lambda: oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], nthreads=1), n=1)
+            row["oracle_single_thread_s"] = round(st, 3)
+            row["oracle_single_thread_tokens_per_s"] = round(tokens / st, 1)
+        rows[cfg.name] = row
+        print("config %s: %s" % (cfg.name, json.dumps(row)), file=sys.stderr, flush=True)
+        del x, q, k, v, got, ref
+    out = {"metric": "per-configuration GPU time, parity and oracle time", "unit": "tokens/s", "n_gpus": 1,
+           "higher_is_better": True, "data": "synthetic", "configs": rows, "host": cpu_info(),
+           "oracle_threads_max": nthreads, "sources_sha": sources_sha()}
     print(json.dumps(out), flush=True)
 
 
@@ -345,6 +514,9 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="instead: the recurrent (decoding) forward, N sequences of one new token "
                          "each with their states in place (H=16, d=128, bf16)")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead: every workload configuration once (GPU time warm and cold, error "
+                         "against the oracle, the oracle's own time); not the headline")
     ap.add_argument("--no-profile-pass", action="store_true",
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
@@ -355,6 +527,8 @@ def main():
         sys.exit(2)
     if args.decode:
         return decode_bench(args)
+    if args.configs:
+        return config_sweep(args)
 
     import numpy as np
     import torch
@@ -456,21 +630,32 @@ def main():
             num[name] = num.get(name, 0) + 1
         evs.close()
         kbytes, per_unit_b = kernel_bytes(D, 2, units, B * H)
+        obytes, per_unit_o = op_bytes(D, 2, units, B * H)
         kflops = kernel_flops(D, units)
         for name in tot:
             avg_us = 1e3 * tot[name] / num[name]
             kernels[name] = {"avg_us": round(avg_us, 2), "launches_per_step": num[name] / args.steps}
+            if obytes.get(name):
+                kernels[name]["op_GBps"] = round(obytes[name] / (avg_us * 1e-6) / 1e9, 1)
             if name in kbytes:
-                kernels[name]["achieved_GBps"] = round(kbytes[name] / (avg_us * 1e-6) / 1e9, 1)
+                kernels[name]["moved_GBps"] = round(kbytes[name] / (avg_us * 1e-6) / 1e9, 1)
             if name in kflops:
                 kernels[name]["achieved_TFLOPs"] = round(kflops[name] / (avg_us * 1e-6) / 1e12, 2)
-        dom = max((k_ for k_ in tot if k_ in kbytes), key=lambda k_: tot[k_])
-        a_gbs = kbytes[dom] / (1e-3 * tot[dom] / num[dom]) / 1e9
+        # the dominant kernel (longest), against the HBM roofline by the operator's own bytes
+        dom = max((k_ for k_ in tot if obytes.get(k_)), key=lambda k_: tot[k_])
+        avg_s = 1e-3 * tot[dom] / num[dom]
+        a_gbs = obytes[dom] / avg_s / 1e9
         tr = traffic_for(dom)
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": tr, "algorithmic_bytes_per_launch": kbytes[dom],
-                    "units_per_launch": units, "bytes_per_unit": per_unit_b[dom]}
+                    "traffic": tr, "algorithmic_bytes_per_launch": obytes[dom],
+                    "units_per_launch": units, "bytes_per_unit": per_unit_o[dom],
+                    "bytes_per_token_head": per_unit_o[dom] // C, "avg_us": round(avg_s * 1e6, 2),
+                    "traffic_over_algorithmic": None if tr is None else round(tr / obytes[dom], 3),
+                    # every tensor the kernel moves, its workspace records included
+                    "moved_model": {"bytes_per_unit": per_unit_b[dom], "bytes_per_launch": kbytes[dom],
+                                    "GBps": round(kbytes[dom] / avg_s / 1e9, 1),
+                                    "frac": round(kbytes[dom] / avg_s / 1e9 / HBM_PEAK_GBS, 4)}}
         # whole step: the operator's own input/output bytes per token and head
         step_bytes = (1032 + 1808) * B * T * H + B * H * D * D * 4
         step_flops = (140629 + 297643) * B * T * H
@@ -492,12 +677,35 @@ def main():
     if not args.no_profile_pass:
         timing = {"warm": step_percentiles(torch, dev, step, 30, 0),
                   "cold": step_percentiles(torch, dev, step, 30, 1 << 30)}
-        best, cp, rd = measured_peak_gbs(torch, dev)
+        for tm in timing.values():
+            tm["tokens_per_s_at_median"] = round(B * T / (tm["median_ms"] * 1e-3), 1)
+        pk = measured_peaks(torch, dev)
+        best = max(pk["hbm_copy_GBps"], pk["hbm_read_GBps"])
         if roofline is not None:
-            roofline["measured_peak"] = round(best, 1)
+            roofline["measured_peak"] = best
             roofline["frac_of_measured_peak"] = round(roofline["achieved"] / best, 4)
-            roofline["measured_copy_GBps"] = round(cp, 1)
-            roofline["measured_read_GBps"] = round(rd, 1)
+            roofline["measured_peaks"] = pk
+        if step_roof is not None:
+            step_roof["mfma_frac_of_measured_peak"] = round(
+                step_roof["achieved_TFLOPs"] / pk["mfma_bf16_TFLOPs"], 5)
+
+    # the same step with gdn_bwd recomputing the forward context (no saved context), as the
+    # backward runs when the forward's workspace is not kept
+    recompute = None
+    if not args.no_profile_pass and cv is None and gn is None:
+        def step_rc():
+            gdn.fwd(q, k, v, g, beta, workspace=wsf, qk_l2norm=l2)
+            return gdn.bwd(q, k, v, g, beta, do, need_dh0=False, workspace=wsb, qk_l2norm=l2)
+        for _ in range(args.warmup):
+            step_rc()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            step_rc()
+        torch.cuda.synchronize()
+        el_rc = time.perf_counter() - t1
+        recompute = {"ms_per_step": round(1e3 * el_rc / args.steps, 4),
+                     "tokens_per_s": round(B * T * args.steps / el_rc, 1)}
 
     if args.copy_calib:
         copy_calibration(torch, dev)
@@ -513,7 +721,7 @@ def main():
                    "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,
-        "step_timing": timing,
+        "step_timing": timing, "recompute_step": recompute,
         "sources_sha": sources_sha(),
     }
     print(json.dumps(out), flush=True)
