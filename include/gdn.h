@@ -58,9 +58,10 @@
  * gdn_last_error_message() returns a thread-local description of the last
  * non-OK return.  Nothing aborts, prints or throws across this interface.
  *
- * Supported set: d_k = d_v in {64, 128}, chunk = 64, dtype fp32 or bf16,
- * any T >= 0 (a problem with no tokens enqueues only state copies).
- * Anything else returns GDN_ERR_UNSUPPORTED.
+ * Supported set (gdn_fwd, gdn_bwd): d_k = d_v in {64, 128}, chunk = 64, dtype
+ * fp32 or bf16 (forward and backward in each), any T >= 0 (a problem with no
+ * tokens enqueues only state copies).  Anything else returns
+ * GDN_ERR_UNSUPPORTED.
  *
  * In-operator L2 normalisation (qk_l2norm = 1) is the usual prologue of the
  * GDN layer (Qwen3.5 normalises q and k per head before the recurrence).

@@ -754,7 +754,7 @@ size_t gdn_fwd_workspace_bytes(const gdn_problem* p) {
 size_t gdn_bwd_workspace_bytes(const gdn_problem* p) {
   try {
     Layout L;
-    if (plan_problem(p, &L) != GDN_OK || (!L.bf16 && L.D == 128)) return 0;
+    if (plan_problem(p, &L) != GDN_OK) return 0;
     return L.bwd_bytes;
   } catch (...) {
     return 0;
@@ -815,8 +815,6 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     Layout L;
     gdn_status st = plan_problem(p, &L);
     if (st != GDN_OK) return st;
-    if (!L.bf16 && L.D == 128)
-      return fail(GDN_ERR_UNSUPPORTED, "backward in fp32 supports head dim 64 only (use bf16 for 128)");
     const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
     const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
     const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);

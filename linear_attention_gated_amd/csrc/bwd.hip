@@ -247,12 +247,14 @@ struct BwdRing {
   // with two compute waves, at most two loaders and three slots
   static constexpr int S = CPW == 1 ? ring_slots(SLOT) : (ring_slots(SLOT) < 3 ? ring_slots(SLOT) : 3);
   static constexpr int WAVES = CPW + S - 1;   // compute waves, then loaders
+  static constexpr bool FITS = S * SLOT <= 160 * 1024;
   static_assert(WAVES <= 4, "one wave per SIMD");
 };
 
 template <typename E, int D, bool ROT, int CPW>
 __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(Params p) {
   using R = BwdRing<E, D, CPW>;
+  static_assert(R::FITS, "the ring fits the LDS");
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
   __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
@@ -440,23 +442,32 @@ struct BwdGradSmem {
   static constexpr int PMAT = 64 * LDE * (int)sizeof(E);
   static constexpr int RECB = REC * (int)sizeof(E);
   static constexpr int SET = 4 * KB * RECB;             // records of a 64 x D fragment set
-  static constexpr int UNI = (2 * SET > MAT + 6 * RECB) ? 2 * SET : MAT + 6 * RECB;  // dV'^T + dW, later M1 + (dP*D)^T
   static constexpr int TILE = NatTile<E, D>::BYTES;
-  static constexpr int oEE = 0;                         // E + E^T, operand type
-  static constexpr int oT = oEE + PMAT;                 // T, from the forward context
+  // Q and K are staged as natural tiles where they fit; in fp32 at D = 128
+  // their fragments are read from global memory instead (the 64 KB of tiles
+  // would take the workgroup past the 160 KB of LDS), and the gradients are
+  // stored straight from the waves (a staged 64 x 128 fp32 tile needs 32 KB).
+  static constexpr bool kStageQK = !(sizeof(E) == 4 && D == 128);
+  static constexpr int QKT = kStageQK ? TILE : 0;
+  // region U: dV'^T + dW (through dT), then M1 | (dP*D)^T records | E + E^T
+  static constexpr int UNI_A = 2 * SET, UNI_B = MAT + 6 * RECB + PMAT;
+  static constexpr int UNI = UNI_A > UNI_B ? UNI_A : UNI_B;
+  static constexpr int oT = 0;                          // T, from the forward context
   static constexpr int odP = oT + MAT;                  // dP * D
   static constexpr int oVt = odP + PMAT;
-  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1 | sPDt
+  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1 | sPDt | sEE
   static constexpr int oPDt = oU + MAT;
+  static constexpr int oEE = oPDt + 6 * RECB;           // E + E^T, operand type
   static constexpr int odTt = oU + UNI;
   static constexpr int oQ = odTt + MAT;                 // staged natural tiles
-  static constexpr int oK = oQ + TILE;
-  static constexpr int oSm = oK + TILE;
+  static constexpr int oK = oQ + QKT;
+  static constexpr int oSm = oK + QKT;
   static constexpr int SMALL = (64 * 2 + NW * 64 * 2 + NW * 2) * 4;
   static constexpr int BASE = oSm + SMALL;
   static constexpr bool kStageDO = BASE + TILE <= 160 * 1024;
   static constexpr int odO = BASE;
   static constexpr int BYTES = BASE + (kStageDO ? TILE : 0);
+  static_assert(BYTES + 128 * 4 <= 160 * 1024, "bwd_grad fits the LDS of a workgroup");
 };
 
 template <typename E, int D, bool NORM>
@@ -510,8 +521,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   auto gnat = [&](const E* X, size_t xb, size_t xr, int row, int kb) {
     return row < L ? load_frag_row<E>(X + xb + (size_t)row * xr + 32 * kb, lg) : zero_frag<E>();
   };
-  auto qf = [&](int ab, int kb) { return tile_frag<E, D>(tQ, ab, kb, li, lg); };
-  auto kf = [&](int ab, int kb) { return tile_frag<E, D>(tK, ab, kb, li, lg); };
+  __shared__ float s_inv[NORM ? 128 : 1];   // sign-encoded reciprocal norms of the q, k rows
+  // natural fragments of Q and K (normalised rows with NORM): from the staged
+  // tiles, or from global memory, scaled here
+  auto qf = [&](int ab, int kb) {
+    if constexpr (S::kStageQK) {
+      return tile_frag<E, D>(tQ, ab, kb, li, lg);
+    } else {
+      const frag_t<E> f = gnat(Q, xbase, xrow, 16 * ab + li, kb);
+      if constexpr (NORM) return scale_frag<E>(f, fabsf(s_inv[16 * ab + li]));
+      else return f;
+    }
+  };
+  auto kf = [&](int ab, int kb) {
+    if constexpr (S::kStageQK) {
+      return tile_frag<E, D>(tK, ab, kb, li, lg);
+    } else {
+      const frag_t<E> f = gnat(K, xbase, xrow, 16 * ab + li, kb);
+      if constexpr (NORM) return scale_frag<E>(f, fabsf(s_inv[64 + 16 * ab + li]));
+      else return f;
+    }
+  };
   auto of = [&](int ab, int kb) {
     if constexpr (S::kStageDO) return tile_frag<E, D>(tO, ab, kb, li, lg);
     else return gnat(dO, base, rowstride, 16 * ab + li, kb);
@@ -572,7 +602,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   constexpr unsigned long long TREC_LIST = NW == 8 ? pack_owned<12, 8, 2>(TREC_OWN8) : pack_owned<12, 4, 3>(RREC4);
   static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
-  __shared__ float s_inv[NORM ? 128 : 1];   // sign-encoded reciprocal norms of the q, k rows
   // value rows of this wave's dT tiles, read with the setup's reads (used
   // several phases later)
   constexpr int NTT = (10 + NW - 1) / NW;   // dT tiles per wave, at most
@@ -583,8 +612,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H);
-    sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    if constexpr (S::kStageQK) {
+      sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H);
+      sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    }
+    float inv_row = 0.f;   // unstaged: thread r < 128 fetches the scale of q row r or k row r - 64
+    if constexpr (NORM && !S::kStageQK) {
+      if (tid < 128) {
+        const int r = tid & 63;
+        inv_row = (tid < 64 ? p.qinv : p.kinv)[nb + (size_t)(r < L ? r : 0) * H];
+      }
+    }
     if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
 #pragma unroll
     for (int k = 0; k < NTT; ++k) {
@@ -607,11 +645,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       s_gam[lane] = gv;
       s_beta[lane] = bv;
     }
-    sq.store(tQ, tid);
-    sk.store(tK, tid);
-    if constexpr (NORM) {
-      sq.store_scales(s_inv, tid);
-      sk.store_scales(s_inv + 64, tid);
+    if constexpr (S::kStageQK) {
+      sq.store(tQ, tid);
+      sk.store(tK, tid);
+      if constexpr (NORM) {
+        sq.store_scales(s_inv, tid);
+        sk.store_scales(s_inv + 64, tid);
+      }
+    } else if constexpr (NORM) {
+      if (tid < 128) s_inv[tid] = inv_row;
     }
     if constexpr (S::kStageDO) so.store(tO, tid);
 #pragma unroll
@@ -903,15 +945,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // normalised, in Q's tile (free after the last barrier); dv in K's tile.
   constexpr int RB = D * (int)sizeof(E);   // bytes of a staged row
   constexpr int PPR = RB / 16;             // 16-byte pieces per row
-  static_assert(64 * RB <= S::MAT && 64 * RB <= S::TILE, "a staged output tile fits its region");
-  char* stq = reinterpret_cast<char*>(sT);
-  char* stk = norm ? tQ : reinterpret_cast<char*>(sM1);
-  char* stv = tK;
-  // columns 16 w + 4 lg .. + 3 of row r (this lane's four values) into a staging tile
+  constexpr bool kStageOut = S::kStageQK;
+  static_assert(!kStageOut || (64 * RB <= S::MAT && 64 * RB <= S::TILE), "a staged output tile fits its region");
+  // staging regions, or (unstaged) the gradient tensors themselves
+  char* stq = kStageOut ? reinterpret_cast<char*>(sT) : reinterpret_cast<char*>(p.dq);
+  char* stk = kStageOut ? (norm ? tQ : reinterpret_cast<char*>(sM1)) : reinterpret_cast<char*>(p.dk);
+  char* stv = kStageOut ? tK : reinterpret_cast<char*>(p.dv);
+  // columns 16 w + 4 lg .. + 3 of row r (this lane's four values) into a
+  // staging tile, or straight to row r of the gradient (rows < L only)
   auto stage4 = [&](char* st, int r, f32x4 x) {
     const int byte = (16 * w + 4 * lg) * (int)sizeof(E);
-    const int pc = (byte >> 4) ^ (r % PPR);
-    *reinterpret_cast<quad_t<E>*>(st + r * RB + 16 * pc + (byte & 15)) = to_quad<E>(x);
+    if constexpr (kStageOut) {
+      const int pc = (byte >> 4) ^ (r % PPR);
+      *reinterpret_cast<quad_t<E>*>(st + r * RB + 16 * pc + (byte & 15)) = to_quad<E>(x);
+    } else {
+      if (r < L) store_quad_nt<E>(reinterpret_cast<E*>(st + (xbase + (size_t)r * xrow) * sizeof(E) + byte), x);
+    }
   };
   f32x4 dqh[4], dkh[4], qn4[4], kn4[4];
   // dx for rows 16 rb + li of this wave's columns (rows above the floor:
@@ -1102,7 +1151,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // would be written back in the middle of later kernels' reads
   static_assert((64 * PPR) % NT == 0, "the staged rows divide over the threads");
 #pragma unroll
-  for (int e0 = 0; e0 < 64 * PPR; e0 += NT) {
+  for (int e0 = 0; e0 < (kStageOut ? 64 * PPR : 0); e0 += NT) {
     const int e = e0 + tid, r = e / PPR, pc = e - r * PPR;
     if (r < L) {
       const int off = r * RB + 16 * (pc ^ (r % PPR));
@@ -1153,9 +1202,13 @@ static hipError_t bwd_state_t(const Params& p, hipStream_t s) {
   if (p.N * p.H == 0) return hipSuccess;
   Params a = p;
   void* args[] = {&a};
-  if (p.state_cpw == 2)
-    return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true, 2> : (const void*)k_bwd_state<E, D, false, 2>,
-                           dim3(state_grid(p.N * p.H, D, 2)), dim3(64 * BwdRing<E, D, 2>::WAVES), args, 0, s);
+  // two column blocks per workgroup (a grid past one round; always with rotated
+  // reads) where the ring's slots for them fit the LDS
+  if constexpr (BwdRing<E, D, 2>::FITS) {
+    if (p.state_cpw == 2)
+      return hipLaunchKernel((const void*)k_bwd_state<E, D, true, 2>, dim3(state_grid(p.N * p.H, D, 2)),
+                             dim3(64 * BwdRing<E, D, 2>::WAVES), args, 0, s);
+  }
   return hipLaunchKernel(p.dma_rot ? (const void*)k_bwd_state<E, D, true, 1> : (const void*)k_bwd_state<E, D, false, 1>,
                          dim3(state_grid(p.N * p.H, D)), dim3(64 * BwdRing<E, D, 1>::WAVES), args, 0, s);
 }
@@ -1167,8 +1220,6 @@ static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {
   return hipLaunchKernel(p.qk_l2norm ? (const void*)k_bwd_grad<E, D, true> : (const void*)k_bwd_grad<E, D, false>, dim3(p.NC * p.H), dim3(64 * (D / 16)), args, 0, s);
 }
 
-// fp32 with D = 128 needs more LDS than a workgroup has for the gradient
-// kernel; the host rejects that combination before launching anything.
 #define GDN_BWD_DISPATCH(fn, ...)                                    \
   do {                                                               \
     if (is_bf16) {                                                   \
@@ -1176,6 +1227,7 @@ static hipError_t bwd_grad_t(const Params& p, hipStream_t s) {
       if (D == 128) return fn<bf16, 128>(__VA_ARGS__);               \
     } else {                                                         \
       if (D == 64) return fn<float, 64>(__VA_ARGS__);                \
+      if (D == 128) return fn<float, 128>(__VA_ARGS__);              \
     }                                                                \
     return hipErrorInvalidValue;                                     \
   } while (0)

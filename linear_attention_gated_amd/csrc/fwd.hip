@@ -338,12 +338,14 @@ struct FwdRing {
   // with two compute waves, at most two loaders and three slots
   static constexpr int S = CPW == 1 ? ring_slots(SLOT) : (ring_slots(SLOT) < 3 ? ring_slots(SLOT) : 3);
   static constexpr int WAVES = CPW + S - 1;   // compute waves, then loaders
+  static constexpr bool FITS = S * SLOT <= 160 * 1024;
   static_assert(WAVES <= 4, "one wave per SIMD");
 };
 
 template <typename E, int D, bool ROT, int CPW>
 __global__ __launch_bounds__((64 * FwdRing<E, D, CPW>::WAVES)) void k_fwd_state(Params p, int write_ht) {
   using R = FwdRing<E, D, CPW>;
+  static_assert(R::FITS, "the ring fits the LDS");
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
   __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
@@ -651,9 +653,13 @@ static hipError_t fwd_state_t(const Params& p, bool write_ht, hipStream_t s) {
   Params a = p;
   int wh = write_ht ? 1 : 0;
   void* args[] = {&a, &wh};
-  if (p.state_cpw == 2)
-    return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true, 2> : (const void*)k_fwd_state<E, D, false, 2>,
-                           dim3(state_grid(p.N * p.H, D, 2)), dim3(64 * FwdRing<E, D, 2>::WAVES), args, 0, s);
+  // two column blocks per workgroup (a grid past one round; always with rotated
+  // reads) where the ring's slots for them fit the LDS
+  if constexpr (FwdRing<E, D, 2>::FITS) {
+    if (p.state_cpw == 2)
+      return hipLaunchKernel((const void*)k_fwd_state<E, D, true, 2>, dim3(state_grid(p.N * p.H, D, 2)),
+                             dim3(64 * FwdRing<E, D, 2>::WAVES), args, 0, s);
+  }
   return hipLaunchKernel(p.dma_rot ? (const void*)k_fwd_state<E, D, true, 1> : (const void*)k_fwd_state<E, D, false, 1>,
                          dim3(state_grid(p.N * p.H, D)), dim3(64 * FwdRing<E, D, 1>::WAVES), args, 0, s);
 }

@@ -59,8 +59,8 @@ struct Params {
   float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;
   void *Z, *dVl;
-  int dma_rot;
-  int state_cpw;           // 16-column blocks of d_v per state-pass workgroup: 1 or 2             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
+  int dma_rot;             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
+  int state_cpw;           // 16-column blocks of d_v per state-pass workgroup: 1 or 2 (2 implies dma_rot)
 };
 
 // Chunk c: (first token, length, sequence, index in sequence).  Dense

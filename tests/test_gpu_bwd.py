@@ -59,6 +59,9 @@ SMALL = [
     ("fp32", 64, 1, 200, 3, 0.0, False, 0.7),
     ("fp32", 64, 2, 130, 2, 0.3, True, 1.0),
     ("fp32", 64, 1, 1, 2, 0.5, True, 1.0),
+    ("fp32", 128, 1, 200, 2, 0.2, True, 0.8),
+    ("fp32", 128, 2, 65, 1, 0.0, False, 1.0),
+    ("fp32", 128, 1, 1, 1, 0.3, True, 1.0),
     ("bf16", 64, 2, 300, 2, 0.0, False, 1.0),
     ("bf16", 128, 1, 257, 3, 0.2, True, 1.0),
     ("bf16", 128, 1, 63, 1, 0.0, False, 0.125),
@@ -75,7 +78,7 @@ def test_small_dense(dtype, d, B, T, H, h0, with_dht, scale):
     compare(x, dht=dht, scale=scale, label="small")
 
 
-@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128), ("fp32", 128)])
 def test_small_varlen(dtype, d):
     cfg = small_cfg(dtype, d, H=2, h0_std=0.3, with_grad=True)
     x = gi.make_inputs(cfg, 12, lengths=[1, 0, 63, 64, 65, 130, 0, 7])
@@ -104,13 +107,17 @@ def test_bitwise_deterministic_backward():
         assert np.array_equal(u, v), n
 
 
-def test_fp32_head_dim_128_backward_rejected():
-    cfg = small_cfg("fp32", 128, T=64, H=1, with_grad=True)
+def test_fp32_head_dim_128_config0_shape_and_recompute():
+    # fp32 at d = 128: the gradient kernel reads Q and K from global memory and stores its
+    # outputs directly (the staged tiles would not fit the LDS); T = 256, H = 2 as the fp32
+    # workload, with h0 and dht; recomputing the forward context gives the same bits
+    cfg = gi.Config("fp32_d128_bwd", 1, 256, 2, 128, 128, "fp32", h0_std=0.1, with_grad=True)
     x = gi.make_inputs(cfg, 15)
-    d = dev_inputs(x)
-    with pytest.raises(gdn.GdnError) as e:
-        gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"])
-    assert e.value.status == gdn.GDN_ERR_UNSUPPORTED
+    dht = np.random.default_rng(16).standard_normal((1, 2, 128, 128)) * 0.1
+    a = compare(x, dht=dht, label="fp32 d=128 fwd+bwd")
+    b = run_bwd(x, dht=dht, use_context=False)
+    for n, u, v in zip(NAMES, a, b):
+        assert np.array_equal(u, v), n
 
 
 @pytest.mark.parametrize("name", ["metric", "c4"])
@@ -152,6 +159,7 @@ def test_packed_varlen_with_states_and_scale():
 # in-operator L2 normalisation of q and k, on raw rows
 L2 = [
     ("fp32", 64, 1, 150, 2, 0.2, True, 0.9),
+    ("fp32", 128, 1, 130, 2, 0.1, True, 1.0),
     ("bf16", 64, 2, 130, 2, 0.0, False, 1.0),
     ("bf16", 128, 1, 200, 3, 0.1, True, 1.0),
 ]
@@ -180,7 +188,7 @@ def test_l2norm_metric_shape_fwd_bwd():
     compare(gi.make_inputs(cfg, 0), label="metric shape, raw q/k, in-operator normalisation", l2=True)
 
 
-@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128), ("fp32", 128)])
 def test_l2norm_rows_below_the_floor(dtype, d):
     # rows of q and k that are exactly zero lie below the norm floor: the normalised row is
     # zero and its gradient is dy / floor.  Those rows' gradients are ~1e12 times the others',
@@ -219,7 +227,8 @@ def test_l2norm_rows_below_the_floor(dtype, d):
             assert mr <= tol["maxrel"] and fr <= tol["frob"], (name, mr, fr)
 
 
-@pytest.mark.parametrize("dtype,d,B,H", [("fp32", 64, 20, 4), ("bf16", 128, 5, 8), ("bf16", 64, 40, 2)])
+@pytest.mark.parametrize("dtype,d,B,H", [("fp32", 64, 20, 4), ("bf16", 128, 5, 8), ("bf16", 64, 40, 2),
+                                         ("fp32", 128, 5, 8)])
 def test_state_passes_grid_past_one_round(dtype, d, B, H):
     # more than 256 (sequence, head, 16-column block) workgroups in both state
     # passes: two column blocks per workgroup, rotated shared reads

@@ -73,6 +73,7 @@ def test_stress_forward(dtype, d, T, H, h0, sigma, min_a):
 @pytest.mark.parametrize("dtype,d,T,H,h0,sigma,with_dht,min_a", [
     ("fp32", 64, 256, 2, 0.0, 0.05, False, 0.99),
     ("fp32", 64, 300, 2, 0.2, 0.02, True, 0.99),
+    ("fp32", 128, 256, 2, 0.1, 0.05, True, 0.99),
     ("bf16", 128, 512, 2, 0.0, 0.5, False, 0.85),
     ("bf16", 128, 300, 2, 0.1, 0.5, True, 0.85),
 ])
