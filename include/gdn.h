@@ -58,10 +58,10 @@
  * gdn_last_error_message() returns a thread-local description of the last
  * non-OK return.  Nothing aborts, prints or throws across this interface.
  *
- * Supported set (gdn_fwd, gdn_bwd): d_k = d_v in {64, 128}, chunk = 64, dtype
- * fp32 or bf16 (forward and backward in each), any T >= 0 (a problem with no
- * tokens enqueues only state copies).  Anything else returns
- * GDN_ERR_UNSUPPORTED.
+ * Supported set (gdn_fwd, gdn_bwd): d_k and d_v each in {64, 128} (equal or
+ * not), chunk = 64, dtype fp32 or bf16 (forward and backward in each), any
+ * T >= 0 (a problem with no tokens enqueues only state copies).  Anything else
+ * returns GDN_ERR_UNSUPPORTED.
  *
  * In-operator L2 normalisation (qk_l2norm = 1) is the usual prologue of the
  * GDN layer (Qwen3.5 normalises q and k per head before the recurrence).
@@ -96,7 +96,7 @@ typedef struct {
   int64_t seqlen;  /* T: tokens per batch row, or total packed tokens (varlen)  */
   int64_t heads;   /* H                                                          */
   int64_t dk;      /* key/query head dim                                         */
-  int64_t dv;      /* value head dim (must equal dk)                             */
+  int64_t dv;      /* value head dim (64 or 128; may differ from dk)             */
   int64_t chunk;   /* chunk length of the chunked form; must be 64               */
   int64_t num_seqs;                /* N when varlen; ignored when dense            */
   const int32_t* cu_seqlens_host;  /* [N+1] host copy: validation and launch sizes */

@@ -109,10 +109,11 @@ bool strided_overlap(const Strided& a, const Strided& b) {
 }
 
 struct Layout {
-  int64_t B = 0, T = 0, H = 0, D = 0, N = 0, NC = 0, tokens = 0;
+  int64_t B = 0, T = 0, H = 0, N = 0, NC = 0, tokens = 0;
+  int64_t DK = 0, DV = 0, D = 0;   // head dims; the kernels run at D = max(DK, DV)
   bool varlen = false, bf16 = false, l2norm = false;
   size_t esz = 0;
-  int64_t ld = 0;   // token stride (elements) of q, k, v and their gradients
+  int64_t ldq = 0, ldv = 0;   // token strides (elements) of q, k, dq, dk and of v, dv
   // byte offsets into a workspace
   size_t chunk_tab = 0, seq_tab = 0, gamma = 0, Wn = 0, Ktf = 0, Ua = 0, Hf = 0, Vf = 0, Tm = 0;
   size_t qinv = 0, kinv = 0;
@@ -128,8 +129,8 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
     return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
   if (p->heads < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "heads = %lld < 1", (long long)p->heads);
   if (p->dk < 1 || p->dv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "dk/dv must be >= 1");
-  if (p->dk != p->dv) return fail(GDN_ERR_UNSUPPORTED, "dk (%lld) != dv (%lld)", (long long)p->dk, (long long)p->dv);
-  if (p->dk != 64 && p->dk != 128) return fail(GDN_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)p->dk);
+  if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
+    return fail(GDN_ERR_UNSUPPORTED, "head dims dk %lld, dv %lld not in {64, 128}", (long long)p->dk, (long long)p->dv);
   if (p->chunk != 64) return fail(GDN_ERR_UNSUPPORTED, "chunk %lld != 64", (long long)p->chunk);
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
@@ -144,12 +145,15 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
     return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
   L->varlen = has_h;
   L->H = p->heads;
-  L->D = p->dk;
+  L->DK = p->dk;
+  L->DV = p->dv;
+  L->D = p->dk > p->dv ? p->dk : p->dv;
   L->T = p->seqlen;
   L->bf16 = p->dtype == GDN_BF16;
   L->l2norm = p->qk_l2norm == 1;
   L->esz = L->bf16 ? 2 : 4;
-  L->ld = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dk;
+  L->ldq = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dk;
+  L->ldv = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dv;
   const int64_t maxtok = (int64_t)1 << 31;
   if (L->varlen) {
     if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
@@ -294,7 +298,10 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws, hipStre
   P.Vf = ws + L.Vf;
   P.Tm = reinterpret_cast<float*>(ws + L.Tm);
   P.qk_l2norm = L.l2norm ? 1 : 0;
-  P.ldx = L.ld;
+  P.kdim = (int)L.DK;
+  P.vdim = (int)L.DV;
+  P.ldq = L.ldq;
+  P.ldv = L.ldv;
   // State-pass workgroups, one per (sequence, head, 16-column block), one
   // resident per CU: with more than half the CUs' worth, rotated shared reads
   // (measured 8-11% faster there, 1-2% slower with fewer); with more than one
@@ -442,15 +449,15 @@ size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
 gdn_status check_fwd_args(const Layout& L, const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const float* h0, const void* o, const float* ht,
                           const void* workspace, bool with_ws) {
-  const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
+  const size_t ob = (size_t)(L.tokens * L.H * L.DV) * L.esz;
   const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
-  const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
-  const Range rq = strided(q, L.tokens, L.H * L.D, L.ld, L.esz, "q"), rk = strided(k, L.tokens, L.H * L.D, L.ld, L.esz, "k"),
-              rv = strided(v, L.tokens, L.H * L.D, L.ld, L.esz, "v");
+  const size_t sb = (size_t)(L.N * L.H * L.DK * L.DV) * sizeof(float);
+  const Range rq = strided(q, L.tokens, L.H * L.DK, L.ldq, L.esz, "q"), rk = strided(k, L.tokens, L.H * L.DK, L.ldq, L.esz, "k"),
+              rv = strided(v, L.tokens, L.H * L.DV, L.ldv, L.esz, "v");
   const size_t wb = with_ws ? L.fwd_bytes : 0;
-  const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {o, qk, "o"}, {workspace, wb, "workspace"}};
+  const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {o, ob, "o"}, {workspace, wb, "workspace"}};
   const Range opt[] = {{h0, sb, "h0"}, {ht, sb, "ht"}};
-  const Range outs[] = {{o, qk, "o"}, {ht, sb, "ht"}, {workspace, wb, "workspace"}};
+  const Range outs[] = {{o, ob, "o"}, {ht, sb, "ht"}, {workspace, wb, "workspace"}};
   const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"}, {h0, sb, "h0"}};
   return check_ptrs(req, with_ws ? 7 : 6, opt, 2, outs, 3, ins, 6);
 }
@@ -815,21 +822,22 @@ gdn_status gdn_bwd(const gdn_problem* p, const void* q, const void* k, const voi
     Layout L;
     gdn_status st = plan_problem(p, &L);
     if (st != GDN_OK) return st;
-    const size_t qk = (size_t)(L.tokens * L.H * L.D) * L.esz;
+    const size_t ob = (size_t)(L.tokens * L.H * L.DV) * L.esz;
     const size_t gb = (size_t)(L.tokens * L.H) * sizeof(float);
-    const size_t sb = (size_t)(L.N * L.H * L.D * L.D) * sizeof(float);
-    auto st_ = [&](const void* x, const char* nm) { return strided(x, L.tokens, L.H * L.D, L.ld, L.esz, nm); };
-    const Range rq = st_(q, "q"), rk = st_(k, "k"), rv = st_(v, "v"), rdq = st_(dq, "dq"), rdk = st_(dk, "dk"),
-                rdv = st_(dv, "dv");
+    const size_t sb = (size_t)(L.N * L.H * L.DK * L.DV) * sizeof(float);
+    auto sq_ = [&](const void* x, const char* nm) { return strided(x, L.tokens, L.H * L.DK, L.ldq, L.esz, nm); };
+    auto sv_ = [&](const void* x, const char* nm) { return strided(x, L.tokens, L.H * L.DV, L.ldv, L.esz, nm); };
+    const Range rq = sq_(q, "q"), rk = sq_(k, "k"), rv = sv_(v, "v"), rdq = sq_(dq, "dq"), rdk = sq_(dk, "dk"),
+                rdv = sv_(dv, "dv");
     const Range req[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
-                         {d_o, qk, "do"}, rdq, rdk, rdv, {dg, gb, "dg"},
+                         {d_o, ob, "do"}, rdq, rdk, rdv, {dg, gb, "dg"},
                          {dbeta, gb, "dbeta"}, {workspace, L.bwd_bytes, "workspace"}};
     const Range opt[] = {{h0, sb, "h0"}, {dht, sb, "dht"}, {dh0, sb, "dh0"},
                          {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
     const Range outs[] = {rdq, rdk, rdv, {dg, gb, "dg"}, {dbeta, gb, "dbeta"},
                           {dh0, sb, "dh0"}, {workspace, L.bwd_bytes, "workspace"}};
     const Range ins[] = {rq, rk, rv, {g, gb, "g"}, {beta, gb, "beta"},
-                         {h0, sb, "h0"}, {d_o, qk, "do"}, {dht, sb, "dht"},
+                         {h0, sb, "h0"}, {d_o, ob, "do"}, {dht, sb, "dht"},
                          {fwd_workspace, L.fwd_bytes, "fwd_workspace"}};
     st = check_ptrs(req, 12, opt, 4, outs, 7, ins, 9);
     if (st != GDN_OK) return st;

@@ -98,8 +98,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
   E* Ktn = reinterpret_cast<E*>(p.Ktn);
   E* WnT = reinterpret_cast<E*>(p.WnT);
-  const size_t rowstride = (size_t)H * D;
-  const size_t base = ((size_t)tok0 * H + h) * D;
+  // dO: [tokens][H][dv], contiguous
+  const size_t rowstride = (size_t)H * p.vdim;
+  const size_t base = ((size_t)tok0 * H + h) * p.vdim;
   const float sc = p.scale;
 
   // ---- stage Q, K, dO; the -W records of this wave's i-slice.  Every global
@@ -109,11 +110,11 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_bwd_prep(Params p) {
   {
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    // q, k: token stride ldx; dO: contiguous
-    const size_t xbase = (size_t)tok0 * p.ldx + (size_t)h * D;
-    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldx, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldx, L, tid, NORM ? p.kinv + nb : nullptr, H);
-    so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid);
+    // q, k: token stride ldq, dk wide; dO: contiguous, dv wide (zeros past the widths)
+    const size_t xbase = (size_t)tok0 * p.ldq + (size_t)h * p.kdim;
+    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldq, L, tid, nullptr, 0, p.kdim);
+    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldq, L, tid, NORM ? p.kinv + nb : nullptr, H, p.kdim);
+    so.load(reinterpret_cast<const E*>(p.dO) + base, rowstride, L, tid, nullptr, 0, p.vdim);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) wrec[rb] = load_rec<E>(Wn + (((size_t)ch * 4 + rb) * KB + w) * REC, lane);
     if (w == 0) s_gam[lane] = gv;
@@ -267,7 +268,9 @@ __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(
   const int n = unit / p.H, h = unit - n * p.H;
   const int4 st = seq_info(p, n);
   const int c0 = st.x, nc = st.y;
-  const size_t sbase = (size_t)unit * D * D;
+  // states [N][H][dk][dv]; rows past dk and columns past dv are the padding of D
+  const size_t sbase = (size_t)unit * p.kdim * p.vdim;
+  const bool col_real = 16 * jb < p.vdim;
   const E* Ktn = reinterpret_cast<const E*>(p.Ktn);
   const E* WnT = reinterpret_cast<const E*>(p.WnT);
   E* HPf = reinterpret_cast<E*>(p.HPf);
@@ -295,9 +298,10 @@ __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(
     f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
-      if (p.dht) {
-        const float* src = p.dht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-        hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+      if (p.dht && col_real && 16 * ib < p.kdim) {
+        const int ld = p.vdim;
+        const float* src = p.dht + sbase + (size_t)(16 * ib + 4 * lg) * ld + 16 * jb + li;
+        hs[ib] = f32x4{src[0], src[ld], src[2 * ld], src[3 * ld]};
       } else {
         hs[ib] = zero4();
       }
@@ -404,14 +408,16 @@ __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(
         wait_lds();
       }
     }
-    if (p.dh0) {
+    if (p.dh0 && col_real) {
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib) {
-        float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        if (16 * ib >= p.kdim) continue;
+        const int ld = p.vdim;
+        float* dst = p.dh0 + sbase + (size_t)(16 * ib + 4 * lg) * ld + 16 * jb + li;
         dst[0] = hs[ib][0];
-        dst[D] = hs[ib][1];
-        dst[2 * D] = hs[ib][2];
-        dst[3 * D] = hs[ib][3];
+        dst[ld] = hs[ib][1];
+        dst[2 * ld] = hs[ib][2];
+        dst[3 * ld] = hs[ib][3];
       }
     }
   } else {
@@ -512,14 +518,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   const E* HPf = reinterpret_cast<const E*>(p.HPf);
   const E* dVf = reinterpret_cast<const E*>(p.dVf);
   const float sc = p.scale;
-  // q, k, v and their gradients: token stride ldx; dO: contiguous
-  const size_t rowstride = (size_t)H * D;
-  const size_t base = ((size_t)tok0 * H + h) * D;
-  const size_t xrow = (size_t)p.ldx;
-  const size_t xbase = (size_t)tok0 * xrow + (size_t)h * D;
+  // q, k and dq, dk: token stride ldq, dk wide; v and dv: token stride ldv, dv
+  // wide; dO: contiguous, dv wide.  Columns past a width read as zero.
+  const size_t rowstride = (size_t)H * p.vdim;
+  const size_t base = ((size_t)tok0 * H + h) * p.vdim;
+  const size_t xrow = (size_t)p.ldq;
+  const size_t xbase = (size_t)tok0 * xrow + (size_t)h * p.kdim;
+  const size_t vrow = (size_t)p.ldv;
+  const size_t vbase = (size_t)tok0 * vrow + (size_t)h * p.vdim;
 
-  auto gnat = [&](const E* X, size_t xb, size_t xr, int row, int kb) {
-    return row < L ? load_frag_row<E>(X + xb + (size_t)row * xr + 32 * kb, lg) : zero_frag<E>();
+  // natural fragment of row `row`, 32-column block kb, of a tensor `width` wide
+  auto gnat = [&](const E* X, size_t xb, size_t xr, int row, int kb, int width) {
+    return row < L && 32 * kb < width ? load_frag_row<E>(X + xb + (size_t)row * xr + 32 * kb, lg) : zero_frag<E>();
   };
   __shared__ float s_inv[NORM ? 128 : 1];   // sign-encoded reciprocal norms of the q, k rows
   // natural fragments of Q and K (normalised rows with NORM): from the staged
@@ -528,7 +538,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     if constexpr (S::kStageQK) {
       return tile_frag<E, D>(tQ, ab, kb, li, lg);
     } else {
-      const frag_t<E> f = gnat(Q, xbase, xrow, 16 * ab + li, kb);
+      const frag_t<E> f = gnat(Q, xbase, xrow, 16 * ab + li, kb, p.kdim);
       if constexpr (NORM) return scale_frag<E>(f, fabsf(s_inv[16 * ab + li]));
       else return f;
     }
@@ -537,14 +547,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     if constexpr (S::kStageQK) {
       return tile_frag<E, D>(tK, ab, kb, li, lg);
     } else {
-      const frag_t<E> f = gnat(K, xbase, xrow, 16 * ab + li, kb);
+      const frag_t<E> f = gnat(K, xbase, xrow, 16 * ab + li, kb, p.kdim);
       if constexpr (NORM) return scale_frag<E>(f, fabsf(s_inv[64 + 16 * ab + li]));
       else return f;
     }
   };
   auto of = [&](int ab, int kb) {
     if constexpr (S::kStageDO) return tile_frag<E, D>(tO, ab, kb, li, lg);
-    else return gnat(dO, base, rowstride, 16 * ab + li, kb);
+    else return gnat(dO, base, rowstride, 16 * ab + li, kb, p.vdim);
   };
   // fp32 LDS matrix fragments: index rows 16ab.., contraction cols 32kb..
   auto mfrag32 = [&](const float* M, int ab, int kb) {
@@ -613,8 +623,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     TileStage<E, D, NT> sq, sk, so;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
     if constexpr (S::kStageQK) {
-      sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H);
-      sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H);
+      sq.load(Q + xbase, xrow, L, tid, NORM ? p.qinv + nb : nullptr, H, p.kdim);
+      sk.load(K + xbase, xrow, L, tid, NORM ? p.kinv + nb : nullptr, H, p.kdim);
     }
     float inv_row = 0.f;   // unstaged: thread r < 128 fetches the scale of q row r or k row r - 64
     if constexpr (NORM && !S::kStageQK) {
@@ -623,14 +633,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         inv_row = (tid < 64 ? p.qinv : p.kinv)[nb + (size_t)(r < L ? r : 0) * H];
       }
     }
-    if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid);
+    if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid, nullptr, 0, p.vdim);
 #pragma unroll
     for (int k = 0; k < NTT; ++k) {
       const int t = w + NW * k;
       const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
       const int sbt = t - rbt * (rbt + 1) / 2;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, xbase, xrow, 16 * sbt + li, kb) : zero_frag<E>();
+      for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, vbase, vrow, 16 * sbt + li, kb, p.vdim) : zero_frag<E>();
     }
     // T = (I + diag(beta) A')^-1 as the forward solved it
     constexpr int TPER = 64 * 16 / NT;
@@ -925,7 +935,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // operands of the output phase that come from global memory
   frag_t<E> vw[4];
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, xbase, xrow, 16 * sb + li, kw);
+  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, vbase, vrow, 16 * sb + li, kw, p.vdim);
   __syncthreads();
 
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
@@ -952,14 +962,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   char* stk = kStageOut ? (norm ? tQ : reinterpret_cast<char*>(sM1)) : reinterpret_cast<char*>(p.dk);
   char* stv = kStageOut ? tK : reinterpret_cast<char*>(p.dv);
   // columns 16 w + 4 lg .. + 3 of row r (this lane's four values) into a
-  // staging tile, or straight to row r of the gradient (rows < L only)
-  auto stage4 = [&](char* st, int r, f32x4 x) {
+  // staging tile, or straight to row r of the gradient (rows < L and columns
+  // inside its width only); is_v: the tensor is dv (else dq or dk)
+  auto stage4 = [&](char* st, int r, f32x4 x, bool is_v) {
     const int byte = (16 * w + 4 * lg) * (int)sizeof(E);
     if constexpr (kStageOut) {
       const int pc = (byte >> 4) ^ (r % PPR);
       *reinterpret_cast<quad_t<E>*>(st + r * RB + 16 * pc + (byte & 15)) = to_quad<E>(x);
     } else {
-      if (r < L) store_quad_nt<E>(reinterpret_cast<E*>(st + (xbase + (size_t)r * xrow) * sizeof(E) + byte), x);
+      const size_t row0 = is_v ? vbase + (size_t)r * vrow : xbase + (size_t)r * xrow;
+      if (r < L && 16 * w < (is_v ? p.vdim : p.kdim))
+        store_quad_nt<E>(reinterpret_cast<E*>(st + row0 * sizeof(E) + byte), x);
     }
   };
   f32x4 dqh[4], dkh[4], qn4[4], kn4[4];
@@ -980,7 +993,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       f32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = ir > 0.f ? (dy[rb][q] - yn[rb][q] * yd) * ir : -dy[rb][q] * ir;
-      stage4(dst, r, o);
+      stage4(dst, r, o, false);
     }
   };
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
@@ -1032,7 +1045,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dqh[rb] = acc;
         qn4[rb] = qn;
       } else {
-        stage4(stq, r, acc);
+        stage4(stq, r, acc, false);
       }
     }
     if constexpr (norm) {
@@ -1095,7 +1108,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         dkh[sb] = acc;
         kn4[sb] = kn;
       } else {
-        stage4(stk, s_, acc);
+        stage4(stk, s_, acc, false);
       }
     }
     csum = sum_in_group(csum);
@@ -1144,21 +1157,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 
   if constexpr (norm) norm_out(dkh, kn4, s_kd, s_inv + 64, stk);
 #pragma unroll
-  for (int sb = 0; sb < 4; ++sb) stage4(stv, 16 * sb + li, dvo[sb]);
+  for (int sb = 0; sb < 4; ++sb) stage4(stv, 16 * sb + li, dvo[sb], true);
   __syncthreads();
   // whole rows of dq, dk, dv, 16 bytes a lane, non-temporal: another kernel
   // reads them next, and a step's 48 MB of them left dirty in the caches
   // would be written back in the middle of later kernels' reads
   static_assert((64 * PPR) % NT == 0, "the staged rows divide over the threads");
+  const int ppq = p.kdim * (int)sizeof(E) / 16, ppv = p.vdim * (int)sizeof(E) / 16;   // pieces of a row that exist
 #pragma unroll
   for (int e0 = 0; e0 < (kStageOut ? 64 * PPR : 0); e0 += NT) {
     const int e = e0 + tid, r = e / PPR, pc = e - r * PPR;
     if (r < L) {
       const int off = r * RB + 16 * (pc ^ (r % PPR));
-      const size_t dst = (xbase + (size_t)r * xrow) * sizeof(E) + 16 * (size_t)pc;
-      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stq + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dq) + dst));
-      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stk + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dk) + dst));
-      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stv + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dv) + dst));
+      if (pc < ppq) {
+        const size_t dst = (xbase + (size_t)r * xrow) * sizeof(E) + 16 * (size_t)pc;
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stq + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dq) + dst));
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stk + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dk) + dst));
+      }
+      if (pc < ppv) {
+        const size_t dst = (vbase + (size_t)r * vrow) * sizeof(E) + 16 * (size_t)pc;
+        __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(stv + off), reinterpret_cast<i32x4*>(reinterpret_cast<char*>(p.dv) + dst));
+      }
     }
   }
 

@@ -268,7 +268,9 @@ template <typename E> __device__ __forceinline__ frag_t<E> scale_frag(frag_t<E> 
 
 // One thread's share of a staged tile, NTHR threads per tile: load() issues
 // every global read of rows [0, L) of X (row r at src + r * rstride
-// elements; rows >= L read as zero), store() writes the swizzled LDS tile.
+// elements; rows >= L, and with `width` < D the columns past it, read as
+// zero: a narrower tensor padded with zeros to D), store() writes the
+// swizzled LDS tile.
 // With `rs`, row r is scaled by |rs[r * rsstride]| on its way to LDS (the
 // scale reads are issued with the tile's, rows >= L read row 0's and scale
 // zeros).  Loading several tiles before storing any keeps all their reads
@@ -283,12 +285,13 @@ struct TileStage {
   float sc[PER];
   bool scaled = false;
   __device__ __forceinline__ void load(const E* src, size_t rstride, int L, int tid,
-                                       const float* rs = nullptr, size_t rsstride = 0) {
+                                       const float* rs = nullptr, size_t rsstride = 0, int width = D) {
+    const int wp = width * (int)sizeof(E) / 16;   // 16-byte pieces of a row that exist
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int q = tid + k * NTHR, r = q / T::NCH, c = q - r * T::NCH;
       v[k] = i32x4{0, 0, 0, 0};
-      if (r < L) v[k] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * c);
+      if (r < L && c < wp) v[k] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const char*>(src + (size_t)r * rstride) + 16 * c);
     }
     scaled = rs != nullptr;
     if (rs) {

@@ -115,20 +115,21 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(s
   constexpr bool kStage = NatTile<E, D>::BYTES <= 64 * LDA * 4;
   frag_t<E> kf[4][KB], vfw[4];
   TileStage<E, D, 64 * NW> sk, sv;
+  // (keys dk and values dv wide, zero past that: the records below are D wide)
+  const size_t kbase = (size_t)tok0 * p.ldq + (size_t)h * p.kdim, vbase = (size_t)tok0 * p.ldv + (size_t)h * p.vdim;
   if constexpr (kStage) {
-    const size_t base = (size_t)tok0 * p.ldx + (size_t)h * D, rowstride = (size_t)p.ldx;
-    sk.load(K + base, rowstride, L, tid);
-    sv.load(V + base, rowstride, L, tid);
+    sk.load(K + kbase, (size_t)p.ldq, L, tid, nullptr, 0, p.kdim);
+    sv.load(V + vbase, (size_t)p.ldv, L, tid, nullptr, 0, p.vdim);
   } else {
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const int row = 16 * sb + li;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        kf[sb][kb] = row < L ? load_frag_row<E>(K + (size_t)(tok0 + row) * p.ldx + (size_t)h * D + 32 * kb, lg)
-                             : zero_frag<E>();
-      vfw[sb] = row < L ? load_frag_row<E>(V + (size_t)(tok0 + row) * p.ldx + (size_t)h * D + 32 * w, lg)
-                        : zero_frag<E>();
+        kf[sb][kb] = row < L && 32 * kb < p.kdim ? load_frag_row<E>(K + kbase + (size_t)row * p.ldq + 32 * kb, lg)
+                                               : zero_frag<E>();
+      vfw[sb] = row < L && 32 * w < p.vdim ? load_frag_row<E>(V + vbase + (size_t)row * p.ldv + 32 * w, lg)
+                                         : zero_frag<E>();
     }
   }
   // chunk-local cumulative log decay (read after the key and value reads are
@@ -359,7 +360,10 @@ __global__ __launch_bounds__((64 * FwdRing<E, D, CPW>::WAVES)) void k_fwd_state(
   const int n = unit / p.H, h = unit - n * p.H;
   const int4 st = seq_info(p, n);
   const int c0 = st.x, nc = st.y;
-  const size_t sbase = (size_t)unit * D * D;
+  // states [N][H][dk][dv]; rows past dk and columns past dv are the padding
+  // of D (they start at zero and stay zero)
+  const size_t sbase = (size_t)unit * p.kdim * p.vdim;
+  const bool col_real = 16 * jb < p.vdim;
   const E* Wn = reinterpret_cast<const E*>(p.Wn);
   const E* Ktf = reinterpret_cast<const E*>(p.Ktf);
   const E* Ua = reinterpret_cast<const E*>(p.Ua);
@@ -389,9 +393,10 @@ __global__ __launch_bounds__((64 * FwdRing<E, D, CPW>::WAVES)) void k_fwd_state(
     f32x4 hs[NJ];
 #pragma unroll
     for (int ib = 0; ib < NJ; ++ib) {
-      if (p.h0) {
-        const float* src = p.h0 + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
-        hs[ib] = f32x4{src[0], src[D], src[2 * D], src[3 * D]};
+      if (p.h0 && col_real && 16 * ib < p.kdim) {
+        const int ld = p.vdim;
+        const float* src = p.h0 + sbase + (size_t)(16 * ib + 4 * lg) * ld + 16 * jb + li;
+        hs[ib] = f32x4{src[0], src[ld], src[2 * ld], src[3 * ld]};
       } else {
         hs[ib] = zero4();
       }
@@ -497,14 +502,16 @@ __global__ __launch_bounds__((64 * FwdRing<E, D, CPW>::WAVES)) void k_fwd_state(
         wait_lds();
       }
     }
-    if (write_ht && p.ht) {
+    if (write_ht && p.ht && col_real) {
 #pragma unroll
       for (int ib = 0; ib < NJ; ++ib) {
-        float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * D + 16 * jb + li;
+        if (16 * ib >= p.kdim) continue;
+        const int ld = p.vdim;
+        float* dst = p.ht + sbase + (size_t)(16 * ib + 4 * lg) * ld + 16 * jb + li;
         dst[0] = hs[ib][0];
-        dst[D] = hs[ib][1];
-        dst[2 * D] = hs[ib][2];
-        dst[3 * D] = hs[ib][3];
+        dst[ld] = hs[ib][1];
+        dst[2 * ld] = hs[ib][2];
+        dst[3 * ld] = hs[ib][3];
       }
     }
   } else {
@@ -555,8 +562,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   const E* Hf = reinterpret_cast<const E*>(p.Hf);
   const E* Vf = reinterpret_cast<const E*>(p.Vf);
   E* O = reinterpret_cast<E*>(p.o);
-  const size_t rowstride = (size_t)H * D;
-  const size_t base = ((size_t)tok0 * H + h) * D;
+  // o: [tokens][H][dv], contiguous
+  const size_t rowstride = (size_t)H * p.vdim;
+  const size_t base = ((size_t)tok0 * H + h) * p.vdim;
 
   // every global read is issued before the first use of any of them
   const float gv = p.gamma[(size_t)ch * 64 + lane];
@@ -564,10 +572,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   {
     TileStage<E, D, NT> sq, sk;
     const size_t nb = (size_t)tok0 * H + h;   // reciprocal norms of this chunk's rows, stride H
-    // q, k: token stride ldx (the output keeps the contiguous layout)
-    const size_t xbase = (size_t)tok0 * p.ldx + (size_t)h * D;
-    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldx, L, tid);
-    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldx, L, tid, NORM ? p.kinv + nb : nullptr, H);
+    // q, k: token stride ldq, dk wide (the output keeps the contiguous layout)
+    const size_t xbase = (size_t)tok0 * p.ldq + (size_t)h * p.kdim;
+    sq.load(reinterpret_cast<const E*>(p.q) + xbase, (size_t)p.ldq, L, tid, nullptr, 0, p.kdim);
+    sk.load(reinterpret_cast<const E*>(p.k) + xbase, (size_t)p.ldq, L, tid, NORM ? p.kinv + nb : nullptr, H, p.kdim);
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
@@ -609,6 +617,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void k_fwd_out(Params p) {
   }
   __syncthreads();
 
+  if (32 * w >= p.vdim) return;   // this wave's output columns are padding of D
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int r = 16 * rb + li;

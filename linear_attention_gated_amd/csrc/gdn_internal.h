@@ -11,7 +11,7 @@ constexpr int CHUNK = 64;   // chunk length of the chunked form
 constexpr int REC = 512;    // elements per fragment record (64 lanes x 8)
 constexpr int AREC = 256;   // elements per accumulator record (64 lanes x 4)
 
-// Record counts per (chunk, head), for head dim D:
+// Record counts per (chunk, head), for head dim D = max(dk, dv):
 //   Wn  F(-W; r, i)      [4][D/32]        forward WY factor, negated
 //   Ktf F(Kt; i, s)      [D/16][2]        decayed keys, transposed
 //   Ua  acc U[r][j]      [D/16][4]        WY values (accumulator records)
@@ -54,7 +54,12 @@ struct Params {
   void *Wn, *Ktf, *Ua, *Hf, *Vf;
   float* Tm;
   int qk_l2norm;          // 1: q and k rows L2-normalised inside the operator
-  long long ldx;          // token stride (elements) of q, k, v, dq, dk, dv
+  // Head dims.  The kernels run at D = max(dk, dv); a narrower q/k (dk < D)
+  // or v (dv < D) is read with zeros past its width and its outputs are
+  // written only up to it: zero columns stay zero through every product, so
+  // the padded problem has exactly the rectangular one's results.
+  int kdim, vdim;
+  long long ldq, ldv;     // token strides (elements) of q, k, dq, dk and of v, dv
   float* kinv;            // reciprocal key norms [tokens][H] (forward context), sign-encoded
   float* qinv;            // reciprocal query norms [tokens][H] (backward workspace)
   void *WnT, *Ktn, *HPf, *dVf;

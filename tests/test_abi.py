@@ -116,8 +116,8 @@ def test_workspace_query_valid_and_invalid():
 
 
 CASES = [
-    ("dk_not_dv", dict(dv=128), {}, gdn.GDN_ERR_UNSUPPORTED, "dk"),
-    ("dim_96", dict(dk=96, dv=96), {}, gdn.GDN_ERR_UNSUPPORTED, "head dim"),
+    ("dv_96", dict(dv=96), {}, gdn.GDN_ERR_UNSUPPORTED, "head dims"),
+    ("dim_96", dict(dk=96, dv=96), {}, gdn.GDN_ERR_UNSUPPORTED, "head dims"),
     ("chunk_32", dict(chunk=32), {}, gdn.GDN_ERR_UNSUPPORTED, "chunk"),
     ("dtype_7", dict(dtype=7), {}, gdn.GDN_ERR_UNSUPPORTED, "dtype"),
     ("heads_0", dict(heads=0), {}, gdn.GDN_ERR_INVALID_ARGUMENT, "heads"),
