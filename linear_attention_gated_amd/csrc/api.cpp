@@ -65,6 +65,17 @@ gdn_status fail(gdn_status s, const char* fmt, ...) {
   return s;
 }
 
+// The dtype field as the integer the caller stored: a C caller may put any
+// int in the enum, and loading an out-of-range value through the enum type
+// itself would be undefined in C++.
+template <class Prob>
+int dtype_of(const Prob* p) {
+  int v;
+  static_assert(sizeof(v) == sizeof(p->dtype), "the dtype field is an int");
+  std::memcpy(&v, &p->dtype, sizeof(v));
+  return v;
+}
+
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -73,7 +84,7 @@ gdn_status check_stride(const gdn_problem* p) {
   const int64_t s = p->qkv_token_stride;
   if (s == 0) return GDN_OK;
   const int64_t wmax = p->heads * (p->dk > p->dv ? p->dk : p->dv);
-  const int64_t mult = p->dtype == GDN_BF16 ? 8 : 4;
+  const int64_t mult = dtype_of(p) == GDN_BF16 ? 8 : 4;
   if (s < 0 || s < wmax)
     return fail(GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride %lld < H * max(dk, dv) = %lld", (long long)s, (long long)wmax);
   if (s % mult) return fail(GDN_ERR_INVALID_ARGUMENT, "qkv_token_stride %lld is not a multiple of %lld", (long long)s, (long long)mult);
@@ -125,8 +136,8 @@ struct Layout {
 // Validate the problem description and derive sizes.  No HIP call.
 gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
-    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (dtype_of(p) != GDN_F32 && dtype_of(p) != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", dtype_of(p));
   if (p->heads < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "heads = %lld < 1", (long long)p->heads);
   if (p->dk < 1 || p->dv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "dk/dv must be >= 1");
   if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
@@ -149,7 +160,7 @@ gdn_status plan_problem(const gdn_problem* p, Layout* L) {
   L->DV = p->dv;
   L->D = p->dk > p->dv ? p->dk : p->dv;
   L->T = p->seqlen;
-  L->bf16 = p->dtype == GDN_BF16;
+  L->bf16 = dtype_of(p) == GDN_BF16;
   L->l2norm = p->qk_l2norm == 1;
   L->esz = L->bf16 ? 2 : 4;
   L->ldq = p->qkv_token_stride ? p->qkv_token_stride : p->heads * p->dk;
@@ -320,8 +331,8 @@ gdn_status hip_fail(hipError_t e, const char* what) {
 
 gdn_status check_gnorm(const gdn_gated_norm_problem* p) {
   if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
-    return fail(GDN_ERR_INVALID_ARGUMENT, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (dtype_of(p) != GDN_F32 && dtype_of(p) != GDN_BF16)
+    return fail(GDN_ERR_INVALID_ARGUMENT, "dtype %d is not GDN_F32 or GDN_BF16", dtype_of(p));
   if (p->rows < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "rows < 0");
   if (p->dim != 64 && p->dim != 128) return fail(GDN_ERR_UNSUPPORTED, "dim %lld not in {64, 128}", (long long)p->dim);
   if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(GDN_ERR_INVALID_ARGUMENT, "eps is negative or not finite");
@@ -336,8 +347,8 @@ struct ConvPlan {
 
 gdn_status check_conv(const gdn_conv_problem* p, ConvPlan* P) {
   if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
-    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (dtype_of(p) != GDN_F32 && dtype_of(p) != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", dtype_of(p));
   if (p->kernel_size < 1 || p->kernel_size > 4)
     return fail(GDN_ERR_UNSUPPORTED, "kernel_size %lld not in [1, 4]", (long long)p->kernel_size);
   if (p->channels < 1 || p->channels % 4)
@@ -349,7 +360,7 @@ gdn_status check_conv(const gdn_conv_problem* p, ConvPlan* P) {
   if (has_h != has_d)
     return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
   P->varlen = has_h;
-  P->bf16 = p->dtype == GDN_BF16;
+  P->bf16 = dtype_of(p) == GDN_BF16;
   P->T = p->seqlen;
   if (P->varlen) {
     if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
@@ -399,8 +410,8 @@ struct RecPlan {
 
 gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
   if (!p) return fail(GDN_ERR_INVALID_ARGUMENT, "problem is NULL");
-  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
-    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", (int)p->dtype);
+  if (dtype_of(p) != GDN_F32 && dtype_of(p) != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "dtype %d is not GDN_F32 or GDN_BF16", dtype_of(p));
   if (p->heads < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "heads = %lld < 1", (long long)p->heads);
   if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
     return fail(GDN_ERR_UNSUPPORTED, "dk %lld / dv %lld not in {64, 128}", (long long)p->dk, (long long)p->dv);
@@ -416,7 +427,7 @@ gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
   if (has_h != has_d)
     return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens_host and cu_seqlens_dev must both be set or both be NULL");
   P->varlen = has_h;
-  P->bf16 = p->dtype == GDN_BF16;
+  P->bf16 = dtype_of(p) == GDN_BF16;
   if (P->varlen) {
     if (p->batch != 1) return fail(GDN_ERR_INVALID_ARGUMENT, "varlen requires batch == 1 (got %lld)", (long long)p->batch);
     if (p->num_seqs < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "num_seqs = %lld < 1", (long long)p->num_seqs);
@@ -440,7 +451,7 @@ gdn_status check_recurrent(const gdn_problem* p, RecPlan* P) {
 }
 
 size_t gnorm_ws_bytes(const gdn_gated_norm_problem* p) {
-  const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, p->dtype == GDN_BF16, true);
+  const int nb = gdn::gnorm_blocks(p->rows, (int)p->dim, dtype_of(p) == GDN_BF16, true);
   return align_up((size_t)(nb > 0 ? nb : 1) * (size_t)p->dim * sizeof(float));
 }
 
@@ -548,7 +559,7 @@ gdn_status gdn_gated_rmsnorm_fwd(const gdn_gated_norm_problem* p, const void* x,
   try {
     gdn_status st = check_gnorm(p);
     if (st != GDN_OK) return st;
-    const size_t rb = (size_t)(p->rows * p->dim) * (p->dtype == GDN_BF16 ? 2 : 4);
+    const size_t rb = (size_t)(p->rows * p->dim) * (dtype_of(p) == GDN_BF16 ? 2 : 4);
     const size_t wb = (size_t)p->dim * sizeof(float);
     const Range req[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}, {y, rb, "y"}};
     const Range outs[] = {{y, rb, "y"}};
@@ -559,7 +570,7 @@ gdn_status gdn_gated_rmsnorm_fwd(const gdn_gated_norm_problem* p, const void* x,
     std::memset(&P, 0, sizeof(P));
     P.x = x; P.z = z; P.w = w; P.y = y; P.rows = p->rows; P.eps = p->eps;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = timed("gnorm_fwd", s, [&] { return gdn::launch_gnorm_fwd(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    hipError_t e = timed("gnorm_fwd", s, [&] { return gdn::launch_gnorm_fwd(P, (int)p->dim, dtype_of(p) == GDN_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "gated rmsnorm forward launch");
     return GDN_OK;
   } catch (...) {
@@ -573,7 +584,7 @@ gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x,
   try {
     gdn_status st = check_gnorm(p);
     if (st != GDN_OK) return st;
-    const size_t rb = (size_t)(p->rows * p->dim) * (p->dtype == GDN_BF16 ? 2 : 4);
+    const size_t rb = (size_t)(p->rows * p->dim) * (dtype_of(p) == GDN_BF16 ? 2 : 4);
     const size_t wb = (size_t)p->dim * sizeof(float);
     const size_t need = gnorm_ws_bytes(p);
     const Range req[] = {{x, rb, "x"}, {z, rb, "z"}, {w, wb, "w"}, {dy, rb, "dy"}, {dx, rb, "dx"},
@@ -592,9 +603,9 @@ gdn_status gdn_gated_rmsnorm_bwd(const gdn_gated_norm_problem* p, const void* x,
     P.part = reinterpret_cast<float*>(workspace);
     P.rows = p->rows; P.eps = p->eps;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = timed("gnorm_bwd", s, [&] { return gdn::launch_gnorm_bwd(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    hipError_t e = timed("gnorm_bwd", s, [&] { return gdn::launch_gnorm_bwd(P, (int)p->dim, dtype_of(p) == GDN_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "gated rmsnorm backward launch");
-    e = timed("gnorm_dw", s, [&] { return gdn::launch_gnorm_dw(P, (int)p->dim, p->dtype == GDN_BF16, s); });
+    e = timed("gnorm_dw", s, [&] { return gdn::launch_gnorm_dw(P, (int)p->dim, dtype_of(p) == GDN_BF16, s); });
     if (e != hipSuccess) return hip_fail(e, "gated rmsnorm weight-gradient launch");
     return GDN_OK;
   } catch (...) {
