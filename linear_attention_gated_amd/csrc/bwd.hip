@@ -14,6 +14,18 @@
 //   dA   = strict_lower(-T^T dT T^T)
 //   dV   = diag(beta) T^T dU
 //   dbeta_r = Gam_r k_r.(T^T dW)_r + v_r.(T^T dU)_r + sum_s dA_rs (K K^T * D)_rs
+// Two of these are formed without dW and dT: since V' = T (Xu - Xw h),
+// dT = dV' (Xu - Xw h)^T = (dV' V'^T)(I + A)^T, and T (I + A) = I, so
+//   dA   = strict_lower(-T^T (dV' V'^T)),   T^T dW = -(T^T dV') h^T.
+// dbeta has a second form: with B = diag(beta) invertible, V' = (B^-1 +
+// A')^-1 (V - Gam K h) (A = B A'), so differentiating B^-1 gives
+//   dbeta_r = (T^T dV')_r . V'_r / beta_r.
+// The two agree exactly but round differently: V' is held in the operand
+// type, and its rounding reaches the sum through sum_s dA_rs A_rs (dA_rs =
+// -(T^T dV')_r . V'_s), the quotient through V'_r alone.  Row by row the
+// kernel takes the quotient where ||A_r||^2 = sum_s A_rs^2 exceeds 1 (keys
+// that cluster, where the sum's terms cancel) and the sum elsewhere (which
+// includes beta_r = 0, where A_r vanishes).
 //   dgamma collects the decay terms (output, P, Xw, A, Kt and the state decay);
 //   dg_s = sum_{r >= s} dgamma_r within the chunk.
 // These are the reverse-mode equations of the chunked forward; the kernel
@@ -435,8 +447,8 @@ __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(
 // K6: per (chunk, head) gradients dq, dk, dv, dbeta, dg.  D/16 waves; wave
 // w owns the 16 feature columns [16w, 16w+16) of dq/dk (i) and dv (j);
 // column block w is half hw = w % 2 of the 32-wide contraction block
-// kw = w / 2.  Quantities that need every column (dP, dW for dT, T, dT, dA,
-// E) are shared through LDS, their 16 x 16 tiles dealt round-robin over the
+// kw = w / 2.  Quantities that need every column (dP, G = dV' V'^T, T, dA,
+// E, T^T dV') are shared through LDS, their 16 x 16 tiles dealt over the
 // waves; sums over waves use per-wave slots so the result is deterministic.
 template <typename E, int D>
 struct BwdGradSmem {
@@ -451,29 +463,32 @@ struct BwdGradSmem {
   static constexpr int TILE = NatTile<E, D>::BYTES;
   // Q and K are staged as natural tiles where they fit; in fp32 at D = 128
   // their fragments are read from global memory instead (the 64 KB of tiles
-  // would take the workgroup past the 160 KB of LDS), and the gradients are
-  // stored straight from the waves (a staged 64 x 128 fp32 tile needs 32 KB).
+  // would take the workgroup past the 160 KB of LDS), the gradients are
+  // stored straight from the waves (a staged 64 x 128 fp32 tile needs 32 KB),
+  // and the transposed T and dP*D operands are read from those matrices
+  // rather than from records of their own.
   static constexpr bool kStageQK = !(sizeof(E) == 4 && D == 128);
+  static constexpr bool kRec = kStageQK;
   static constexpr int QKT = kStageQK ? TILE : 0;
-  // region U: dV'^T + dW (through dT), then M1 | (dP*D)^T records | E + E^T
-  static constexpr int UNI_A = 2 * SET, UNI_B = MAT + 6 * RECB + PMAT;
-  static constexpr int UNI = UNI_A > UNI_B ? UNI_A : UNI_B;
+  static constexpr int RECS = kRec ? 6 * RECB : 0;
   static constexpr int oT = 0;                          // T, from the forward context
   static constexpr int odP = oT + MAT;                  // dP * D
-  static constexpr int oVt = odP + PMAT;
-  static constexpr int oU = oVt + SET;                  // sdVt | sdW, later sM1 | sPDt | sEE
-  static constexpr int oPDt = oU + MAT;
-  static constexpr int oEE = oPDt + 6 * RECB;           // E + E^T, operand type
-  static constexpr int odTt = oU + UNI;
-  static constexpr int oQ = odTt + MAT;                 // staged natural tiles
+  static constexpr int oVt = odP + PMAT;                // F(V'; s, j) records
+  static constexpr int oDV = oVt + SET;                 // F(dV'; r, j) records, later F(T^T dV'; s, j)
+  static constexpr int oG = oDV + SET;                  // G = dV' V'^T (fp32), later dk staging
+  static constexpr int oEE = oG + MAT;                  // E + E^T, operand type
+  static constexpr int oPDt = oEE + PMAT;               // F(dP*D; s, r) records
+  static constexpr int oTt = oPDt + RECS;               // F(T; s, r) records
+  static constexpr int oQ = oTt + RECS;                 // staged natural tiles
   static constexpr int oK = oQ + QKT;
   static constexpr int oSm = oK + QKT;
   static constexpr int SMALL = (64 * 2 + NW * 64 * 2 + NW * 2) * 4;
   static constexpr int BASE = oSm + SMALL;
-  static constexpr bool kStageDO = BASE + TILE <= 160 * 1024;
+  static constexpr bool kStageDO = BASE + TILE <= 160 * 1024 - 512;
   static constexpr int odO = BASE;
   static constexpr int BYTES = BASE + (kStageDO ? TILE : 0);
   static_assert(BYTES + 128 * 4 <= 160 * 1024, "bwd_grad fits the LDS of a workgroup");
+  static_assert(SET >= 2 * NW * 64 * 4, "the dbeta slots fit the dX_u region");
 };
 
 template <typename E, int D, bool NORM>
@@ -485,12 +500,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   float* sT = reinterpret_cast<float*>(smem + S::oT);
   E* sdP = reinterpret_cast<E*>(smem + S::odP);
   E* sVt = reinterpret_cast<E*>(smem + S::oVt);
-  E* sdVt = reinterpret_cast<E*>(smem + S::oU);
-  E* sdW = reinterpret_cast<E*>(smem + S::oU + S::SET);
-  float* sM1 = reinterpret_cast<float*>(smem + S::oU);
-  float* sdTt = reinterpret_cast<float*>(smem + S::odTt);
-  E* sTt = reinterpret_cast<E*>(smem + S::odTt);       // after M1: F(T; s, r) records
-  E* sPDt = reinterpret_cast<E*>(smem + S::oPDt);      // after M1: F(dP*D; s, r) records
+  E* sdVt = reinterpret_cast<E*>(smem + S::oDV);
+  E* sdXu = reinterpret_cast<E*>(smem + S::oDV);       // after G: F(T^T dV'; s, j) records
+  float* sG = reinterpret_cast<float*>(smem + S::oG);
+  E* sTt = reinterpret_cast<E*>(smem + S::oTt);        // F(T; s, r) records
+  E* sPDt = reinterpret_cast<E*>(smem + S::oPDt);      // F(dP*D; s, r) records
   char* tQ = smem + S::oQ;
   char* tK = smem + S::oK;
   char* tO = smem + S::odO;
@@ -499,6 +513,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   float* s_pg = s_beta + 64;          // [NW][64] dgamma partials
   float* s_pb = s_pg + NW * 64;       // [NW][64] dbeta partials
   float* s_misc = s_pb + NW * 64;     // [NW][2]: sum_s c_s, <h, H'>
+  // at the end, in the dX_u records' region (free once the dk phase is done):
+  float* s_pq = reinterpret_cast<float*>(smem + S::oDV);   // [NW][64] dbeta partials, quotient form
+  float* s_pa = s_pq + NW * 64;                            // [NW][64] partials of ||A_r||^2
 
   const int ch = blockIdx.x;
   const int H = p.H;
@@ -597,25 +614,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   auto my4 = [&](f32x8 x) {
     return hw ? f32x4{x[4], x[5], x[6], x[7]} : f32x4{x[0], x[1], x[2], x[3]};
   };
-  // Owners of the M1 and dA tiles and of the transposed records at 8 waves,
-  // balanced by cost: M1 tiles of a-block <= 1 and dA tiles of b-block >= 2
-  // take two 32-deep fp32 steps, the others one; a record costs about a
-  // third of a one-step tile.  Other wave counts deal round-robin.
-  constexpr int M1_OWN8[10] = {0, 1, 2, 3, 4, 5, 6, 7, 3, 4};
-  constexpr int DA_OWN8[10] = {3, 3, 4, 4, 5, 2, 5, 6, 0, 1};
-  constexpr int TREC_OWN8[12] = {2, 3, 4, 5, 6, 7, 2, 3, 4, 5, 6, 7};
+  // Owners of the dA tiles and of the transposed records at 8 waves,
+  // balanced by cost: dA tiles of a-block <= 1 take two 32-deep fp32 steps,
+  // the others one; a record costs about a third of a one-step tile.  Other
+  // wave counts deal round-robin.
+  constexpr int DA_OWN8[10] = {0, 1, 2, 3, 4, 5, 6, 7, 3, 4};
+  constexpr int TREC_OWN8[12] = {5, 6, 7, 0, 1, 2, 5, 6, 7, 0, 1, 2};
   constexpr int RR4[10] = {0, 1, 2, 3, 0, 1, 2, 3, 0, 1};
   constexpr int RREC4[12] = {3, 2, 1, 0, 3, 2, 1, 0, 3, 2, 1, 0};
   constexpr int MAXT = NW == 8 ? 2 : 3;
-  constexpr unsigned long long M1_LIST = NW == 8 ? pack_owned<10, 8, 2>(M1_OWN8) : pack_owned<10, 4, 3>(RR4);
   constexpr unsigned long long DA_LIST = NW == 8 ? pack_owned<10, 8, 2>(DA_OWN8) : pack_owned<10, 4, 3>(RR4);
   constexpr unsigned long long TREC_LIST = NW == 8 ? pack_owned<12, 8, 2>(TREC_OWN8) : pack_owned<12, 4, 3>(RREC4);
   static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
-  // value rows of this wave's dT tiles, read with the setup's reads (used
-  // several phases later)
-  constexpr int NTT = (10 + NW - 1) / NW;   // dT tiles per wave, at most
-  frag_t<E> vn[NTT][KB];
   // ---- setup: decays, staged tiles, and the records the transposes need
   {
     const float gv = p.gamma[(size_t)ch * 64 + lane];
@@ -634,14 +645,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       }
     }
     if constexpr (S::kStageDO) so.load(dO + base, rowstride, L, tid, nullptr, 0, p.vdim);
-#pragma unroll
-    for (int k = 0; k < NTT; ++k) {
-      const int t = w + NW * k;
-      const int rbt = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-      const int sbt = t - rbt * (rbt + 1) / 2;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) vn[k][kb] = t < 10 ? gnat(V, vbase, vrow, 16 * sbt + li, kb, p.vdim) : zero_frag<E>();
-    }
     // T = (I + diag(beta) A')^-1 as the forward solved it
     constexpr int TPER = 64 * 16 / NT;
     f32x4 tv[TPER];
@@ -693,8 +696,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     store_half(sVt + (sbp * KB + kw) * REC, mma(vrec[skb], idh, zero4()));
     store_half(sdVt + (sbp * KB + kw) * REC, mma(drec[skb], idh, zero4()));
   }
-  // zero the blocks no tile writes: dT^T below the block diagonal, dP*D above
-  zero_off_blocks<float, false>(sdTt, LDF, tid, NT);
+  // zero the blocks no tile writes: G and dP*D above the block diagonal
+  zero_off_blocks<float, true>(sG, LDF, tid, NT);
   zero_off_blocks<E, true>(sdP, LDE, tid, NT);
   // halves of the h and H' records this wave's i-block needs (used after the next barrier)
   frag_t<E> hrec[NJ], hprec[NJ];
@@ -710,6 +713,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // groups) land in lane 16 blk + li; row-indexed values (token 16 blk +
   // 4 lg + q, equal in the 16 lanes of group lg) in lane (li = 4 blk + q, lg).
   float dgc = 0.f, dgr = 0.f, dbc = 0.f, dbr = 0.f;
+  float dbq = 0.f, dar = 0.f;   // quotient form of dbeta (column-indexed), ||A_r||^2 (row-indexed)
   auto add_col = [&](float& acc, int blk, float v) { acc += (lg == blk) ? v : 0.f; };
   auto add_row = [&](float& acc, int blk, const float* v4) {
     const int q = li & 3;
@@ -717,21 +721,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     acc += ((li >> 2) == blk) ? x : 0.f;
   };
 
-  // ---- dP = dO V'^T and P (lower tiles, round-robin): sdP = dP * D,
-  //      dgamma += rowsum(dP * P) - colsum(dP * P)
+  // ---- dP = dO V'^T, P, and G = dV' V'^T (lower tiles, round-robin):
+  //      sdP = dP * D, sG = G, dgamma += rowsum(dP * P) - colsum(dP * P)
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
     const int t = w + NW * k;
     if (t >= 10) break;
     const int rb = tri_row(t), sb = tri_col(t);
-    f32x4 dp = zero4(), qk = zero4();
+    f32x4 dp = zero4(), qk = zero4(), gt = zero4();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      dp = mma(of(rb, kb), lrec(sVt, sb, kb), dp);
+      const frag_t<E> vs = lrec(sVt, sb, kb);
+      dp = mma(of(rb, kb), vs, dp);
+      gt = mma(lrec(sdVt, rb, kb), vs, gt);
       qk = mma(qf(rb, kb), kf(sb, kb), qk);
     }
     // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
     const int s_ = 16 * sb + li;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sG[(16 * rb + 4 * lg + q) * LDF + s_] = gt[q];
     const float gs = s_gam[s_];
     const f32x4 gr4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * rb + 4 * lg);
     float rs[4], cs = 0.f;
@@ -752,7 +760,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     add_col(dgc, sb, -cs);
   }
 
-  // ---- transposes of h and H' for this wave's i-block; dW = -dV' h^T
+  // ---- transposes of h and H' for this wave's i-block
   frag_t<E> hT[KB], hpT[KB];   // F(h; i, j), F(H'; i, j) for i-block w
   {
     float hh = 0.f;
@@ -770,88 +778,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     hh = sum_in_group(sum_groups(hh));
     if (lane == 0) s_misc[2 * w + 1] = hh;
   }
-  frag_t<E> dWir[2];  // F(dW; i, r) for i-block w, rkb
-  {
-    f32x4 dw[4];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int jkb = 0; jkb < KB; ++jkb) acc = mma(lrec(sdVt, rb, jkb), hT[jkb], acc);
-      dw[rb] = -acc;   // lane holds dW[r = 16rb + 4lg + q][i = 16w + li]
-    }
-#pragma unroll
-    for (int rkb = 0; rkb < 2; ++rkb) dWir[rkb] = to_frag<E>(dw[2 * rkb], dw[2 * rkb + 1]);
-    // half hw of the F(dW; r, i) records (rb, kw) for the dT product
-#pragma unroll
-    for (int rbp = 0; rbp < 4; ++rbp)
-      store_half(sdW + (rbp * KB + kw) * REC, mma(dWir[rbp >> 1], (rbp & 1) ? id1 : id0, zero4()));
-  }
   __syncthreads();
 
-  // ---- dT = dW Xw^T + dV' Xu^T (lower tiles, round-robin) -> sdTt[s][r], strict lower only.
-  //      Xw = diag(beta Gam) K and Xu = diag(beta) V scale the columns s of the
-  //      tile, so the products run on the unscaled rows.
-#pragma unroll
-  for (int k = 0; k < NTT; ++k) {
-    const int t = w + NW * k;
-    if (t >= 10) continue;
-    const int rb = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-    const int sb = t - rb * (rb + 1) / 2;
-    const int s_ = 16 * sb + li;
-    const float bs = s_beta[s_], bgs = bs * __expf(s_gam[s_]);
-    f32x4 aw = zero4(), au = zero4();
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      aw = mma(lrec(sdW, rb, kb), kf(sb, kb), aw);
-      au = mma(lrec(sdVt, rb, kb), vn[k][kb], au);
-    }
-    // lane holds dT[r = 16rb + 4lg + q][s]
-    f32x4 out;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = (16 * rb + 4 * lg + q) > s_ ? bgs * aw[q] + bs * au[q] : 0.f;
-    *reinterpret_cast<f32x4*>(&sdTt[s_ * LDF + 16 * rb + 4 * lg]) = out;
-  }
-  __syncthreads();
-
-  // ---- M1 = T^T dT (fp32): M1[a][s] = sum_r T[r][a] dT[r][s]; tiles s-block <= a-block -> sM1[a][s]
-  zero_off_blocks<float, true>(sM1, LDF, tid, NT);   // blocks no tile writes are read as zero later
-#pragma unroll
-  for (int k = 0; k < MAXT; ++k) {
-    const int t = owned_item(M1_LIST, w, MAXT, k);
-    if (t == 15) break;
-    const int ab = tri_row(t), sb = tri_col(t);
-    // every operand read first, then the products
-    const bool two = ab <= 1;   // T[r][a] = 0 for r < a: the first 32-block only for a-block <= 1
-    f32x8 df[2], tf[2];
-#pragma unroll
-    for (int rkb = 0; rkb < 2; ++rkb) {
-      df[rkb] = (rkb == 1 || two) ? mfrag32(sdTt, sb, rkb) : f32x8{};
-      tf[rkb] = (rkb == 1 || two) ? mfragT32(sT, ab, rkb) : f32x8{};
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc = zero4();
-    if (two) acc = mma(df[0], tf[0], acc);
-    acc = mma(df[1], tf[1], acc);
-    // lane holds M1[a = 16ab + li][s = 16sb + 4lg + q]
-    *reinterpret_cast<f32x4*>(&sM1[(16 * ab + li) * LDF + 16 * sb + 4 * lg]) = acc;
-  }
-  __syncthreads();
-
-  // ---- dA = strict_lower(-M1 T^T); dbeta, dgamma terms of A; E + E^T -> sEE
+  // ---- dA = strict_lower(-T^T G); dbeta, dgamma terms of A; E + E^T -> sEE
 #pragma unroll
   for (int k = 0; k < MAXT; ++k) {
     const int t = owned_item(DA_LIST, w, MAXT, k);
     if (t == 15) break;
     const int ab = tri_row(t), bb = tri_col(t);
     // every operand read first, then the products (one LDS latency per tile)
-    f32x8 mf[2], tf[2];
+    f32x8 tf[2], gf[2];
     frag_t<E> ka[KB], kb_[KB];
-    const bool two = bb >= 2;   // T[b][s] = 0 for s > b: the second 32-block only for b-block >= 2
+    const bool two = ab <= 1;   // T[r][a] = 0 for r < a: the first 32-block of r only for a-block <= 1
 #pragma unroll
-    for (int skb = 0; skb < 2; ++skb) {
-      mf[skb] = (skb == 0 || two) ? mfrag32(sM1, ab, skb) : f32x8{};
-      tf[skb] = (skb == 0 || two) ? mfrag32(sT, bb, skb) : f32x8{};
+    for (int rkb = 0; rkb < 2; ++rkb) {
+      tf[rkb] = (rkb == 1 || two) ? mfragT32(sT, ab, rkb) : f32x8{};
+      gf[rkb] = (rkb == 1 || two) ? mfragT32(sG, bb, rkb) : f32x8{};
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -860,8 +802,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = zero4(), kk = zero4();
-    acc = mma(mf[0], tf[0], acc);
-    if (two) acc = mma(mf[1], tf[1], acc);
+    if (two) acc = mma(tf[0], gf[0], acc);
+    acc = mma(tf[1], gf[1], acc);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) kk = mma(ka[kb], kb_[kb], kk);
     // lane holds -dA[a = 16ab + 4lg + q][b = 16bb + li] and (K K^T)[a][b]
@@ -869,7 +811,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const float gb = s_gam[b];
     const f32x4 ga4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * ab + 4 * lg);
     const f32x4 be4 = *reinterpret_cast<const f32x4*>(s_beta + 16 * ab + 4 * lg);
-    float rs_b[4], rs_g[4], cs = 0.f;
+    float rs_b[4], rs_g[4], rs_a[4], cs = 0.f;
     f32x4 ev;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -881,6 +823,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         ap = kk[q] * Dm;   // A'[a][b]
       }
       rs_b[q] = da * ap;
+      const float av = be4[q] * ap;   // A[a][b]
+      rs_a[q] = av * av;
       const float ma = da * be4[q] * ap;
       rs_g[q] = ma;
       cs += ma;
@@ -909,16 +853,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     for (int q = 0; q < 4; ++q) {
       rs_b[q] = sum_in_group(rs_b[q]);
       rs_g[q] = sum_in_group(rs_g[q]);
+      rs_a[q] = sum_in_group(rs_a[q]);
     }
     cs = sum_groups(cs);
     add_row(dbr, ab, rs_b);
     add_row(dgr, ab, rs_g);
+    add_row(dar, ab, rs_a);
     add_col(dgc, bb, -cs);
   }
   // transposed records of T and dP*D for the output phase, once per workgroup
-  // (sdTt is free after M1; the dP*D records sit above sM1)
 #pragma unroll
-  for (int j = 0; j < MAXT; ++j) {
+  for (int j = 0; j < (S::kRec ? MAXT : 0); ++j) {
     const int k = owned_item(TREC_LIST, w, MAXT, j);
     if (k == 15) break;
     const int kk = k < 6 ? k : k - 6;
@@ -940,26 +885,27 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
   // computed are those of the normalised rows, y = x / ||x||; their per-row
-  // dots y . dy over all D columns are gathered in LDS (the M1 region is
-  // free now) and dx = (dy - y (y . dy)) / ||x|| is formed after a barrier:
-  // dq's right after its products, dk's at the end.
+  // dots y . dy over all D columns are gathered in LDS (G's region is free
+  // now) and dx = (dy - y (y . dy)) / ||x|| is formed after a barrier: dq's
+  // right after its products, dk's at the end.
   constexpr bool norm = NORM;
-  float* s_qd = sM1;             // [64][NW] partial q . dq
-  float* s_kd = sM1 + NW * 64;   // [64][NW] partial k . dk
+  float* s_qd = sG;             // [64][NW] partial q . dq
+  float* s_kd = sG + NW * 64;   // [64][NW] partial k . dk
   // dq, dk, dv leave through LDS: each wave holds 16 columns of a row (32
   // bytes in bf16), so its own stores would write partial lines; staged, the
   // rows go out whole, 16 bytes a lane, after the last barrier.  Staging
   // rows are unpadded, their 16-byte pieces XOR-swizzled by the row so that
   // the column-block writes of a wave fall in distinct banks.  Regions: dq in
-  // T's (free after the dA phase); dk in M1's (free after the dA phase) or,
-  // normalised, in Q's tile (free after the last barrier); dv in K's tile.
+  // T's (free after the records are made); dk in G's (free after the dA
+  // phase) or, normalised, in Q's tile (free after the last barrier); dv in
+  // K's tile.
   constexpr int RB = D * (int)sizeof(E);   // bytes of a staged row
   constexpr int PPR = RB / 16;             // 16-byte pieces per row
   constexpr bool kStageOut = S::kStageQK;
   static_assert(!kStageOut || (64 * RB <= S::MAT && 64 * RB <= S::TILE), "a staged output tile fits its region");
   // staging regions, or (unstaged) the gradient tensors themselves
   char* stq = kStageOut ? reinterpret_cast<char*>(sT) : reinterpret_cast<char*>(p.dq);
-  char* stk = kStageOut ? (norm ? tQ : reinterpret_cast<char*>(sM1)) : reinterpret_cast<char*>(p.dk);
+  char* stk = kStageOut ? (norm ? tQ : reinterpret_cast<char*>(sG)) : reinterpret_cast<char*>(p.dk);
   char* stv = kStageOut ? tK : reinterpret_cast<char*>(p.dv);
   // columns 16 w + 4 lg .. + 3 of row r (this lane's four values) into a
   // staging tile, or straight to row r of the gradient (rows < L and columns
@@ -996,6 +942,53 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       stage4(dst, r, o, false);
     }
   };
+  // F(T; s, r) and F(dP*D; s, r): from their records, or read transposed
+  auto tt = [&](int sb, int rkb) {
+    if constexpr (S::kRec) return trec(sTt, sb, rkb);
+    else return mfragT(sT, sb, rkb);
+  };
+  auto pdt = [&](int sb, int rkb) {
+    if constexpr (S::kRec) return trec(sPDt, sb, rkb);
+    else return pfragT(sb, rkb);
+  };
+  // dX_u = T^T dV' for this wave's j-block, first: dV = diag(beta) dX_u, the
+  // dbeta terms v_s . dX_u[s] (sum) and V'_s . dX_u[s] / beta_s (quotient), and
+  // its records (all waves' blocks) give dX_w = T^T dW = -dX_u h^T in the dk phase.
+  // Accumulator sb holds dX_u^T[j = 16w + 4lg + q][s = 16sb + li], which is
+  // half hw of the record F(dX_u; s, j) (sb, kw); the same half of the record
+  // F(V'; s, j) holds V' at the same (s, j).
+  f32x4 dvo[4];
+  {
+    f32x4 acc[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
+#pragma unroll
+    for (int rkb = 0; rkb < 2; ++rkb)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        if (32 * rkb + 31 < 16 * sb) continue;
+        acc[sb] = mma(drec[rkb], tt(sb, rkb), acc[sb]);
+      }
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int s_ = 16 * sb + li;
+      const float bs = s_beta[s_];
+      const f32x4 vv = my4(frag_to_f32<E>(vw[sb]));
+      const f32x4 vp = my4(frag_to_f32<E>(lrec(sVt, sb, kw)));
+      float dot = 0.f, dqt = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dot += vv[q] * acc[sb][q];
+        dqt += vp[q] * acc[sb][q];
+      }
+      dot = sum_groups(dot);
+      dqt = sum_groups(dqt);
+      add_col(dbc, sb, dot);
+      add_col(dbq, sb, bs != 0.f ? dqt / bs : 0.f);
+      dvo[sb] = scale4(acc[sb], bs);
+      store_half(sdXu + (sb * KB + kw) * REC, acc[sb]);
+    }
+  }
   // K and Q transposes for this wave's i-block: F(K; i, s), F(Q; i, r)
   frag_t<E> kT[2], qT[2];
   {
@@ -1011,6 +1004,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       qT[kb2] = to_frag<E>(tq[2 * kb2], tq[2 * kb2 + 1]);
     }
   }
+  __syncthreads();   // every block of dX_u is in sdXu
 
   // dQ^T[i][r] = scale (Gam_r sum_j h[i][j] dO[r][j] + sum_s K[s][i] dPD[r][s])
   {
@@ -1055,7 +1049,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
 
   // dK^T[i][s] = scale sum_r Q[r][i] dPD[r][s] + exp(gL - g_s) sum_j H'[i][j] V'[s][j]
-  //            + beta_s Gam_s sum_r dW[r][i] T[r][s] + sum_r K[r][i] (E + E^T)[s][r]
+  //            + beta_s Gam_s dX_w[s][i] + sum_r K[r][i] (E + E^T)[s][r],
+  // dX_w[s][i] = -sum_j dX_u[s][j] h[i][j]
   {
     f32x4 ta[4], tb[4], tc[4], td[4];
 #pragma unroll
@@ -1068,15 +1063,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 #pragma unroll
     for (int jkb = 0; jkb < KB; ++jkb)
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) tb[sb] = mma(hpT[jkb], lrec(sVt, sb, jkb), tb[sb]);
+      for (int sb = 0; sb < 4; ++sb) {
+        tb[sb] = mma(hpT[jkb], lrec(sVt, sb, jkb), tb[sb]);
+        tc[sb] = mma(hT[jkb], lrec(sdXu, sb, jkb), tc[sb]);
+      }
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) tc[sb] = -tc[sb];
 #pragma unroll
     for (int rkb = 0; rkb < 2; ++rkb)
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         td[sb] = mma(kT[rkb], efrag(sEE, sb, rkb), td[sb]);
-        if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s], T[r][s] vanish for r < s
-        ta[sb] = mma(qT[rkb], trec(sPDt, sb, rkb), ta[sb]);
-        tc[sb] = mma(dWir[rkb], trec(sTt, sb, rkb), tc[sb]);
+        if (32 * rkb + 31 < 16 * sb) continue;  // dPD[r][s] vanishes for r < s
+        ta[sb] = mma(qT[rkb], pdt(sb, rkb), ta[sb]);
       }
     float csum = 0.f;
 #pragma unroll
@@ -1115,33 +1114,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     if (lane == 0) s_misc[2 * w] = csum;
   }
 
-  // dV^T[j][s] = beta_s sum_r dV'[r][j] T[r][s]; dbeta_s += v_s . (T^T dV')_s
-  // (kept in registers until K's tile is free for its staging)
-  f32x4 dvo[4];
-  {
-    f32x4 acc[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) acc[sb] = zero4();
-#pragma unroll
-    for (int rkb = 0; rkb < 2; ++rkb)
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        if (32 * rkb + 31 < 16 * sb) continue;
-        acc[sb] = mma(drec[rkb], trec(sTt, sb, rkb), acc[sb]);
-      }
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const int s_ = 16 * sb + li;
-      const float bs = s_beta[s_];
-      const f32x4 vv = my4(frag_to_f32<E>(vw[sb]));
-      float dot = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dot += vv[q] * acc[sb][q];
-      dot = sum_groups(dot);
-      add_col(dbc, sb, dot);
-      dvo[sb] = scale4(acc[sb], bs);
-    }
-  }
   {
     // this wave's slots: the row-indexed sums are stored, the column-indexed
     // ones added (one wave's LDS accesses complete in order)
@@ -1154,6 +1126,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     pb[lane] += dbc;
   }
   __syncthreads();
+  {
+    const int tr = 16 * (li >> 2) + 4 * lg + (li & 3);
+    s_pa[w * 64 + tr] = dar;
+    s_pq[w * 64 + lane] = dbq;
+  }
 
   if constexpr (norm) norm_out(dkh, kn4, s_kd, s_inv + 64, stk);
 #pragma unroll
@@ -1184,15 +1161,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // ---- dgamma -> dg (reverse chunk-local cumsum), dbeta
   if (w == 0) {
     const int r = lane;
-    float dgam = 0.f, db = 0.f, ctot = 0.f, hh = 0.f;
+    float dgam = 0.f, db = 0.f, dbt = 0.f, an = 0.f, ctot = 0.f, hh = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       dgam += s_pg[ww * 64 + r];
       db += s_pb[ww * 64 + r];
+      dbt += s_pq[ww * 64 + r];
+      an += s_pa[ww * 64 + r];
       ctot += s_misc[2 * ww];
       hh += s_misc[2 * ww + 1];
     }
     if (r == L - 1) dgam += ctot + GL * hh;
+    if (an > 1.f) db = dbt;
     if (r >= L) dgam = 0.f;
     // reverse inclusive scan over lanes
     float x = dgam;
