@@ -69,8 +69,8 @@ __device__ __forceinline__ int tri_col(int t) { const int r = tri_row(t); return
 // K4: per (chunk, head), D/32 waves; wave w owns feature columns [32w, 32w+32).
 // Writes the operands of the reverse pass:
 //   Ktn = F(Kt; s, i), WnT = F(-W; i, r)            (fragment-native)
-//   Z   = (scale Gam Q)^T dO   [jb][ib] accumulator records, fp32
-//   dVl = P^T dO               [jb][sb] accumulator records, fp32
+//   Z   = (scale Gam Q)^T dO   [jb][ib] accumulator records, operand type
+//   dVl = P^T dO               [jb][sb] accumulator records, operand type
 template <typename E, int D>
 struct BwdPrepSmem {
   static constexpr int NJ = D / 16;
@@ -627,7 +627,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   constexpr unsigned long long TREC_LIST = NW == 8 ? pack_owned<12, 8, 2>(TREC_OWN8) : pack_owned<12, 4, 3>(RREC4);
   static_assert(NW == 8 || NW == 4, "bwd_grad deals its tiles over 4 or 8 waves");
 
-  // ---- setup: decays, staged tiles, and the records the transposes need
+  // ---- setup.  Reads are issued in three groups, each ahead of the phase
+  // that waits for it: the staged tiles and T (stored to LDS before the first
+  // barrier), the V' and dV' records (transposed after it), and the h and H'
+  // record halves with the V rows of dbeta (used after the second).  Issuing
+  // all of them at the start measured slower: the reads of a unit stream in
+  // at a fixed rate per CU, so the early ones only wait longer.
+  frag_t<E> vrec[2], drec[2];      // F(V'; j, s), F(dV'; j, r) of column block w
+  frag_t<E> hrec[NJ], hprec[NJ];   // halves of the h and H' records of this wave's i-block
+  // V[16 sb + li][32 kw + 16 hw + 4 lg + q], the v_s of this wave's columns:
+  // read unconditionally (row and column clamped into the tensor) and zeroed
+  // where they fall outside when used, so that no read waits at a branch
+  quad_t<E> vq[4];
+  auto load_vq = [&]() {
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int vr = 16 * sb + li < L ? 16 * sb + li : L - 1;
+      const int vc = 32 * kw < p.vdim ? 32 * kw + 16 * hw + 4 * lg : 0;
+      vq[sb] = *reinterpret_cast<const quad_t<E>*>(V + vbase + (size_t)vr * vrow + vc);
+    }
+  };
   {
     const float gv = p.gamma[(size_t)ch * 64 + lane];
     const float bv = lane < L ? p.beta[(size_t)(tok0 + lane) * H + h] : 0.f;
@@ -675,7 +694,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       *reinterpret_cast<f32x4*>(&sT[r * LDF + 4 * c4]) = tv[k];
     }
   }
-  frag_t<E> vrec[2], drec[2];   // F(V'; j, s), F(dV'; j, r) of column block w
 #pragma unroll
   for (int skb = 0; skb < 2; ++skb) {
     vrec[skb] = load_rec<E>(Vf + (((size_t)ch * NJ + w) * 2 + skb) * REC, lane);
@@ -699,13 +717,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // zero the blocks no tile writes: G and dP*D above the block diagonal
   zero_off_blocks<float, true>(sG, LDF, tid, NT);
   zero_off_blocks<E, true>(sdP, LDE, tid, NT);
-  // halves of the h and H' records this wave's i-block needs (used after the next barrier)
-  frag_t<E> hrec[NJ], hprec[NJ];
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
     hrec[jb] = load_half(Hf + (((size_t)ch * NJ + jb) * KB + kw) * REC);
     hprec[jb] = load_half(HPf + (((size_t)ch * NJ + jb) * KB + kw) * REC);
   }
+  if constexpr (sizeof(E) == 2) load_vq();
   __syncthreads();
 
   // Per-token partial sums of dgamma and dbeta stay in registers until the
@@ -877,10 +894,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       store_rec<E>(sPDt + kk * REC, lane, x);
     }
   }
-  // operands of the output phase that come from global memory
-  frag_t<E> vw[4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) vw[sb] = gnat(V, vbase, vrow, 16 * sb + li, kw, p.vdim);
+  // (in fp32 the V rows are read here: held across the dP and dA phases,
+  // their 16 registers would spill)
+  if constexpr (sizeof(E) == 4) load_vq();
   __syncthreads();
 
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
@@ -973,7 +989,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     for (int sb = 0; sb < 4; ++sb) {
       const int s_ = 16 * sb + li;
       const float bs = s_beta[s_];
-      const f32x4 vv = my4(frag_to_f32<E>(vw[sb]));
+      const f32x4 vv = s_ < L && 32 * kw < p.vdim ? quad_to_f32<E>(vq[sb]) : zero4();
       const f32x4 vp = my4(frag_to_f32<E>(lrec(sVt, sb, kw)));
       float dot = 0.f, dqt = 0.f;
 #pragma unroll

@@ -15,6 +15,26 @@ TORCH_DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
 TOL = {"fp32": dict(maxrel=1e-4, frob=1e-4), "bf16": dict(maxrel=2e-2, frob=1e-2)}
 
 
+def device_cus():
+    """Compute units of the current device: the state passes pick their
+    instance (one or two column blocks per workgroup, rotated reads) from the
+    ratio of their workgroup count to this."""
+    return torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+
+
+def batch_past_one_round(B, H, d):
+    """The smallest batch >= B whose state-pass grid, B * H * (d / 16)
+    workgroups, exceeds the device's compute units."""
+    return max(B, device_cus() // (H * (d // 16)) + 1)
+
+
+def batch_in_one_round(H, d):
+    """A batch whose state-pass grid lies in (CUs / 2, CUs], or None."""
+    per, cus = H * (d // 16), device_cus()
+    B = cus // per
+    return B if B >= 1 and cus // 2 < B * per <= cus else None
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

@@ -7,7 +7,7 @@ import torch
 import gdn_inputs as gi
 import linear_attention_gated_amd as gdn
 import oracle
-from gpu_util import check, dev_inputs, say, small_cfg, to_np
+from gpu_util import batch_past_one_round, check, device_cus, dev_inputs, say, small_cfg, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -133,8 +133,10 @@ def test_l2norm_is_a_no_op_on_unit_rows():
 
 @pytest.mark.parametrize("dtype,d,B,H", [("fp32", 64, 20, 4), ("fp32", 128, 5, 8), ("bf16", 128, 5, 8)])
 def test_state_pass_grid_past_one_round(dtype, d, B, H):
-    # more than 256 (sequence, head, 16-column block) workgroups: the state pass
-    # takes two column blocks per workgroup and rotates its shared reads
-    assert B * H * (d // 16) > 256
+    # more (sequence, head, 16-column block) workgroups than the device has
+    # CUs: the state pass takes two column blocks per workgroup and rotates its
+    # shared reads
+    B = batch_past_one_round(B, H, d)
+    assert B * H * (d // 16) > device_cus()
     x = gi.make_inputs(small_cfg(dtype, d, B=B, T=100, H=H, h0_std=0.05), 31 + d)
     compare(x, scale=0.8, label="state grid past one round")
