@@ -828,7 +828,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const float gb = s_gam[b];
     const f32x4 ga4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * ab + 4 * lg);
     const f32x4 be4 = *reinterpret_cast<const f32x4*>(s_beta + 16 * ab + 4 * lg);
-    float rs_b[4], rs_g[4], rs_a[4], cs = 0.f;
+    float rs_b[4], rs_a[4], cs = 0.f;
     f32x4 ev;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -840,11 +840,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
         ap = kk[q] * Dm;   // A'[a][b]
       }
       rs_b[q] = da * ap;
-      const float av = be4[q] * ap;   // A[a][b]
-      rs_a[q] = av * av;
-      const float ma = da * be4[q] * ap;
-      rs_g[q] = ma;
-      cs += ma;
+      rs_a[q] = ap * ap;
+      cs += da * be4[q] * ap;
       ev[q] = da * be4[q] * Dm;   // E[a][b]; zero on and above the diagonal
     }
     // E + E^T into sEE: E[a][b] at (a, b) and at (b, a).  Off the block
@@ -869,8 +866,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       rs_b[q] = sum_in_group(rs_b[q]);
-      rs_g[q] = sum_in_group(rs_g[q]);
       rs_a[q] = sum_in_group(rs_a[q]);
+    }
+    // the dgamma row term is beta_a times the dbeta one; ||A_a||^2 = beta_a^2 sum_b A'^2
+    float rs_g[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rs_g[q] = be4[q] * rs_b[q];
+      rs_a[q] *= be4[q] * be4[q];
     }
     cs = sum_groups(cs);
     add_row(dbr, ab, rs_b);
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
       dot = sum_groups(dot);
       dqt = sum_groups(dqt);
       add_col(dbc, sb, dot);
-      add_col(dbq, sb, bs != 0.f ? dqt / bs : 0.f);
+      add_col(dbq, sb, bs != 0.f ? __fdividef(dqt, bs) : 0.f);
       dvo[sb] = scale4(acc[sb], bs);
       store_half(sdXu + (sb * KB + kw) * REC, acc[sb]);
     }
