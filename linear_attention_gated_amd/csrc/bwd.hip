@@ -270,7 +270,7 @@ __global__ __launch_bounds__((64 * BwdRing<E, D, CPW>::WAVES)) void k_bwd_state(
   static_assert(R::FITS, "the ring fits the LDS");
   constexpr int NJ = D / 16, KB = D / 32, S = R::S;
   __shared__ __attribute__((aligned(1024))) char ring[S * R::SLOT];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   // CPW column blocks per workgroup (one compute wave each), as in the forward pass
   constexpr int NJP = NJ / CPW;

@@ -48,7 +48,9 @@ template <typename E> using frag_t = typename VecT<E>::x8;
 template <typename E> using quad_t = typename VecT<E>::x4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave index, as a scalar: it is one value per wave, and addresses, trip
+// counts and branches derived from it then stay in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ constexpr int kslot(int lg, int e) {
   return e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4);

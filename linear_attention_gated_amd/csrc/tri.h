@@ -40,7 +40,7 @@ __device__ __forceinline__ void store_acc16(float* M, int ld, int r0, int c0, in
 // means 1).  M: strictly lower part read only.  T: full 64x64 written (upper
 // zero).  All `nw` waves of the workgroup call this; it ends with a barrier.
 __device__ inline void tri_inverse64(const float* M, const float* rs, float* T, int ld, int nw) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, li = lane & 15, lg = lane >> 4;
+  const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   zero_off_blocks<float, true>(T, ld, threadIdx.x, 64 * nw);
   // diagonal blocks: lane (li, lg) solves column li, row group lg
   for (int b = w; b < 4; b += nw) {
