@@ -123,6 +123,43 @@ def test_stress_packed_fwd_bwd():
     compare_bwd(x, label="stress packed")
 
 
+def row_norms_A(x):
+    """||A_r||^2 of every token (rows of the strictly lower A of its 64-token chunk)."""
+    k, beta, g = x["k"], x["beta"], x["g"]
+    B, T, H, _ = k.shape
+    out = np.zeros((B, T, H))
+    for b in range(B):
+        for h in range(H):
+            for c0 in range(0, T, 64):
+                K = k[b, c0:c0 + 64, h]
+                gam = np.cumsum(g[b, c0:c0 + 64, h])
+                A = np.tril(beta[b, c0:c0 + 64, h][:, None] * (K @ K.T) * np.exp(gam[:, None] - gam[None, :]), -1)
+                out[b, c0:c0 + 64, h] = np.sum(A * A, axis=1)
+    return out
+
+
+@pytest.mark.parametrize("dtype,d,sigma", [("fp32", 64, 0.05), ("fp32", 128, 0.2), ("bf16", 128, 0.5)])
+def test_dbeta_rows_of_both_forms_in_one_chunk(dtype, d, sigma):
+    # dbeta has two exact forms, a three-term sum and (T^T dV')_r . V'_r / beta_r; the
+    # backward takes the quotient on rows where ||A_r||^2 > 1 and the sum elsewhere, which
+    # includes beta_r = 0 (there A_r = 0).  Clustered keys put many rows on the quotient;
+    # rows with beta = 0 and beta = 1e-13 in the same chunks take the sum.
+    x = gi.make_inputs(stress_cfg(dtype, d, sigma, T=300, H=2, h0_std=0.1, with_grad=True), 71)
+    b = x["beta"]
+    b[0, ::9, :] = 0.0
+    b[0, 4::13, :] = float(np.float32(1e-13))
+    rn = row_norms_A(x)
+    say("rows on the quotient form:", int(np.sum(rn > 1)), "of", rn.size, "; beta = 0 rows:", int(np.sum(b == 0)))
+    assert np.sum(rn > 1) > rn.size // 4 and np.sum(b == 0) > 0
+    got = compare_bwd(x, label="dbeta forms")
+    ref = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["h0"])
+    db, rdb = got[NAMES.index("dbeta")], ref[NAMES.index("dbeta")]
+    zero = b == 0
+    err0 = np.max(np.abs(db[zero] - rdb[zero])) / np.max(np.abs(rdb))
+    say("  dbeta on beta = 0 rows: max error / max|dbeta| = %.3e" % err0)
+    assert np.all(np.isfinite(db[zero])) and err0 <= TOL[dtype]["maxrel"]
+
+
 def _fwd_bwd(x):
     o, ht = run_fwd(x)
     grads = run_bwd(x)
