@@ -521,7 +521,7 @@ def main():
                     help="skip the second, event-bracketed timing region")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (the operator's sequences and heads "
+        print("bench.py: runs on one GPU only (the operator's sequences and heads "
               "would shard across GPUs without any exchange, but no multi-GPU path is built); "
               "got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
