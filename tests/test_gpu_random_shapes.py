@@ -12,7 +12,12 @@ draws).  In bf16 every output must meet the stated gate or, where the gate is
 below the problem's own sensitivity, at most three times the change of the
 exact result when the values the bf16 path rounds (q, k, v, do, and the
 states it keeps as bf16 between chunks) are perturbed by up to half a bf16
-unit in the last place."""
+unit in the last place.
+
+A second property test draws fp32 shapes in the clustered-key regime (keys
+around one direction, beta near 1, some beta zero), where the triangular solve
+is near its singular limit and dbeta takes both of its forms, at the fp32
+gate."""
 import numpy as np
 import pytest
 import torch
@@ -102,3 +107,45 @@ def run_case(c):
 @given(cases())
 def test_random_shapes_fwd_bwd(c):
     run_case(c)
+
+
+@st.composite
+def clustered_cases(draw):
+    return dict(d=draw(st.sampled_from([64, 128])), H=draw(st.integers(1, 2)),
+                sigma=draw(st.sampled_from([0.02, 0.05, 0.2, 0.5])), lo=draw(st.sampled_from([0.5, 0.9])),
+                lengths=draw(st.one_of(st.none(), st.lists(st.integers(0, 150), min_size=1, max_size=4))),
+                T=draw(st.integers(1, 300)), h0=draw(st.sampled_from([0.0, 0.1])), zero_beta=draw(st.booleans()),
+                seed=draw(st.integers(0, 2 ** 16)))
+
+
+@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+          phases=[Phase.explicit, Phase.generate], suppress_health_check=list(HealthCheck))
+@given(clustered_cases())
+def test_random_clustered_keys_fp32(c):
+    """Random fp32 shapes with keys clustered around one direction and beta near 1
+    (the triangular solve near its singular limit; most rows take the quotient
+    form of dbeta), some with every 7th beta zero (those rows take the sum):
+    forward and backward within 1e-4 of the oracle."""
+    lengths = c["lengths"]
+    if lengths is not None and sum(lengths) == 0:
+        lengths = lengths[:-1] + [1]
+    cfg = gi.Config("clustered", 1, c["T"], c["H"], c["d"], c["d"], "fp32", h0_std=c["h0"], with_grad=True,
+                    g_scale=0.001, k_cluster=c["sigma"], beta_range=(c["lo"], 1.0))
+    x = gi.make_inputs(cfg, c["seed"], lengths=lengths)
+    if c["zero_beta"]:
+        x["beta"][0, ::7, :] = 0.0
+    say("case", c, "tokens", x["B"] * x["T"], "N", x["N"])
+    d = dev_inputs(x)
+    o, ht, ctx = gdn.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["h0"], cu_seqlens=d["cu"],
+                         return_context=True)
+    grads = gdn.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["do"], initial_state=d["h0"], cu_seqlens=d["cu"],
+                    context=ctx)
+    torch.cuda.synchronize()
+    ro, rht = oracle.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], cu_seqlens=x["cu_seqlens"])
+    rg = oracle.bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], x["h0"], None, cu_seqlens=x["cu_seqlens"])
+    for name, a, b in zip(("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"), [o, ht] + list(grads), [ro, rht] + list(rg)):
+        a = to_np(a)
+        assert np.all(np.isfinite(a)), name
+        e = maxrel(a, b)
+        assert e <= TOL["fp32"]["maxrel"], (name, e, c)
+
