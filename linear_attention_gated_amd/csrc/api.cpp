@@ -321,6 +321,10 @@ gdn::Params base_params(const gdn_problem* p, const Layout& L, char* ws, hipStre
   const int64_t state_wgs = L.N * L.H * (L.D / 16), cus = device_cus(s);
   P.dma_rot = state_wgs > cus / 2 ? 1 : 0;
   P.state_cpw = state_wgs > cus ? 2 : 1;
+  // k_bwd_grad holds one workgroup per CU (bf16, d = 128): a round is one
+  // workgroup per CU, and workgroups `cus` apart share an XCD when it is a
+  // multiple of 8
+  P.grad_ahead = (int)(cus / 8 * 8);
   if (L.l2norm) P.kinv = reinterpret_cast<float*>(ws + L.kinv);
   return P;
 }

@@ -521,6 +521,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   const int H = p.H;
   const int c = ch / H, h = ch - c * H;
   const int4 ct = chunk_info(p, c);
+  // the unit one round ahead, for the L2 prefetch below (this unit when none)
+  constexpr bool kPrefetch = sizeof(E) == 2 && D == 128;
+  const int ua = kPrefetch && p.grad_ahead > 0 && ch + p.grad_ahead < p.NC * H ? ch + p.grad_ahead : ch;
+  const int ha = ua % H;
+  const int4 cta = kPrefetch ? chunk_info(p, ua / H) : ct;
   const int tok0 = ct.x, L = ct.y;
   const int lane = lane_id(), w = wave_id(), li = lane & 15, lg = lane >> 4;
   const int kw = w >> 1, hw = w & 1;
@@ -724,6 +729,29 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
   if constexpr (sizeof(E) == 2) load_vq();
   __syncthreads();
+  // L2 prefetch for the unit one round ahead (bf16, d = 128).  With one
+  // workgroup per CU the units of a round read at the same time and then
+  // compute with HBM idle; the unit `grad_ahead` further on (a multiple of 8,
+  // so on this XCD) runs next round, and the lines of its first phase (Q, K
+  // and dO rows and T: 512 lines of 128 bytes, one per thread) are touched
+  // now, one 4-byte read each.  The reads are unconditional (this unit's own
+  // lines when none is ahead): behind a branch, the compiler's waits for this
+  // unit's reads would also wait for them.  Their value is consumed before
+  // this unit's first store, as waits count stores too.
+  int pf = 0;
+  if constexpr (kPrefetch) {
+    static_assert(NT == 512, "one line per thread");
+    const int rr = (tid & 127) >> 1, part = tid & 1;
+    const int row = rr < cta.y ? rr : 0;
+    const size_t xa = (size_t)cta.x * xrow + (size_t)ha * p.kdim;
+    const size_t oa = ((size_t)cta.x * H + ha) * p.vdim;
+    const E* a;
+    if (tid < 128) a = Q + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
+    else if (tid < 256) a = K + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
+    else if (tid < 384) a = dO + oa + (size_t)row * rowstride + (64 * part < p.vdim ? 64 * part : 0);
+    else a = reinterpret_cast<const E*>(p.Tm + (size_t)ua * 4096 + 32 * (tid - 384));
+    pf = *reinterpret_cast<const int*>(a);
+  }
 
   // Per-token partial sums of dgamma and dbeta stay in registers until the
   // end.  Column-indexed values (token 16 blk + li, equal in the four lane
@@ -1133,6 +1161,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     if (lane == 0) s_misc[2 * w] = csum;
   }
 
+  // the prefetch's value, long arrived, before any store of this unit
+  if constexpr (kPrefetch) asm volatile("" ::"v"(pf));
   {
     // this wave's slots: the row-indexed sums are stored, the column-indexed
     // ones added (one wave's LDS accesses complete in order)

@@ -66,6 +66,7 @@ struct Params {
   void *Z, *dVl;
   int dma_rot;             // 1: the column-block workgroups of a state pass start their shared reads at different pieces
   int state_cpw;           // 16-column blocks of d_v per state-pass workgroup: 1 or 2 (2 implies dma_rot)
+  int grad_ahead;          // k_bwd_grad: workgroups one round holds (a multiple of 8), the prefetch distance
 };
 
 // Chunk c: (first token, length, sequence, index in sequence).  Dense
