@@ -734,9 +734,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // compute with HBM idle; the unit `grad_ahead` further on (a multiple of 8,
   // so on this XCD) runs next round, and the lines of its first phase (Q, K
   // and dO rows and T: 512 lines of 128 bytes, one per thread) are touched
-  // now, one 4-byte read each.  The reads are unconditional (this unit's own
-  // lines when none is ahead): behind a branch, the compiler's waits for this
-  // unit's reads would also wait for them.  Their value is consumed before
+  // now, one 4-byte read each.  The reads are unconditional (all on one line
+  // of this unit's T when none is ahead): behind a branch, the compiler's
+  // waits for this unit's reads would also wait for them.  Their value is consumed before
   // this unit's first store, as waits count stores too.
   int pf = 0;
   if constexpr (kPrefetch) {
@@ -750,6 +750,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     else if (tid < 256) a = K + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
     else if (tid < 384) a = dO + oa + (size_t)row * rowstride + (64 * part < p.vdim ? 64 * part : 0);
     else a = reinterpret_cast<const E*>(p.Tm + (size_t)ua * 4096 + 32 * (tid - 384));
+    if (ua == ch) a = reinterpret_cast<const E*>(p.Tm + (size_t)ch * 4096);   // none ahead: one line
     pf = *reinterpret_cast<const int*>(a);
   }
 
