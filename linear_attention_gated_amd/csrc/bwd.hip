@@ -497,12 +497,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   constexpr int KB = D / 32, NJ = D / 16, NW = D / 16, LDF = S::LDF, LDE = S::LDE;
   __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
   E* sEE = reinterpret_cast<E*>(smem + S::oEE);
-  float* sT = reinterpret_cast<float*>(smem + S::oT);
+  float* sT = reinterpret_cast<float*>(smem + S::oT);   // T^T: row a holds column a of T
   E* sdP = reinterpret_cast<E*>(smem + S::odP);
   E* sVt = reinterpret_cast<E*>(smem + S::oVt);
   E* sdVt = reinterpret_cast<E*>(smem + S::oDV);
   E* sdXu = reinterpret_cast<E*>(smem + S::oDV);       // after G: F(T^T dV'; s, j) records
-  float* sG = reinterpret_cast<float*>(smem + S::oG);
+  float* sG = reinterpret_cast<float*>(smem + S::oG);   // G^T, G = dV' V'^T
   E* sTt = reinterpret_cast<E*>(smem + S::oTt);        // F(T; s, r) records
   E* sPDt = reinterpret_cast<E*>(smem + S::oPDt);      // F(dP*D; s, r) records
   char* tQ = smem + S::oQ;
@@ -583,14 +583,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const float* row = M + (16 * ab + li) * LDF + 32 * kb;
     return to_frag<float>(*reinterpret_cast<const f32x4*>(row + 4 * lg), *reinterpret_cast<const f32x4*>(row + 16 + 4 * lg));
   };
-  // the same read transposed: index = columns 16cb.., contraction = rows 32kb..
-  auto mfragT32 = [&](const float* M, int cb, int kb) {
-    f32x8 t;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = M[(32 * kb + kslot(lg, e)) * LDF + 16 * cb + li];
-    return t;
-  };
-  auto mfragT = [&](const float* M, int cb, int kb) { return f32_to_frag<E>(mfragT32(M, cb, kb)); };
   // operand-type 64 x 64 matrices (dP*D, E + E^T)
   auto efrag = [&](const E* M, int ab, int kb) { return load_frag_row<E>(M + (16 * ab + li) * LDE + 32 * kb, lg); };
   auto pfragT = [&](int cb, int kb) {
@@ -674,8 +666,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     f32x4 tv[TPER];
 #pragma unroll
     for (int k = 0; k < TPER; ++k) {
-      const int e = tid + k * NT, r = e >> 4, c4 = e & 15;
-      tv[k] = *reinterpret_cast<const f32x4*>(p.Tm + (size_t)ch * 4096 + r * 64 + 4 * c4);
+      // column c, rows 4 r4 .. 4 r4 + 3 (a wave's lanes read whole rows)
+      const int e = tid + k * NT, c = e & 63, r4 = e >> 6;
+      const float* src = p.Tm + (size_t)ch * 4096 + (4 * r4) * 64 + c;
+      tv[k] = f32x4{src[0], src[64], src[128], src[192]};
     }
     // (the decays are written once every read above is in flight)
     if (w == 0) {
@@ -695,8 +689,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     if constexpr (S::kStageDO) so.store(tO, tid);
 #pragma unroll
     for (int k = 0; k < TPER; ++k) {
-      const int e = tid + k * NT, r = e >> 4, c4 = e & 15;
-      *reinterpret_cast<f32x4*>(&sT[r * LDF + 4 * c4]) = tv[k];
+      const int e = tid + k * NT, c = e & 63, r4 = e >> 6;
+      *reinterpret_cast<f32x4*>(&sT[c * LDF + 4 * r4]) = tv[k];
     }
   }
 #pragma unroll
@@ -719,8 +713,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     store_half(sVt + (sbp * KB + kw) * REC, mma(vrec[skb], idh, zero4()));
     store_half(sdVt + (sbp * KB + kw) * REC, mma(drec[skb], idh, zero4()));
   }
-  // zero the blocks no tile writes: G and dP*D above the block diagonal
-  zero_off_blocks<float, true>(sG, LDF, tid, NT);
+  // zero the blocks no tile writes: G above the block diagonal (stored
+  // transposed: below it) and dP*D above it
+  zero_off_blocks<float, false>(sG, LDF, tid, NT);
   zero_off_blocks<E, true>(sdP, LDE, tid, NT);
 #pragma unroll
   for (int jb = 0; jb < NJ; ++jb) {
@@ -784,8 +779,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     }
     // lane holds [r = 16rb + 4lg + q][s = 16sb + li]
     const int s_ = 16 * sb + li;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sG[(16 * rb + 4 * lg + q) * LDF + s_] = gt[q];
+    *reinterpret_cast<f32x4*>(&sG[s_ * LDF + 16 * rb + 4 * lg]) = gt;   // G^T[s][r]
     const float gs = s_gam[s_];
     const f32x4 gr4 = *reinterpret_cast<const f32x4*>(s_gam + 16 * rb + 4 * lg);
     float rs[4], cs = 0.f;
@@ -838,8 +832,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const bool two = ab <= 1;   // T[r][a] = 0 for r < a: the first 32-block of r only for a-block <= 1
 #pragma unroll
     for (int rkb = 0; rkb < 2; ++rkb) {
-      tf[rkb] = (rkb == 1 || two) ? mfragT32(sT, ab, rkb) : f32x8{};
-      gf[rkb] = (rkb == 1 || two) ? mfragT32(sG, bb, rkb) : f32x8{};
+      tf[rkb] = (rkb == 1 || two) ? mfrag32(sT, ab, rkb) : f32x8{};
+      gf[rkb] = (rkb == 1 || two) ? mfrag32(sG, bb, rkb) : f32x8{};
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -919,7 +913,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     const int sb = kk < 4 ? kk >> 1 : kk - 2, rkb = kk < 4 ? kk & 1 : 1;
     frag_t<E> x;
     if (k < 6) {
-      x = mfragT(sT, sb, rkb);
+      x = f32_to_frag<E>(mfrag32(sT, sb, rkb));
       store_rec<E>(sTt + kk * REC, lane, x);
     } else {
       x = pfragT(sb, rkb);
@@ -993,7 +987,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // F(T; s, r) and F(dP*D; s, r): from their records, or read transposed
   auto tt = [&](int sb, int rkb) {
     if constexpr (S::kRec) return trec(sTt, sb, rkb);
-    else return mfragT(sT, sb, rkb);
+    else return f32_to_frag<E>(mfrag32(sT, sb, rkb));
   };
   auto pdt = [&](int sb, int rkb) {
     if constexpr (S::kRec) return trec(sPDt, sb, rkb);
