@@ -731,8 +731,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // and dO rows and T: 512 lines of 128 bytes, one per thread) are touched
   // now, one 4-byte read each.  The reads are unconditional (all on one line
   // of this unit's T when none is ahead): behind a branch, the compiler's
-  // waits for this unit's reads would also wait for them.  Their value is consumed before
-  // this unit's first store, as waits count stores too.
+  // waits for this unit's reads would also wait for them.  Their value is
+  // consumed before this unit's first store, as waits count stores too.
   int pf = 0;
   if constexpr (kPrefetch) {
     static_assert(NT == 512, "one line per thread");
