@@ -229,7 +229,10 @@ def measured_peaks(torch, dev, reps=5):
     """Peaks of this GPU measured by the microbenchmarks of libgdn_peak.so (dense bf16
     MFMA issue on independent accumulators; a 2 GiB streaming copy and read, 16 bytes
     per lane), each the median of `reps` runs timed with events on the current stream.
-    Returns {"mfma_bf16_TFLOPs", "hbm_copy_GBps", "hbm_read_GBps"}."""
+    Also one wave's LDS read issue (shader-clock cycles per 1 KiB ds_read_b128, alone and
+    with one MFMA after each read; medians of `reps` runs).
+    Returns {"mfma_bf16_TFLOPs", "hbm_copy_GBps", "hbm_read_GBps",
+    "lds_read_cycles_one_wave", "lds_read_mfma_cycles_one_wave"}."""
     import numpy as np
     path = os.path.join(ROOT, "linear_attention_gated_amd", "libgdn_peak.so")
     lib = ctypes.CDLL(path)
@@ -237,6 +240,7 @@ def measured_peaks(torch, dev, reps=5):
     lib.gdn_peak_mfma_bf16.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
     lib.gdn_peak_copy.argtypes = [P, P, ctypes.c_size_t, ctypes.c_int, P]
     lib.gdn_peak_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_int, P]
+    lib.gdn_peak_lds_wave.argtypes = [P, P, ctypes.c_int, ctypes.c_int, P]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = P(torch.cuda.current_stream(dev).cuda_stream)
 
@@ -268,8 +272,19 @@ def measured_peaks(torch, dev, reps=5):
     tc = med(lambda: ok(lib.gdn_peak_copy(P(a.data_ptr()), P(b.data_ptr()), nbytes, 8 * cus, stream)))
     tr = med(lambda: ok(lib.gdn_peak_read(P(a.data_ptr()), nbytes, P(sink.data_ptr()), 8 * cus, stream)))
     del a, b, sink, out
+    cyc = torch.zeros(1, dtype=torch.int64, device=dev)
+    lsink = torch.zeros(64, dtype=torch.int32, device=dev)
+    lds = []
+    for with_mfma in (0, 1):
+        per = []
+        for _ in range(reps):
+            ok(lib.gdn_peak_lds_wave(P(cyc.data_ptr()), P(lsink.data_ptr()), with_mfma, 256, stream))
+            torch.cuda.synchronize()
+            per.append(int(cyc.item()) / (256 * 32))
+        lds.append(round(float(np.median(per)), 1))
     return {"mfma_bf16_TFLOPs": round(mfma, 1), "hbm_copy_GBps": round(2 * nbytes / tc / 1e9, 1),
-            "hbm_read_GBps": round(nbytes / tr / 1e9, 1)}
+            "hbm_read_GBps": round(nbytes / tr / 1e9, 1), "lds_read_cycles_one_wave": lds[0],
+            "lds_read_mfma_cycles_one_wave": lds[1]}
 
 
 def cpu_info():

@@ -5,6 +5,10 @@
 //     traffic inside the loop);
 //   - HBM bandwidth: a streaming copy and a streaming read of large buffers,
 //     16 bytes per lane per access, grid-stride, enough waves to fill the chip.
+//   - one wave's LDS read issue: the shader-clock cycles one wave spends per
+//     1 KiB ds_read_b128 (64 lanes x 16 bytes, contiguous, no bank conflicts)
+//     with many in flight, alone and with one MFMA issued after each read
+//     (the pattern of the state passes' chunk step).
 // Diagnostics only; the operator does not use them.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,9 +71,57 @@ __global__ __launch_bounds__(256) void k_read(const i32x4* __restrict__ src, siz
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Wave 0 of one workgroup: iters x 32 reads of 1 KiB from LDS (waiting after
+// every 32), each followed by an MFMA when WITH_MFMA; cycles[0] = the loop's
+// shader-clock cycles.  The read values and the accumulators are folded into
+// one value that is written only if it matches a sentinel, so nothing is
+// optimised away.
+template <bool WITH_MFMA>
+__global__ __launch_bounds__(256) void k_lds_wave(long long* cycles, int iters, int* sink) {
+  __shared__ __attribute__((aligned(1024))) char buf[64 * 1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 64 * 1024 / 4; i += blockDim.x) reinterpret_cast<int*>(buf)[i] = i;
+  __syncthreads();
+  if (w != 0) return;
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (__bf16)(1e-3f * (float)(lane + e));
+  f32x4 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int acc = 0;
+  const long long t0 = (long long)__builtin_readcyclecounter();
+  for (int it = 0; it < iters; ++it) {
+    const char* base = buf + (it & 1) * 32768;
+    i32x4 r[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      r[i] = *reinterpret_cast<const i32x4*>(base + i * 1024 + 16 * lane);
+      if (WITH_MFMA) c[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, c[i & 7], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc ^= r[i][0] ^ r[i][3];
+  }
+  const long long t1 = (long long)__builtin_readcyclecounter();
+  float f = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f += c[i][0];
+  if (lane == 0) cycles[0] = t1 - t0;
+  if (acc == 0x13572468 || f == 12345.f) sink[lane] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gdn_peak_lds_wave(long long* cycles, int* sink, int with_mfma, int iters, void* stream) {
+  if (!cycles || !sink || iters < 1) return (int)hipErrorInvalidValue;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (with_mfma) hipLaunchKernelGGL(k_lds_wave<true>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
+  else hipLaunchKernelGGL(k_lds_wave<false>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
+  return (int)hipGetLastError();
+}
 
 int gdn_peak_mfma_bf16(float* out, int blocks, int iters, void* stream) {
   if (!out || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;

@@ -32,13 +32,15 @@ def test_peak_library_exports_its_header():
     # the measured-peak microbenchmarks live in a library of their own
     src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdn_peak.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
-    assert names == ["gdn_peak_copy", "gdn_peak_mfma_bf16", "gdn_peak_read"], names
+    assert names == ["gdn_peak_copy", "gdn_peak_lds_wave", "gdn_peak_mfma_bf16", "gdn_peak_read"], names
     lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_gated_amd", "libgdn_peak.so"))
     for n in names:
         assert hasattr(lib, n), n
     # invalid arguments are rejected before any launch
     lib.gdn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     assert lib.gdn_peak_copy(None, None, 16, 1, None) != 0
+    lib.gdn_peak_lds_wave.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.gdn_peak_lds_wave(None, None, 0, 1, None) != 0
 
 
 def test_abi_version_and_status_strings():
