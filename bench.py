@@ -722,6 +722,31 @@ def main():
         recompute = {"ms_per_step": round(1e3 * el_rc / args.steps, 4),
                      "tokens_per_s": round(B * T * args.steps / el_rc, 1)}
 
+    # the same step captured once in a HIP graph and replayed: the kernels without the host's
+    # per-launch work (the headline value stays the eager step)
+    graph = None
+    if not args.no_profile_pass:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(args.warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        el_g = time.perf_counter() - t2
+        graph = {"ms_per_step": round(1e3 * el_g / args.steps, 4),
+                 "tokens_per_s": round(B * T * args.steps / el_g, 1)}
+        del gr
+
     if args.copy_calib:
         copy_calibration(torch, dev)
 
@@ -736,7 +761,7 @@ def main():
                    "B": B, "T": T, "H": H,
                    "dk": D, "dv": D, "chunk": C, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "step_roofline": step_roof,
-        "step_timing": timing, "recompute_step": recompute,
+        "step_timing": timing, "recompute_step": recompute, "graph_step": graph,
         "sources_sha": sources_sha(),
     }
     print(json.dumps(out), flush=True)
