@@ -304,6 +304,34 @@ def cpu_info():
     return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": aff}
 
 
+def graph_step(torch, step, steps, warmup, tokens):
+    """The step captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed `steps`
+    times: {"ms_per_step", "tokens_per_s"}, or {"error"} if the capture fails (an optional
+    figure that must not cost the bench line)."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(warmup):
+            gr.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gr.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        return {"ms_per_step": round(1e3 * el / steps, 4), "tokens_per_s": round(tokens * steps / el, 1)}
+    except RuntimeError as e:
+        torch.cuda.synchronize()
+        return {"error": str(e)[:200]}
+
+
 def step_percentiles(torch, dev, step, n, flush_bytes):
     """Per-step times (ms) over n steps, each bracketed by events on the current stream;
     with flush_bytes > 0 a write of that many bytes runs before each step, outside the
@@ -724,28 +752,7 @@ def main():
 
     # the same step captured once in a HIP graph and replayed: the kernels without the host's
     # per-launch work (the headline value stays the eager step)
-    graph = None
-    if not args.no_profile_pass:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            step()
-        for _ in range(args.warmup):
-            gr.replay()
-        torch.cuda.synchronize()
-        t2 = time.perf_counter()
-        for _ in range(args.steps):
-            gr.replay()
-        torch.cuda.synchronize()
-        el_g = time.perf_counter() - t2
-        graph = {"ms_per_step": round(1e3 * el_g / args.steps, 4),
-                 "tokens_per_s": round(B * T * args.steps / el_g, 1)}
-        del gr
+    graph = None if args.no_profile_pass else graph_step(torch, step, args.steps, args.warmup, B * T)
 
     if args.copy_calib:
         copy_calibration(torch, dev)
