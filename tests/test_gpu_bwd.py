@@ -80,6 +80,20 @@ def test_small_dense(dtype, d, B, T, H, h0, with_dht, scale):
 
 
 @pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128), ("fp32", 128)])
+def test_decay_extremes(dtype, d):
+    # per-token log decays of exactly 0 (no forgetting), -30 (exp(g) ~ 1e-13: the chunk's
+    # cumulative decays underflow to 0 within a few tokens) and the usual draws, in runs
+    # that straddle chunk boundaries; the backward must stay finite and match the oracle
+    cfg = small_cfg(dtype, d, T=300, H=2, h0_std=0.2, with_grad=True)
+    x = gi.make_inputs(cfg, 13)
+    rng = np.random.default_rng(14)
+    runs = np.repeat(rng.integers(0, 3, size=(x["B"], 300 // 25 + 1, x["H"])), 25, axis=1)[:, :300]
+    x["g"] = np.where(runs == 0, 0.0, np.where(runs == 1, -30.0, x["g"]))
+    dht = np.random.default_rng(15).standard_normal((x["N"], 2, d, d)) * 0.1
+    compare(x, dht=dht, label="decay 0 / -30 / drawn")
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 64), ("bf16", 128), ("fp32", 128)])
 def test_small_varlen(dtype, d):
     cfg = small_cfg(dtype, d, H=2, h0_std=0.3, with_grad=True)
     x = gi.make_inputs(cfg, 12, lengths=[1, 0, 63, 64, 65, 130, 0, 7])
