@@ -724,30 +724,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   }
   if constexpr (sizeof(E) == 2) load_vq();
   __syncthreads();
-  // L2 prefetch for the unit one round ahead (bf16, d = 128).  With one
-  // workgroup per CU the units of a round read at the same time and then
-  // compute with HBM idle; the unit `grad_ahead` further on (a multiple of 8,
-  // so on this XCD) runs next round, and the lines of its first phase (Q, K
-  // and dO rows and T: 512 lines of 128 bytes, one per thread) are touched
-  // now, one 4-byte read each.  The reads are unconditional (all on one line
-  // of this unit's T when none is ahead): behind a branch, the compiler's
-  // waits for this unit's reads would also wait for them.  Their value is
-  // consumed before this unit's first store, as waits count stores too.
-  int pf = 0;
-  if constexpr (kPrefetch) {
-    static_assert(NT == 512, "one line per thread");
-    const int rr = (tid & 127) >> 1, part = tid & 1;
-    const int row = rr < cta.y ? rr : 0;
-    const size_t xa = (size_t)cta.x * xrow + (size_t)ha * p.kdim;
-    const size_t oa = ((size_t)cta.x * H + ha) * p.vdim;
-    const E* a;
-    if (tid < 128) a = Q + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
-    else if (tid < 256) a = K + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
-    else if (tid < 384) a = dO + oa + (size_t)row * rowstride + (64 * part < p.vdim ? 64 * part : 0);
-    else a = reinterpret_cast<const E*>(p.Tm + (size_t)ua * 4096 + 32 * (tid - 384));
-    if (ua == ch) a = reinterpret_cast<const E*>(p.Tm + (size_t)ch * 4096);   // none ahead: one line
-    pf = *reinterpret_cast<const int*>(a);
-  }
 
   // Per-token partial sums of dgamma and dbeta stay in registers until the
   // end.  Column-indexed values (token 16 blk + li, equal in the four lane
@@ -924,6 +900,32 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // their 16 registers would spill)
   if constexpr (sizeof(E) == 4) load_vq();
   __syncthreads();
+  // L2 prefetch for the unit one round ahead (bf16, d = 128).  With one
+  // workgroup per CU the units of a round read at the same time and then
+  // compute with HBM idle; the unit `grad_ahead` further on (a multiple of 8,
+  // so on this XCD) runs next round, and the lines of its first phase (Q, K
+  // and dO rows and T: 512 lines of 128 bytes, one per thread) are touched
+  // now, one 4-byte read each.  The reads are unconditional (all on one line
+  // of this unit's T when none is ahead): behind a branch, the compiler's
+  // waits for this unit's reads would also wait for them.  Their value is
+  // consumed before this unit's first store, as waits count stores too.
+  // They go out here, after the dA phase: issued at the second barrier the
+  // backward measured about 1 us slower, after the dX_u barrier slower still.
+  int pf = 0;
+  if constexpr (kPrefetch) {
+    static_assert(NT == 512, "one line per thread");
+    const int rr = (tid & 127) >> 1, part = tid & 1;
+    const int row = rr < cta.y ? rr : 0;
+    const size_t xa = (size_t)cta.x * xrow + (size_t)ha * p.kdim;
+    const size_t oa = ((size_t)cta.x * H + ha) * p.vdim;
+    const E* a;
+    if (tid < 128) a = Q + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
+    else if (tid < 256) a = K + xa + (size_t)row * xrow + (64 * part < p.kdim ? 64 * part : 0);
+    else if (tid < 384) a = dO + oa + (size_t)row * rowstride + (64 * part < p.vdim ? 64 * part : 0);
+    else a = reinterpret_cast<const E*>(p.Tm + (size_t)ua * 4096 + 32 * (tid - 384));
+    if (ua == ch) a = reinterpret_cast<const E*>(p.Tm + (size_t)ch * 4096);   // none ahead: one line
+    pf = *reinterpret_cast<const int*>(a);
+  }
 
   // ---- per-wave outputs.  With in-operator normalisation the gradients just
   // computed are those of the normalised rows, y = x / ||x||; their per-row
