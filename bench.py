@@ -229,10 +229,11 @@ def measured_peaks(torch, dev, reps=5):
     """Peaks of this GPU measured by the microbenchmarks of libgdn_peak.so (dense bf16
     MFMA issue on independent accumulators; a 2 GiB streaming copy and read, 16 bytes
     per lane), each the median of `reps` runs timed with events on the current stream.
-    Also one wave's LDS read issue (shader-clock cycles per 1 KiB ds_read_b128, alone and
-    with one MFMA after each read; medians of `reps` runs).
+    Also one wave's LDS reads and MFMAs in shader-clock cycles (medians of `reps` runs):
+    per 1 KiB ds_read_b128 alone, per such read with one v_mfma_f32_16x16x32_bf16 after it
+    (order pinned), and per MFMA alone (four independent accumulator chains).
     Returns {"mfma_bf16_TFLOPs", "hbm_copy_GBps", "hbm_read_GBps",
-    "lds_read_cycles_one_wave", "lds_read_mfma_cycles_one_wave"}."""
+    "lds_read_cycles_one_wave", "lds_read_mfma_cycles_one_wave", "mfma_cycles_one_wave"}."""
     import numpy as np
     path = os.path.join(ROOT, "linear_attention_gated_amd", "libgdn_peak.so")
     lib = ctypes.CDLL(path)
@@ -275,16 +276,16 @@ def measured_peaks(torch, dev, reps=5):
     cyc = torch.zeros(1, dtype=torch.int64, device=dev)
     lsink = torch.zeros(64, dtype=torch.int32, device=dev)
     lds = []
-    for with_mfma in (0, 1):
+    for mode in (0, 1, 2):
         per = []
         for _ in range(reps):
-            ok(lib.gdn_peak_lds_wave(P(cyc.data_ptr()), P(lsink.data_ptr()), with_mfma, 256, stream))
+            ok(lib.gdn_peak_lds_wave(P(cyc.data_ptr()), P(lsink.data_ptr()), mode, 256, stream))
             torch.cuda.synchronize()
             per.append(int(cyc.item()) / (256 * 32))
         lds.append(round(float(np.median(per)), 1))
     return {"mfma_bf16_TFLOPs": round(mfma, 1), "hbm_copy_GBps": round(2 * nbytes / tc / 1e9, 1),
             "hbm_read_GBps": round(nbytes / tr / 1e9, 1), "lds_read_cycles_one_wave": lds[0],
-            "lds_read_mfma_cycles_one_wave": lds[1]}
+            "lds_read_mfma_cycles_one_wave": lds[1], "mfma_cycles_one_wave": lds[2]}
 
 
 def cpu_info():

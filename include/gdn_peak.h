@@ -31,14 +31,17 @@ int gdn_peak_copy(const void* src, void* dst, size_t bytes, int blocks, void* st
  * written (an xor of the data, so the reads cannot be dropped). */
 int gdn_peak_read(const void* src, size_t bytes, int* out, int blocks, void* stream);
 
-/* One wave's LDS read issue: wave 0 of one workgroup reads iters x 32 blocks of
- * 1 KiB from LDS with ds_read_b128 (64 lanes x 16 bytes, contiguous), waiting
- * after every 32; with with_mfma != 0 it issues one v_mfma_f32_16x16x32_bf16
- * after each read.  cycles[0] (one long long, device) receives the loop's
- * shader-clock cycles: cycles[0] / (32 iters) is the cost of one read (or one
- * read and one MFMA) to that wave.  sink: 64 ints, written only if the data
- * matches a sentinel (keeps the reads). */
-int gdn_peak_lds_wave(long long* cycles, int* sink, int with_mfma, int iters, void* stream);
+/* One wave's LDS reads and MFMAs: wave 0 of one workgroup runs iters rounds of
+ * mode 0: 32 reads of 1 KiB from LDS with ds_read_b128 (64 lanes x 16
+ * contiguous bytes), waited for at the round's end; mode 1: the same reads,
+ * each followed by one v_mfma_f32_16x16x32_bf16 (order pinned); mode 2: the 32
+ * MFMAs alone (four independent accumulator chains in modes 1 and 2).
+ * cycles[0] (one long long, device) receives the loop's shader-clock cycles:
+ * cycles[0] / (32 iters) is the cost to that wave of one read, one read with
+ * one MFMA, or one MFMA.  sink: 64 ints, written only if the data matches a
+ * sentinel (keeps the work).  Invalid pointers, iters < 1 or a mode outside
+ * 0..2 return hipErrorInvalidValue. */
+int gdn_peak_lds_wave(long long* cycles, int* sink, int mode, int iters, void* stream);
 
 #ifdef __cplusplus
 }

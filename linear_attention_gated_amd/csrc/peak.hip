@@ -71,42 +71,55 @@ __global__ __launch_bounds__(256) void k_read(const i32x4* __restrict__ src, siz
   out[blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
-// Wave 0 of one workgroup: iters x 32 reads of 1 KiB from LDS (waiting after
-// every 32), each followed by an MFMA when WITH_MFMA; cycles[0] = the loop's
-// shader-clock cycles.  The read values and the accumulators are folded into
-// one value that is written only if it matches a sentinel, so nothing is
-// optimised away.
-template <bool WITH_MFMA>
+// Wave 0 of one workgroup, iters rounds of: MODE 0, 32 reads of 1 KiB from
+// LDS (ds_read_b128, 64 lanes x 16 contiguous bytes); MODE 1, the same reads
+// each followed by one v_mfma_f32_16x16x32_bf16; MODE 2, the 32 MFMAs alone.
+// The MFMAs accumulate into four independent chains.  The order is pinned
+// with scheduling barriers (left alone, the compiler issues every read first
+// and every MFMA after them), and each round ends by waiting for its reads;
+// the read values are then only passed to an empty asm, so no vector ALU work
+// on them is timed.  cycles[0] = the loop's shader-clock cycles.  A value
+// that depends on the reads and the accumulators is written only if it
+// matches a sentinel, so nothing is optimised away.
+template <int MODE>
 __global__ __launch_bounds__(256) void k_lds_wave(long long* cycles, int iters, int* sink) {
-  __shared__ __attribute__((aligned(1024))) char buf[64 * 1024];
+  constexpr int NR = MODE == 2 ? 0 : 32, NM = MODE == 0 ? 0 : 32;
+  __shared__ __attribute__((aligned(1024))) char buf[32 * 1024];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 64 * 1024 / 4; i += blockDim.x) reinterpret_cast<int*>(buf)[i] = i;
+  for (int i = threadIdx.x; i < 32 * 1024 / 4; i += blockDim.x) reinterpret_cast<int*>(buf)[i] = i;
   __syncthreads();
   if (w != 0) return;
-  bf16x8 a;
+  bf16x8 a, b;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = (__bf16)(1e-3f * (float)(lane + e));
-  f32x4 c[8];
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1e-3f * (float)(lane + e));
+    b[e] = (__bf16)(2e-3f * (float)(lane - e));
+  }
+  f32x4 c[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   int acc = 0;
   const long long t0 = (long long)__builtin_readcyclecounter();
   for (int it = 0; it < iters; ++it) {
-    const char* base = buf + (it & 1) * 32768;
-    i32x4 r[32];
+    i32x4 r[NR > 0 ? NR : 1];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      r[i] = *reinterpret_cast<const i32x4*>(base + i * 1024 + 16 * lane);
-      if (WITH_MFMA) c[i & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, a, c[i & 7], 0, 0, 0);
+    for (int i = 0; i < NR; ++i) r[i] = *reinterpret_cast<const i32x4*>(buf + i * 1024 + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) c[i & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[i & 3], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 32; ++g) {
+      if (NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      if (NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc ^= r[i][0] ^ r[i][3];
+    for (int i = 0; i < NR; ++i) asm volatile("" ::"v"(r[i]));
+    acc ^= NR ? r[0][0] : 0;
   }
   const long long t1 = (long long)__builtin_readcyclecounter();
   float f = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) f += c[i][0];
+  for (int i = 0; i < 4; ++i) f += c[i][0];
   if (lane == 0) cycles[0] = t1 - t0;
   if (acc == 0x13572468 || f == 12345.f) sink[lane] = acc;
 }
@@ -115,11 +128,12 @@ __global__ __launch_bounds__(256) void k_lds_wave(long long* cycles, int iters, 
 
 extern "C" {
 
-int gdn_peak_lds_wave(long long* cycles, int* sink, int with_mfma, int iters, void* stream) {
-  if (!cycles || !sink || iters < 1) return (int)hipErrorInvalidValue;
+int gdn_peak_lds_wave(long long* cycles, int* sink, int mode, int iters, void* stream) {
+  if (!cycles || !sink || iters < 1 || mode < 0 || mode > 2) return (int)hipErrorInvalidValue;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (with_mfma) hipLaunchKernelGGL(k_lds_wave<true>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
-  else hipLaunchKernelGGL(k_lds_wave<false>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
+  if (mode == 0) hipLaunchKernelGGL(k_lds_wave<0>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
+  else if (mode == 1) hipLaunchKernelGGL(k_lds_wave<1>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
+  else hipLaunchKernelGGL(k_lds_wave<2>, dim3(1), dim3(256), 0, s, cycles, iters, sink);
   return (int)hipGetLastError();
 }
 

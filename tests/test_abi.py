@@ -41,6 +41,7 @@ def test_peak_library_exports_its_header():
     assert lib.gdn_peak_copy(None, None, 16, 1, None) != 0
     lib.gdn_peak_lds_wave.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert lib.gdn_peak_lds_wave(None, None, 0, 1, None) != 0
+    assert lib.gdn_peak_lds_wave(ctypes.c_void_p(16), ctypes.c_void_p(16), 3, 1, None) != 0
 
 
 def test_abi_version_and_status_strings():
