@@ -600,13 +600,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   auto store_half = [&](E* rec, f32x4 x) {
     *reinterpret_cast<quad_t<E>*>(rec + 8 * lane + 4 * hw) = to_quad<E>(x);
   };
-  // a record read for an identity transpose that keeps half hw of the
-  // contraction: the other half is never multiplied by a nonzero
-  auto load_half = [&](const E* rec) {
-    const quad_t<E> x = *reinterpret_cast<const quad_t<E>*>(rec + 8 * lane + 4 * hw);
-    const quad_t<E> z = to_quad<E>(zero4());
-    return hw ? join<E>(z, x) : join<E>(x, z);
-  };
+  // half hw of a record (a quad): the operand of a 16-deep identity
+  // transpose, the other half of the contraction being one that is only ever
+  // multiplied by zeros
+  auto load_half = [&](const E* rec) { return *reinterpret_cast<const quad_t<E>*>(rec + 8 * lane + 4 * hw); };
   // the four elements of a natural fragment that fall in this wave's columns
   auto my4 = [&](f32x8 x) {
     return hw ? f32x4{x[4], x[5], x[6], x[7]} : f32x4{x[0], x[1], x[2], x[3]};
@@ -631,7 +628,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   // all of them at the start measured slower: the reads of a unit stream in
   // at a fixed rate per CU, so the early ones only wait longer.
   frag_t<E> vrec[2], drec[2];      // F(V'; j, s), F(dV'; j, r) of column block w
-  frag_t<E> hrec[NJ], hprec[NJ];   // halves of the h and H' records of this wave's i-block
+  quad_t<E> hrec[NJ], hprec[NJ];   // halves of the h and H' records of this wave's i-block
   // V[16 sb + li][32 kw + 16 hw + 4 lg + q], the v_s of this wave's columns:
   // read unconditionally (row and column clamped into the tensor) and zeroed
   // where they fall outside when used, so that no read waits at a branch
@@ -703,6 +700,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
   const float GL = __expf(gL);
   const frag_t<E> id0 = ident_frag<E>(0, li, lg), id1 = ident_frag<E>(1, li, lg);
   const frag_t<E> idw = hw ? id1 : id0;
+  const quad_t<E> idq = ident_quad<E>(li, lg);
 
   // ---- transposes of this wave's column block of V' and dV' into LDS:
   //      half hw of sVt rec (sb, kw) = F(V'; s, j), of sdVt rec (rb, kw) = F(dV'; r, j)
@@ -782,11 +780,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void k_bwd_grad(Params p) {
     float hh = 0.f;
 #pragma unroll
     for (int jkb = 0; jkb < KB; ++jkb) {
-      const f32x4 a0 = mma(hrec[2 * jkb], idw, zero4());
-      const f32x4 a1 = mma(hrec[2 * jkb + 1], idw, zero4());
+      const f32x4 a0 = mma16(hrec[2 * jkb], idq, zero4());
+      const f32x4 a1 = mma16(hrec[2 * jkb + 1], idq, zero4());
       hT[jkb] = to_frag<E>(a0, a1);
-      const f32x4 b0 = mma(hprec[2 * jkb], idw, zero4());
-      const f32x4 b1 = mma(hprec[2 * jkb + 1], idw, zero4());
+      const f32x4 b0 = mma16(hprec[2 * jkb], idq, zero4());
+      const f32x4 b1 = mma16(hprec[2 * jkb + 1], idq, zero4());
       hpT[jkb] = to_frag<E>(b0, b1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) hh += a0[q] * b0[q] + a1[q] * b1[q];

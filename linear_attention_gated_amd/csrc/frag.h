@@ -74,6 +74,23 @@ __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 16-deep products over one half of a fragment's contraction slots (a quad:
+// elements 0..3 or 4..7 of each lane's fragment, as the 32-deep products above
+// pair them): one v_mfma_f32_16x16x16_bf16, or four v_mfma_f32_16x16x4_f32.
+// Equal to the 32-deep product of the fragments with the other half zero.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 a, f32x4 b, f32x4 c) {
+  f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], d, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+  d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], d, 0, 0, 0);
+  return c + d;
+}
+
 // ---- conversions --------------------------------------------------------
 template <typename E> __device__ __forceinline__ frag_t<E> to_frag(f32x4 lo, f32x4 hi);
 template <> __device__ __forceinline__ bf16x8 to_frag<bf16>(f32x4 lo, f32x4 hi) {
@@ -167,6 +184,13 @@ template <typename E> __device__ __forceinline__ frag_t<E> ident_frag(int hsel, 
   f32x8 t = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (lg == (li >> 2)) t[4 * hsel + (li & 3)] = 1.f;
   return f32_to_frag<E>(t);
+}
+
+// The 16 x 16 identity as a quad operand of mma16 (either half)
+template <typename E> __device__ __forceinline__ quad_t<E> ident_quad(int li, int lg) {
+  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+  if (lg == (li >> 2)) t[li & 3] = 1.f;
+  return to_quad<E>(t);
 }
 
 __device__ __forceinline__ f32x4 scale4(f32x4 x, float s) {
