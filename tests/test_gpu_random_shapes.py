@@ -9,10 +9,14 @@ Tiny shapes can be ill-conditioned: with one token per sequence, dk is the
 difference of two terms that may nearly cancel, and its normwise error then
 grows by the cancellation factor (fp32 errors rise from 1e-7 to 1e-6 on such
 draws).  In bf16 every output must meet the stated gate or, where the gate is
-below the problem's own sensitivity, at most three times the change of the
-exact result when the values the bf16 path rounds (q, k, v, do, and the
-states it keeps as bf16 between chunks) are perturbed by up to half a bf16
-unit in the last place.
+below the problem's own sensitivity, at most three times the largest change
+of the exact result over eight draws in which every value the bf16 path
+rounds (q, k, v, do, and the states it keeps as bf16 between chunks) is moved
+by half a bf16 unit in the last place, each with a random sign.  With one
+token per sequence an output has only a few elements, and a single draw can
+land far below what the path's own roundings do (a one-token dbeta whose two
+terms cancel 4:1 moved by 0.1% to 4% over draws, against 3% for a CPU
+emulation of the path's roundings).
 
 A second property test draws fp32 shapes in the clustered-key regime (keys
 around one direction, beta near 1, some beta zero), where the triangular solve
@@ -21,7 +25,7 @@ gate."""
 import numpy as np
 import pytest
 import torch
-from hypothesis import HealthCheck, Phase, given, settings
+from hypothesis import HealthCheck, Phase, example, given, settings
 from hypothesis import strategies as st
 
 import gdn_inputs as gi
@@ -80,18 +84,19 @@ def run_case(c):
     ref = [ro, rht] + list(rg)
     sens = {n: {"maxrel": 0.0, "frob": 0.0} for n in names}
     if c["dtype"] == "bf16":
-        rng = np.random.default_rng(c["seed"] + 2)
-        xp = dict(x)
-        for n in ("q", "k", "v", "do", "h0"):
-            if x[n] is not None:
-                xp[n] = x[n] * (1 + 2.0 ** -9 * rng.uniform(-1, 1, x[n].shape))
-        dhtp = None if dht is None else dht * (1 + 2.0 ** -9 * rng.uniform(-1, 1, dht.shape))
-        po, pht = oracle.fwd(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], xp["h0"], cu_seqlens=x["cu_seqlens"],
-                             scale=c["scale"], qk_l2norm=c["l2"])
-        pg = oracle.bwd(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], xp["do"], xp["h0"], dhtp,
-                        cu_seqlens=x["cu_seqlens"], scale=c["scale"], qk_l2norm=c["l2"])
-        for n, a, b in zip(names, [po, pht] + list(pg), ref):
-            sens[n] = {"maxrel": maxrel(a, b), "frob": frob(a, b)}
+        for draw in range(8):
+            rng = np.random.default_rng(c["seed"] + 2 + draw)
+            xp = dict(x)
+            for n in ("q", "k", "v", "do", "h0"):
+                if x[n] is not None:
+                    xp[n] = x[n] * (1 + 2.0 ** -9 * rng.choice([-1.0, 1.0], x[n].shape))
+            dhtp = None if dht is None else dht * (1 + 2.0 ** -9 * rng.choice([-1.0, 1.0], dht.shape))
+            po, pht = oracle.fwd(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], xp["h0"],
+                                 cu_seqlens=x["cu_seqlens"], scale=c["scale"], qk_l2norm=c["l2"])
+            pg = oracle.bwd(xp["q"], xp["k"], xp["v"], xp["g"], xp["beta"], xp["do"], xp["h0"], dhtp,
+                            cu_seqlens=x["cu_seqlens"], scale=c["scale"], qk_l2norm=c["l2"])
+            for n, a, b in zip(names, [po, pht] + list(pg), ref):
+                sens[n] = {"maxrel": max(sens[n]["maxrel"], maxrel(a, b)), "frob": max(sens[n]["frob"], frob(a, b))}
     for name, a, b in zip(names, got, ref):
         assert np.all(np.isfinite(a)), name
         err = {"maxrel": maxrel(a, b), "frob": frob(a, b)}
@@ -105,6 +110,8 @@ def run_case(c):
 @settings(max_examples=30, deadline=None, derandomize=True, database=None,
           phases=[Phase.explicit, Phase.generate], suppress_health_check=list(HealthCheck))
 @given(cases())
+@example(dict(dtype="bf16", dk=64, dv=64, H=1, B=2, T=1, lengths=None, h0=0.0, with_dht=True, scale=1.0, l2=True,
+              seed=4314))   # one token per sequence; dbeta's two terms cancel 4:1 in the second
 def test_random_shapes_fwd_bwd(c):
     run_case(c)
 
