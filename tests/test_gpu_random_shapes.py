@@ -107,7 +107,7 @@ def run_case(c):
             assert err[kind] <= bound, (name, kind, err[kind], bound, c)
 
 
-@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+@settings(max_examples=60, deadline=None, derandomize=True, database=None,
           phases=[Phase.explicit, Phase.generate], suppress_health_check=list(HealthCheck))
 @given(cases())
 @example(dict(dtype="bf16", dk=64, dv=64, H=1, B=2, T=1, lengths=None, h0=0.0, with_dht=True, scale=1.0, l2=True,
@@ -125,7 +125,7 @@ def clustered_cases(draw):
                 seed=draw(st.integers(0, 2 ** 16)))
 
 
-@settings(max_examples=25, deadline=None, derandomize=True, database=None,
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
           phases=[Phase.explicit, Phase.generate], suppress_health_check=list(HealthCheck))
 @given(clustered_cases())
 def test_random_clustered_keys_fp32(c):
