@@ -189,18 +189,24 @@ def _qkv_stride(tensors, names, dtype, device):
         _require(t, n, dtype, device, contiguous=False)
     if all(t.is_contiguous() for t in tensors):
         return 0
+    # The stride of a dimension of size one never moves an address (torch may report any
+    # value there): with T = 1 the tokens are spaced by the batch stride, and a single
+    # token (B = T = 1) has no spacing at all, which addresses like a contiguous row.
     s = None
     for t, n in zip(tensors, names):
         B, T, H, d = t.shape
         st = t.stride()
-        if st[3] != 1 or st[2] != d or (B > 1 and st[0] != T * st[1]):
+        if st[3] != 1 or (H > 1 and st[2] != d) or (B > 1 and T > 1 and st[0] != T * st[1]):
             raise ValueError("%s: a [B,T,H,d] view with rows of H*d elements, tokens evenly spaced, "
                              "is needed (strides %r)" % (n, st))
+        tok = st[1] if T > 1 else (st[0] if B > 1 else None)
+        if tok is None:
+            continue
         if s is None:
-            s = st[1]
-        elif st[1] != s:
-            raise ValueError("q, k and v must share one token stride (%s has %d, expected %d)" % (n, st[1], s))
-    return s
+            s = tok
+        elif tok != s:
+            raise ValueError("q, k and v must share one token stride (%s has %d, expected %d)" % (n, tok, s))
+    return 0 if s is None else s
 
 
 def _like_layout(tensors):
